@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/qwm.h declares, and its host-side argument/state checks return the
+documented status codes before anything would be enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import video_world_model_amd.qwm as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qwm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwm_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 19
+    L = Q.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _desc(**kw):
+    base = dict(heads=2, head_dim=128, n_centroids=16, rank=8, capacity_tokens=1000, dtype=Q.QWM_BF16,
+                max_epochs=2, max_query_tokens=64, max_build_tokens=512)
+    base.update(kw)
+    return Q.make_desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), Q.QWM_ERR_UNSUPPORTED),
+    (dict(head_dim=256), Q.QWM_ERR_UNSUPPORTED),
+    (dict(group=16), Q.QWM_ERR_UNSUPPORTED),
+    (dict(n_centroids=0), Q.QWM_ERR_UNSUPPORTED),
+    (dict(n_centroids=257), Q.QWM_ERR_UNSUPPORTED),
+    (dict(rank=0), Q.QWM_ERR_UNSUPPORTED),
+    (dict(rank=17), Q.QWM_ERR_UNSUPPORTED),
+    (dict(max_epochs=65), Q.QWM_ERR_UNSUPPORTED),
+    (dict(heads=0), Q.QWM_ERR_INVALID_ARG),
+    (dict(dtype=7), Q.QWM_ERR_INVALID_ARG),
+    (dict(capacity_tokens=0), Q.QWM_ERR_INVALID_ARG),
+    (dict(max_query_tokens=0), Q.QWM_ERR_INVALID_ARG),
+])
+def test_desc_validation(kw, status):
+    d = _desc(**kw)
+    n = ctypes.c_size_t(0)
+    assert Q.lib().qwm_arena_bytes(ctypes.byref(d), ctypes.byref(n)) == status
+    assert Q.last_error()
+
+
+def test_arena_bytes_accounts_for_every_region():
+    d = _desc()
+    nbytes = Q.arena_bytes(d)
+    H, D, cap, r, m = 2, 128, 1024, 8, 16  # capacity rounded to a 64-token tile
+    per_token = 2 * (D // 4) + 2 * (D // 32) * 4 + 1 + 2 * r
+    assert nbytes >= H * cap * per_token + 3 * H * m * D * 2
+    assert nbytes % 256 == 0
+
+
+def _handle(**kw):
+    d = _desc(**kw)
+    h = ctypes.c_void_p()
+    st = Q.lib().qwm_create(ctypes.byref(d), ctypes.c_void_p(1 << 20), Q.arena_bytes(d), None, ctypes.byref(h))
+    assert st == Q.QWM_OK, Q.last_error()
+    return h
+
+
+def test_create_checks_arena():
+    d = _desc()
+    h = ctypes.c_void_p()
+    L = Q.lib()
+    need = Q.arena_bytes(d)
+    assert L.qwm_create(ctypes.byref(d), None, need, None, ctypes.byref(h)) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_create(ctypes.byref(d), ctypes.c_void_p(256 + 16), need, None, ctypes.byref(h)) == \
+        Q.QWM_ERR_ARENA_TOO_SMALL
+    assert L.qwm_create(ctypes.byref(d), ctypes.c_void_p(256), need - 1, None, ctypes.byref(h)) == \
+        Q.QWM_ERR_ARENA_TOO_SMALL
+    assert L.qwm_create(ctypes.byref(d), ctypes.c_void_p(256), need, None, None) == Q.QWM_ERR_INVALID_ARG
+
+
+def test_call_order_and_argument_checks():
+    """State, capacity and argument errors are reported before any launch."""
+    L = Q.lib()
+    h = _handle()
+    P = ctypes.c_void_p(4096)
+    out = ctypes.c_void_p(8192)
+    assert L.qwm_quantize_append(h, P, P, 10) == Q.QWM_ERR_STATE
+    assert L.qwm_attend(h, P, 4, None, None, 0, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_STATE
+    assert L.qwm_build_centroids(h, P, 100, 3) == Q.QWM_ERR_STATE
+    assert L.qwm_build_centroids(h, P, 513, 3) == Q.QWM_ERR_CAPACITY
+    assert L.qwm_build_centroids(h, P, 0, 3) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_build_centroids(h, P, 10, -1) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_build_subspace(h, None, 10) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_build_subspace(h, ctypes.c_void_p(4096 + 2), 10) == Q.QWM_ERR_INVALID_ARG  # misaligned
+    assert L.qwm_build_subspace(h, P, 0) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_quantize_append(h, P, None, 10) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_quantize_append(h, P, P, -1) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend(h, P, 65, None, None, 0, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_CAPACITY
+    assert L.qwm_attend(h, P, 0, None, None, 0, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend(h, P, 4, None, None, 0, 5, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend(h, P, 4, None, None, 3, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend(h, P, 4, P, P, 3, 2, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG  # causal n_self != n_q
+    assert L.qwm_attend(h, P, 4, P, None, 4, 1, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend(h, P, 4, None, None, 0, 0, ctypes.c_float(float("nan")), out) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_truncate(h, 1) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_export_calibration(h, 0, P, None, None) == Q.QWM_ERR_INVALID_ARG
+    n = ctypes.c_int64(-1)
+    assert L.qwm_length(h, ctypes.byref(n)) == Q.QWM_OK and n.value == 0
+    e = ctypes.c_int32(-1)
+    assert L.qwm_epochs(h, ctypes.byref(e)) == Q.QWM_OK and e.value == 0
+    nb = ctypes.c_size_t(0)
+    assert L.qwm_export_bytes(h, 0, 1, ctypes.byref(nb)) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_export_bytes(h, 0, 0, ctypes.byref(nb)) == Q.QWM_OK and nb.value == 0
+    assert L.qwm_profile_read(h, 99, ctypes.byref(ctypes.c_double()), ctypes.byref(ctypes.c_int64())) == \
+        Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_destroy(h) == Q.QWM_OK
+    assert L.qwm_destroy(None) == Q.QWM_ERR_INVALID_ARG
+
+
+def test_no_oracle_in_product_path():
+    """The product package never imports the oracle."""
+    pkg = os.path.join(ROOT, "video_world_model_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f

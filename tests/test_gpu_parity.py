@@ -1,0 +1,241 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar: centroid ids, INT2 codes and fp16 zero-points/steps bit-exact given the
+same (imported) calibration; PSAC coefficients within one fp16 ulp (float64
+dot products summed in a different order may round differently); logits and
+attention outputs within 1e-3 of the row's largest magnitude."""
+
+import numpy as np
+import pytest
+
+import oracle.qwm_oracle as O
+import workloads as W
+from tests.gpu_helpers import (ROW_TOL, compare_records, import_calibration, log, oracle_calibration, row_rel_err,
+                               small, to_dev, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _cache(w, capacity=None, max_epochs=1, max_q=None, max_build=None):
+    from video_world_model_amd import Cache
+    return Cache(w.heads, w.head_dim, w.n_centroids, w.rank, capacity or w.n_kv, dtype=torch_dtype(w.dtype),
+                 max_epochs=max_epochs, max_query_tokens=max_q or max(w.n_q, 16),
+                 max_build_tokens=max_build or max(w.n_kv, 64))
+
+
+def _setup(w, n_kv, cal_keys, iters):
+    """Generator arrays + oracle calibration + oracle head caches for heads 0..H-1."""
+    gens = [W.HeadGen(w, h) for h in range(w.heads)]
+    keys = [g.keys(0, n_kv) for g in gens]
+    vals = [g.values(0, n_kv) for g in gens]
+    cals = [oracle_calibration(w, g, k[:cal_keys], g.hist_queries(), iters) for g, k in zip(gens, keys)]
+    return gens, keys, vals, cals
+
+
+@pytest.mark.parametrize("name,heads,n_kv,cal_keys,iters", [
+    ("tiny", 1, 1024, 1024, 10),
+    ("video_chunk", 12, 7040, 880, 2),
+])
+def test_quantize_bit_exact(name, heads, n_kv, cal_keys, iters):
+    w = small(W.workload(name), heads=heads, n_kv=n_kv)
+    log(f"[quantize parity] {name} H={heads} n={n_kv}")
+    gens, keys, vals, cals = _setup(w, n_kv, cal_keys, iters)
+    cache = _cache(w)
+    import_calibration(cache, cals, w.dtype)
+    cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+    dec = cache.decode_export(cache.export().cpu().numpy(), n_kv)
+    flips = 0
+    for h in range(heads):
+        rec = O.quantize_tokens(keys[h], vals[h], *cals[h], w.group)
+        flips += compare_records(dec, h, rec)
+    assert np.all(dec["epoch"] == 0)
+    log(f"  coef fp16 one-ulp differences: {flips} of {heads * n_kv * w.rank}")
+
+
+def _oracle_heads(w, keys, vals, cals):
+    hcs = []
+    for h in range(w.heads):
+        hc = O.HeadCache(w.group, w.dtype)
+        hc.add_epoch(*cals[h])
+        hc.append(keys[h], vals[h])
+        hcs.append(hc)
+    return hcs
+
+
+@pytest.mark.parametrize("name,heads,n_kv,n_q,mask", [
+    ("tiny", 1, 1024, 16, "none"),
+    ("video_chunk", 12, 7040, 880, "full"),
+    ("video_chunk", 2, 1000, 200, "none"),
+])
+def test_attend_matches_oracle(name, heads, n_kv, n_q, mask):
+    w = small(W.workload(name), heads=heads, n_kv=n_kv, n_q=n_q, n_self=n_q if mask != "none" else 0)
+    log(f"[attend parity] {name} H={heads} n_kv={n_kv} n_q={n_q} mask={mask}")
+    gens, keys, vals, cals = _setup(w, n_kv, min(n_kv, 880), 2)
+    cache = _cache(w)
+    import_calibration(cache, cals, w.dtype)
+    cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+    q = [g.current_queries()[:n_q] for g in gens]
+    ks = vs = None
+    if mask != "none":
+        ks = [g.keys(n_kv, n_kv + n_q) for g in gens]
+        vs = [g.values(n_kv, n_kv + n_q) for g in gens]
+        out = cache.attend(to_dev(q, w.dtype), to_dev(ks, w.dtype), to_dev(vs, w.dtype), mask=mask)
+    else:
+        out = cache.attend(to_dev(q, w.dtype))
+    out = out.cpu().numpy()
+    hcs = _oracle_heads(w, keys, vals, cals)
+    worst = 0.0
+    for h in range(heads):
+        ref = O.attend(q[h], hcs[h], None if ks is None else ks[h], None if vs is None else vs[h], mask=mask)
+        e = row_rel_err(out[h], ref)
+        worst = max(worst, float(e.max()))
+        assert e.max() <= ROW_TOL, f"head {h}: row error {e.max():.3e}"
+    log(f"  worst row error {worst:.3e}")
+
+
+@pytest.mark.parametrize("name,heads,n_kv,n_q", [("tiny", 1, 1024, 16), ("video_chunk", 2, 7040, 150)])
+def test_logits_match_oracle(name, heads, n_kv, n_q):
+    w = small(W.workload(name), heads=heads, n_kv=n_kv, n_q=n_q)
+    log(f"[logits parity] {name}")
+    gens, keys, vals, cals = _setup(w, n_kv, min(n_kv, 880), 2)
+    cache = _cache(w)
+    import_calibration(cache, cals, w.dtype)
+    cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+    q = [g.current_queries()[:n_q] for g in gens]
+    qd = to_dev(q, w.dtype)
+    hcs = _oracle_heads(w, keys, vals, cals)
+    scale = 1.0 / np.sqrt(w.head_dim)
+    for h in range(heads):
+        got = cache.attend_logits(qd, h).cpu().numpy()
+        ref = O.cache_logits(q[h], hcs[h], scale)
+        e = row_rel_err(got, ref)
+        log(f"  head {h}: worst logit row error {e.max():.3e}")
+        assert e.max() <= ROW_TOL
+
+
+def test_causal_self_segment_and_ragged_tiles():
+    """Token-causal self segment; cache and chunk lengths not multiples of 64."""
+    w = small(W.workload("video_chunk"), heads=2, n_kv=333, n_q=77, n_self=77)
+    log("[causal self] H=2 n_kv=333 n_q=77")
+    gens, keys, vals, cals = _setup(w, w.n_kv, 333, 2)
+    cache = _cache(w)
+    import_calibration(cache, cals, w.dtype)
+    cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+    q = [g.current_queries()[:77] for g in gens]
+    ks = [g.keys(333, 410) for g in gens]
+    vs = [g.values(333, 410) for g in gens]
+    out = cache.attend(to_dev(q, w.dtype), to_dev(ks, w.dtype), to_dev(vs, w.dtype), mask="causal").cpu().numpy()
+    hcs = _oracle_heads(w, keys, vals, cals)
+    for h in range(2):
+        ref = O.attend(q[h], hcs[h], ks[h], vs[h], mask="causal")
+        assert row_rel_err(out[h], ref).max() <= ROW_TOL
+
+
+def test_multi_epoch_cache():
+    """Three epochs with different calibrations and ragged epoch lengths;
+    tokens keep their epoch's centroids and subspace."""
+    w = small(W.workload("video_chunk"), heads=2, n_q=96)
+    lens = [700, 1300, 419]
+    log(f"[multi-epoch] lens={lens}")
+    gens = [W.HeadGen(w, h) for h in range(2)]
+    cache = _cache(w, capacity=sum(lens), max_epochs=3, max_q=96)
+    hcs = [O.HeadCache(w.group, w.dtype) for _ in range(2)]
+    t = 0
+    allk, allv = [[], []], [[], []]
+    for e, n in enumerate(lens):
+        keys = [g.keys(t, t + n) for g in gens]
+        vals = [g.values(t, t + n) for g in gens]
+        cals = [oracle_calibration(w, g, k[:300], g.hist_queries(e), 1) for g, k in zip(gens, keys)]
+        import_calibration(cache, cals, w.dtype)
+        cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+        for h in range(2):
+            hcs[h].add_epoch(*cals[h])
+            hcs[h].append(keys[h], vals[h])
+        t += n
+    assert cache.epochs() == 3 and cache.length() == sum(lens)
+    dec = cache.decode_export(cache.export().cpu().numpy(), sum(lens))
+    for h in range(2):
+        off = 0
+        for (start, rec) in hcs[h].records:
+            compare_records(dec, h, rec, start)
+        assert np.array_equal(dec["epoch"][h], hcs[h].field("epoch"))
+    q = [g.current_queries()[:96] for g in gens]
+    out = cache.attend(to_dev(q, w.dtype)).cpu().numpy()
+    for h in range(2):
+        ref = O.attend(q[h], hcs[h])
+        assert row_rel_err(out[h], ref).max() <= ROW_TOL
+
+
+def test_append_in_pieces_and_truncate():
+    w = small(W.workload("video_chunk"), heads=3, n_kv=1000)
+    log("[append pieces / truncate]")
+    gens, keys, vals, cals = _setup(w, 1000, 500, 1)
+    a = _cache(w)
+    import_calibration(a, cals, w.dtype)
+    a.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+    b = _cache(w)
+    import_calibration(b, cals, w.dtype)
+    for s in (0, 130, 131, 600):
+        e = {0: 130, 130: 131, 131: 600, 600: 1000}[s]
+        b.quantize_append(to_dev([k[s:e] for k in keys], w.dtype), to_dev([v[s:e] for v in vals], w.dtype))
+    ea, eb = a.export().cpu().numpy(), b.export().cpu().numpy()
+    assert np.array_equal(ea, eb)
+    # rewind and append again: identical bits
+    b.truncate(131)
+    b.quantize_append(to_dev([k[131:] for k in keys], w.dtype), to_dev([v[131:] for v in vals], w.dtype))
+    assert np.array_equal(b.export().cpu().numpy(), ea)
+
+
+def test_determinism():
+    w = small(W.workload("video_chunk"), heads=4, n_kv=2000, n_q=300, n_self=300)
+    gens, keys, vals, cals = _setup(w, 2000, 500, 1)
+    outs = []
+    for _ in range(2):
+        c = _cache(w)
+        import_calibration(c, cals, w.dtype)
+        c.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+        q = [g.current_queries()[:300] for g in gens]
+        ks = [g.keys(2000, 2300) for g in gens]
+        vs = [g.values(2000, 2300) for g in gens]
+        o = c.attend(to_dev(q, w.dtype), to_dev(ks, w.dtype), to_dev(vs, w.dtype), mask="full")
+        outs.append((c.export().cpu().numpy(), o.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
+
+@pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1024, 10), ("video_chunk", 4, 1760, 4)])
+def test_build_calibration(name, heads, n_keys, iters):
+    """GPU-built calibration: S_G bit-exact (exact float64 sums of bf16/fp32
+    squares), U_r spans the oracle's subspace (projector within 1e-4), and the
+    GPU k-means reaches the oracle's mean QSAC objective within 1%."""
+    w = small(W.workload(name), heads=heads)
+    log(f"[build] {name} H={heads} n_keys={n_keys} iters={iters}")
+    gens = [W.HeadGen(w, h) for h in range(heads)]
+    qh = [g.hist_queries() for g in gens]
+    keys = [g.keys(0, n_keys) for g in gens]
+    cache = _cache(w, max_build=n_keys)
+    cache.build_subspace(to_dev(qh, w.dtype))
+    cache.build_centroids(to_dev(keys, w.dtype), iters)
+    C, S, U = (t.cpu() for t in cache.export_calibration(0))
+    C = C.float().numpy()
+    S = S.numpy()
+    U = U.numpy()
+    for h in range(heads):
+        So = O.sensitivity(qh[h], w.group)
+        Uo = O.subspace(qh[h], w.rank)
+        if w.dtype == "bf16":
+            assert np.array_equal(S[h], So), (S[h], So)  # exact float64 sums of bf16 squares
+        else:
+            assert np.all(np.abs(S[h] - So) <= np.spacing(So)), (S[h], So)
+        P1 = U[h].astype(np.float64) @ U[h].astype(np.float64).T
+        P2 = Uo.astype(np.float64) @ Uo.astype(np.float64).T
+        perr = np.linalg.norm(P1 - P2) / np.linalg.norm(P2)
+        log(f"  head {h}: projector error {perr:.2e}")
+        assert perr < 1e-4
+        Co = O.build_centroids(keys[h], So, w.n_centroids, w.group, iters, w.dtype)
+        jg = O.mean_objective(keys[h], C[h], So, w.group)
+        jo = O.mean_objective(keys[h], Co, So, w.group)
+        log(f"  head {h}: mean J gpu {jg:.6g} oracle {jo:.6g} bit-identical centroids {np.array_equal(C[h], Co)}")
+        assert abs(jg - jo) <= 0.01 * jo

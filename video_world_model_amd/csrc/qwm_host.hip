@@ -1,0 +1,657 @@
+// Host side of the QuantWM 2-bit KV cache library: argument checks, arena
+// layout, the epoch directory, split-KV planning and kernel launches.
+// Every public entry point is declared (and documented) in include/qwm.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "qwm.h"
+#include "qwm_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qwm_status fail(qwm_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+qwm_status fail_hip(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return QWM_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  size_t kcode, vcode, kparam, vparam, ids, coef;
+  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, build_ids, qU, part_o, part_ml;
+  size_t total;
+  int64_t capP, part_rows;
+};
+
+qwm_status check_desc(const qwm_desc* d) {
+  if (!d) return fail(QWM_ERR_INVALID_ARG, "desc is NULL");
+  if (d->heads < 1) return fail(QWM_ERR_INVALID_ARG, "heads must be >= 1");
+  if (d->dtype != QWM_BF16 && d->dtype != QWM_F32) return fail(QWM_ERR_INVALID_ARG, "dtype must be QWM_BF16 or QWM_F32");
+  if (d->reserved != 0) return fail(QWM_ERR_INVALID_ARG, "reserved must be 0");
+  if (d->capacity_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "capacity_tokens must be >= 1");
+  if (d->max_query_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "max_query_tokens must be >= 1");
+  if (d->max_build_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "max_build_tokens must be >= 1");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(QWM_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->group != qwm::kGroup) return fail(QWM_ERR_UNSUPPORTED, "group must be 32");
+  if (d->n_centroids < 1 || d->n_centroids > 256) return fail(QWM_ERR_UNSUPPORTED, "n_centroids must be 1..256");
+  if (d->rank < 1 || d->rank > qwm::kRankPad) return fail(QWM_ERR_UNSUPPORTED, "rank must be 1..16");
+  if (d->max_epochs < 1 || d->max_epochs > qwm::kMaxEpochs) return fail(QWM_ERR_UNSUPPORTED, "max_epochs must be 1..64");
+  if (d->capacity_tokens > (int64_t)INT32_MAX - 2 * qwm::kTileKV)
+    return fail(QWM_ERR_UNSUPPORTED, "capacity_tokens beyond 2^31 - 128");
+  if (d->max_query_tokens > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_UNSUPPORTED, "max_query_tokens too large");
+  if (d->max_build_tokens > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_UNSUPPORTED, "max_build_tokens too large");
+  return QWM_OK;
+}
+
+Layout make_layout(const qwm_desc* d) {
+  Layout L{};
+  const int64_t H = d->heads, D = d->head_dim, nG = D / qwm::kGroup, m = d->n_centroids, r = d->rank;
+  const int64_t E = d->max_epochs, esz = d->dtype == QWM_BF16 ? 2 : 4;
+  const int64_t maxq = d->max_query_tokens;
+  L.capP = (d->capacity_tokens + qwm::kTileKV - 1) / qwm::kTileKV * qwm::kTileKV;
+  const int64_t big = 1 << 18;
+  int64_t pr = 2 * H * maxq > big ? 2 * H * maxq : big;
+  if (pr > 16 * H * maxq) pr = 16 * H * maxq;
+  L.part_rows = pr;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.kcode = take((size_t)(H * L.capP * D / 4));
+  L.vcode = take((size_t)(H * L.capP * D / 4));
+  L.kparam = take((size_t)(H * L.capP * nG * 4));
+  L.vparam = take((size_t)(H * L.capP * nG * 4));
+  L.ids = take((size_t)(H * L.capP));
+  L.coef = take((size_t)(H * L.capP * r * 2));
+  L.epochC = take((size_t)((E + 1) * H * m * D * esz));
+  L.epochS = take((size_t)((E + 1) * H * nG * 4));
+  L.epochU = take((size_t)((E + 1) * H * D * r * 4));
+  L.C32 = take((size_t)(H * m * D * 4));
+  L.kmC32 = take((size_t)(H * m * D * 4));
+  L.U64 = take((size_t)(H * D * r * 8));
+  L.gram = take((size_t)(H * D * D * 8));
+  L.build_ids = take((size_t)(H * d->max_build_tokens));
+  L.qU = take((size_t)(H * E * maxq * qwm::kRankPad * 4));
+  L.part_o = take((size_t)(pr * D * 4));
+  L.part_ml = take((size_t)(pr * 2 * 4));
+  L.total = off;
+  return L;
+}
+
+struct DeviceGuard {
+  int prev = -1, dev;
+  explicit DeviceGuard(int d) : dev(d) {
+    if (dev < 0) return;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0 && prev != dev) (void)hipSetDevice(prev);
+  }
+};
+
+struct ProfRec {
+  int kid;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct qwm_cache {
+  qwm_desc desc{};
+  Layout L{};
+  int H = 0, D = 0, nG = 0, m = 0, r = 0, dtype = 0, esz = 0;
+  int device = 0;
+  hipStream_t stream = nullptr;
+  uint8_t* arena = nullptr;
+  qwm::CacheView view{};
+  int64_t length = 0;
+  std::vector<int64_t> epoch_start;  // committed epoch i lives in slot i
+  bool staged_subspace = false;
+  bool profile = false;
+  std::vector<ProfRec> pending;
+  double prof_ms[QWM_K_COUNT] = {};
+  int64_t prof_n[QWM_K_COUNT] = {};
+
+  uint8_t* slotC(int slot) const {
+    return arena + L.epochC + (size_t)slot * H * m * D * esz;
+  }
+  float* slotS(int slot) const {
+    return reinterpret_cast<float*>(arena + L.epochS) + (size_t)slot * H * nG;
+  }
+  float* slotU(int slot) const {
+    return reinterpret_cast<float*>(arena + L.epochU) + (size_t)slot * H * D * r;
+  }
+  int staged() const { return desc.max_epochs; }
+  float* C32() const { return reinterpret_cast<float*>(arena + L.C32); }
+  float* kmC32() const { return reinterpret_cast<float*>(arena + L.kmC32); }
+  double* U64() const { return reinterpret_cast<double*>(arena + L.U64); }
+  double* gram() const { return reinterpret_cast<double*>(arena + L.gram); }
+  uint8_t* build_ids() const { return arena + L.build_ids; }
+  float* qU() const { return reinterpret_cast<float*>(arena + L.qU); }
+  float* part_o() const { return reinterpret_cast<float*>(arena + L.part_o); }
+  float* part_ml() const { return reinterpret_cast<float*>(arena + L.part_ml); }
+
+  // Launch wrapper: optional event timing around one launch.
+  template <class F>
+  hipError_t run(int kid, F&& f) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (profile) {
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return hipErrorOutOfMemory;
+      (void)hipEventRecord(a, stream);
+    }
+    hipError_t e = f();
+    if (profile) {
+      (void)hipEventRecord(b, stream);
+      pending.push_back({kid, a, b});
+    }
+    return e;
+  }
+};
+
+namespace {
+
+qwm_status check_cache(const qwm_cache* c) {
+  if (!c) return fail(QWM_ERR_INVALID_ARG, "cache is NULL");
+  return QWM_OK;
+}
+
+qwm_status need_device(const qwm_cache* c) {
+  if (c->device < 0) return fail(QWM_ERR_HIP, "no HIP device was available when the cache was created");
+  return QWM_OK;
+}
+
+qwm_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(QWM_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(QWM_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+  return QWM_OK;
+}
+
+// Commit the staged calibration as a new epoch (or in place of an epoch that
+// holds no token yet). Capacity was checked by the caller.
+qwm_status commit_staged(qwm_cache* c) {
+  int slot = (int)c->epoch_start.size();
+  if (!c->epoch_start.empty() && c->epoch_start.back() == c->length) slot -= 1;
+  const int st = c->staged();
+  const size_t bC = (size_t)c->H * c->m * c->D * c->esz, bS = (size_t)c->H * c->nG * 4,
+               bU = (size_t)c->H * c->D * c->r * 4;
+  hipError_t e;
+  if ((e = hipMemcpyAsync(c->slotC(slot), c->slotC(st), bC, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
+    return fail_hip(e, "commit C");
+  if ((e = hipMemcpyAsync(c->slotS(slot), c->slotS(st), bS, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
+    return fail_hip(e, "commit S");
+  if ((e = hipMemcpyAsync(c->slotU(slot), c->slotU(st), bU, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
+    return fail_hip(e, "commit U");
+  e = c->run(QWM_K_OTHER, [&] {
+    return qwm::launch_shadow(c->D, c->dtype, c->slotC(slot), c->slotU(slot), c->H, c->m, c->r, c->C32(), c->U64(),
+                              c->stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "shadow");
+  if (slot == (int)c->epoch_start.size())
+    c->epoch_start.push_back(c->length);
+  else
+    c->epoch_start[slot] = c->length;
+  c->staged_subspace = false;
+  return QWM_OK;
+}
+
+bool epoch_room(const qwm_cache* c) {
+  if (!c->epoch_start.empty() && c->epoch_start.back() == c->length) return true;  // replaces an empty epoch
+  return (int)c->epoch_start.size() < c->desc.max_epochs;
+}
+
+// Segments of the cache (one per epoch holding tokens) plus the self segment.
+void make_plan(const qwm_cache* c, int64_t nself, bool with_self, qwm::AttnPlan& p) {
+  std::memset(&p, 0, sizeof(p));
+  int n = 0;
+  const int E = (int)c->epoch_start.size();
+  for (int e = 0; e < E; ++e) {
+    const int64_t s = c->epoch_start[e];
+    const int64_t t = (e + 1 < E) ? c->epoch_start[e + 1] : c->length;
+    if (t > s) {
+      p.seg_start[n] = (int32_t)s;
+      p.seg_len[n] = (int32_t)(t - s);
+      p.seg_epoch[n] = e;
+      ++n;
+    }
+  }
+  if (with_self && nself > 0) {
+    p.seg_start[n] = 0;
+    p.seg_len[n] = (int32_t)nself;
+    p.seg_epoch[n] = -1;
+    ++n;
+  }
+  p.n_seg = n;
+  p.tile_prefix[0] = 0;
+  for (int i = 0; i < n; ++i)
+    p.tile_prefix[i + 1] = p.tile_prefix[i] + (p.seg_len[i] + qwm::kTileKV - 1) / qwm::kTileKV;
+}
+
+qwm::AttnArgs base_args(qwm_cache* c) {
+  qwm::AttnArgs a{};
+  a.cache = c->view;
+  a.Cbase = c->slotC(0);
+  a.epoch_C_stride = (int64_t)c->H * c->m * c->D * c->esz;
+  a.H = c->H;
+  a.m = c->m;
+  a.r = c->r;
+  a.part_o = c->part_o();
+  a.part_ml = c->part_ml();
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qwm_last_error(void) { return g_last_error.c_str(); }
+const char* qwm_version(void) { return "qwm 0.1 gfx950"; }
+
+qwm_status qwm_arena_bytes(const qwm_desc* desc, size_t* bytes) {
+  qwm_status st = check_desc(desc);
+  if (st != QWM_OK) return st;
+  if (!bytes) return fail(QWM_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_layout(desc).total;
+  return QWM_OK;
+}
+
+qwm_status qwm_create(const qwm_desc* desc, void* dev_arena, size_t arena_bytes, void* stream, qwm_cache** out) {
+  qwm_status st = check_desc(desc);
+  if (st != QWM_OK) return st;
+  if (!out) return fail(QWM_ERR_INVALID_ARG, "out is NULL");
+  if (!dev_arena) return fail(QWM_ERR_INVALID_ARG, "dev_arena is NULL");
+  const Layout L = make_layout(desc);
+  if ((reinterpret_cast<uintptr_t>(dev_arena) % kAlign) != 0)
+    return fail(QWM_ERR_ARENA_TOO_SMALL, "dev_arena must be 256-byte aligned");
+  if (arena_bytes < L.total)
+    return fail(QWM_ERR_ARENA_TOO_SMALL, "arena has " + std::to_string(arena_bytes) + " bytes, needs " +
+                                             std::to_string(L.total));
+  // Without a usable HIP device the handle still exists (device -1) so that
+  // every argument and state check can run; calls that would enqueue work
+  // then fail with QWM_ERR_HIP after their checks.
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  qwm_cache* c = new qwm_cache();
+  c->desc = *desc;
+  c->L = L;
+  c->H = desc->heads;
+  c->D = desc->head_dim;
+  c->nG = desc->head_dim / qwm::kGroup;
+  c->m = desc->n_centroids;
+  c->r = desc->rank;
+  c->dtype = desc->dtype;
+  c->esz = desc->dtype == QWM_BF16 ? 2 : 4;
+  c->device = dev;
+  c->stream = reinterpret_cast<hipStream_t>(stream);
+  c->arena = reinterpret_cast<uint8_t*>(dev_arena);
+  c->view.kcode = c->arena + L.kcode;
+  c->view.vcode = c->arena + L.vcode;
+  c->view.kparam = reinterpret_cast<uint32_t*>(c->arena + L.kparam);
+  c->view.vparam = reinterpret_cast<uint32_t*>(c->arena + L.vparam);
+  c->view.ids = c->arena + L.ids;
+  c->view.coef = reinterpret_cast<uint16_t*>(c->arena + L.coef);
+  c->view.capP = L.capP;
+  *out = c;
+  return QWM_OK;
+}
+
+qwm_status qwm_destroy(qwm_cache* c) {
+  if (!c) return fail(QWM_ERR_INVALID_ARG, "cache is NULL");
+  for (auto& rec : c->pending) {
+    (void)hipEventDestroy(rec.a);
+    (void)hipEventDestroy(rec.b);
+  }
+  delete c;
+  return QWM_OK;
+}
+
+qwm_status qwm_build_subspace(qwm_cache* c, const void* q_hist, int64_t n_hist) {
+  qwm_status st;
+  if ((st = check_cache(c)) != QWM_OK) return st;
+  if ((st = check_ptr(q_hist, "q_hist")) != QWM_OK) return st;
+  if (n_hist < 1) return fail(QWM_ERR_INVALID_ARG, "n_hist must be >= 1");
+  if (n_hist > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_CAPACITY, "n_hist too large");
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  const int st_slot = c->staged();
+  hipError_t e = c->run(QWM_K_GRAM, [&] {
+    return qwm::launch_gram(c->D, c->dtype, q_hist, n_hist, c->H, c->gram(), c->stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "gram");
+  e = c->run(QWM_K_EIGEN, [&] {
+    return qwm::launch_eigen(c->D, c->gram(), n_hist, c->H, c->r, c->slotU(st_slot), c->slotS(st_slot), c->stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "eigen");
+  c->staged_subspace = true;
+  return QWM_OK;
+}
+
+qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, int32_t iters) {
+  qwm_status st;
+  if ((st = check_cache(c)) != QWM_OK) return st;
+  if ((st = check_ptr(keys, "keys")) != QWM_OK) return st;
+  if (n_keys < 1) return fail(QWM_ERR_INVALID_ARG, "n_keys must be >= 1");
+  if (iters < 0) return fail(QWM_ERR_INVALID_ARG, "iters must be >= 0");
+  if (n_keys > c->desc.max_build_tokens) return fail(QWM_ERR_CAPACITY, "n_keys exceeds max_build_tokens");
+  if (!c->staged_subspace) return fail(QWM_ERR_STATE, "build_centroids needs build_subspace first");
+  if (!epoch_room(c)) return fail(QWM_ERR_CAPACITY, "max_epochs reached");
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  const int stg = c->staged();
+  hipError_t e = c->run(QWM_K_OTHER, [&] {
+    return qwm::launch_kmeans_seed(c->D, c->dtype, keys, n_keys, c->H, c->m, c->slotC(stg), c->kmC32(), c->stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "kmeans seed");
+  for (int it = 0; it < iters; ++it) {
+    qwm::QuantArgs a{};
+    a.k = keys;
+    a.v = nullptr;
+    a.n = n_keys;
+    a.C32 = c->kmC32();
+    a.S = c->slotS(stg);
+    a.ids_out = c->build_ids();
+    a.H = c->H;
+    a.m = c->m;
+    a.r = c->r;
+    e = c->run(QWM_K_ASSIGN, [&] { return qwm::launch_quantize(c->D, c->dtype, a, c->stream); });
+    if (e != hipSuccess) return fail_hip(e, "kmeans assign");
+    e = c->run(QWM_K_UPDATE, [&] {
+      return qwm::launch_kmeans_update(c->D, c->dtype, keys, c->build_ids(), n_keys, c->H, c->m, c->slotC(stg),
+                                       c->kmC32(), c->stream);
+    });
+    if (e != hipSuccess) return fail_hip(e, "kmeans update");
+  }
+  return commit_staged(c);
+}
+
+qwm_status qwm_import_calibration(qwm_cache* c, const void* C, const float* S_G, const float* U_r) {
+  qwm_status st;
+  if ((st = check_cache(c)) != QWM_OK) return st;
+  if ((st = check_ptr(C, "C")) != QWM_OK) return st;
+  if ((st = check_ptr(S_G, "S_G")) != QWM_OK) return st;
+  if ((st = check_ptr(U_r, "U_r")) != QWM_OK) return st;
+  if (!epoch_room(c)) return fail(QWM_ERR_CAPACITY, "max_epochs reached");
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  const int stg = c->staged();
+  hipError_t e;
+  if ((e = hipMemcpyAsync(c->slotC(stg), C, (size_t)c->H * c->m * c->D * c->esz, hipMemcpyDeviceToDevice,
+                          c->stream)) != hipSuccess)
+    return fail_hip(e, "import C");
+  if ((e = hipMemcpyAsync(c->slotS(stg), S_G, (size_t)c->H * c->nG * 4, hipMemcpyDeviceToDevice, c->stream)) !=
+      hipSuccess)
+    return fail_hip(e, "import S");
+  if ((e = hipMemcpyAsync(c->slotU(stg), U_r, (size_t)c->H * c->D * c->r * 4, hipMemcpyDeviceToDevice,
+                          c->stream)) != hipSuccess)
+    return fail_hip(e, "import U");
+  return commit_staged(c);
+}
+
+qwm_status qwm_export_calibration(const qwm_cache* cc, int32_t epoch, void* C, float* S_G, float* U_r) {
+  qwm_status st;
+  if ((st = check_cache(cc)) != QWM_OK) return st;
+  qwm_cache* c = const_cast<qwm_cache*>(cc);
+  if (epoch < -1 || epoch >= (int)c->epoch_start.size()) return fail(QWM_ERR_INVALID_ARG, "no such epoch");
+  const int slot = epoch < 0 ? c->staged() : epoch;
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  hipError_t e;
+  if (C && (e = hipMemcpyAsync(C, c->slotC(slot), (size_t)c->H * c->m * c->D * c->esz, hipMemcpyDeviceToDevice,
+                               c->stream)) != hipSuccess)
+    return fail_hip(e, "export C");
+  if (S_G && (e = hipMemcpyAsync(S_G, c->slotS(slot), (size_t)c->H * c->nG * 4, hipMemcpyDeviceToDevice,
+                                 c->stream)) != hipSuccess)
+    return fail_hip(e, "export S");
+  if (U_r && (e = hipMemcpyAsync(U_r, c->slotU(slot), (size_t)c->H * c->D * c->r * 4, hipMemcpyDeviceToDevice,
+                                 c->stream)) != hipSuccess)
+    return fail_hip(e, "export U");
+  return QWM_OK;
+}
+
+qwm_status qwm_quantize_append(qwm_cache* c, const void* k, const void* v, int64_t n_tokens) {
+  qwm_status st;
+  if ((st = check_cache(c)) != QWM_OK) return st;
+  if ((st = check_ptr(k, "k")) != QWM_OK) return st;
+  if ((st = check_ptr(v, "v")) != QWM_OK) return st;
+  if (n_tokens < 0) return fail(QWM_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (c->epoch_start.empty()) return fail(QWM_ERR_STATE, "quantize_append before a committed epoch");
+  if (c->length + n_tokens > c->desc.capacity_tokens) return fail(QWM_ERR_CAPACITY, "capacity exceeded");
+  if (n_tokens == 0) return QWM_OK;
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  const int slot = (int)c->epoch_start.size() - 1;
+  qwm::QuantArgs a{};
+  a.k = k;
+  a.v = v;
+  a.n = n_tokens;
+  a.C32 = c->C32();
+  a.S = c->slotS(slot);
+  a.U64 = c->U64();
+  a.cache = c->view;
+  a.pos0 = c->length;
+  a.H = c->H;
+  a.m = c->m;
+  a.r = c->r;
+  hipError_t e = c->run(QWM_K_QUANTIZE, [&] { return qwm::launch_quantize(c->D, c->dtype, a, c->stream); });
+  if (e != hipSuccess) return fail_hip(e, "quantize");
+  c->length += n_tokens;
+  return QWM_OK;
+}
+
+qwm_status qwm_attend(qwm_cache* c, const void* q, int64_t n_q, const void* k_self, const void* v_self,
+                      int64_t n_self, int32_t mask, float softmax_scale, float* out) {
+  qwm_status st;
+  if ((st = check_cache(c)) != QWM_OK) return st;
+  if ((st = check_ptr(q, "q")) != QWM_OK) return st;
+  if ((st = check_ptr(out, "out")) != QWM_OK) return st;
+  if (n_q < 1) return fail(QWM_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (n_q > c->desc.max_query_tokens) return fail(QWM_ERR_CAPACITY, "n_q exceeds max_query_tokens");
+  if (mask != QWM_SELF_NONE && mask != QWM_SELF_FULL && mask != QWM_SELF_CAUSAL)
+    return fail(QWM_ERR_INVALID_ARG, "bad mask");
+  if (!std::isfinite(softmax_scale) || softmax_scale == 0.0f)
+    return fail(QWM_ERR_INVALID_ARG, "softmax_scale must be finite and nonzero");
+  if (mask == QWM_SELF_NONE) {
+    if (n_self != 0) return fail(QWM_ERR_INVALID_ARG, "n_self must be 0 with QWM_SELF_NONE");
+  } else {
+    if (n_self < 1) return fail(QWM_ERR_INVALID_ARG, "a self mask needs n_self >= 1");
+    if (n_self > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_CAPACITY, "n_self too large");
+    if ((st = check_ptr(k_self, "k_self")) != QWM_OK) return st;
+    if ((st = check_ptr(v_self, "v_self")) != QWM_OK) return st;
+    if (mask == QWM_SELF_CAUSAL && n_self != n_q) return fail(QWM_ERR_INVALID_ARG, "causal self needs n_self == n_q");
+  }
+  if (c->epoch_start.empty()) return fail(QWM_ERR_STATE, "attend before a committed epoch");
+  if (c->length == 0 && mask == QWM_SELF_NONE) return fail(QWM_ERR_STATE, "nothing to attend to");
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  qwm::AttnPlan p;
+  make_plan(c, n_self, mask != QWM_SELF_NONE, p);
+  const int T = p.tile_prefix[p.n_seg];
+  const int E = (int)c->epoch_start.size();
+  qwm::AttnArgs a = base_args(c);
+  a.q = q;
+  a.qU = c->qU();
+  a.kself = k_self;
+  a.vself = v_self;
+  a.nq = n_q;
+  a.nself = n_self;
+  a.causal_self = (mask == QWM_SELF_CAUSAL) ? 1 : 0;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.n_epoch_slots = E;
+  a.out = out;
+  const int64_t qtiles = (n_q + qwm::kTileQ - 1) / qwm::kTileQ;
+  int64_t splits = (1024 + qtiles * c->H - 1) / (qtiles * c->H);
+  if (splits > 16) splits = 16;
+  if (splits > T) splits = T;
+  while (splits > 1 && splits * c->H * n_q > c->L.part_rows) --splits;
+  if (splits < 1) splits = 1;
+  a.splits = (int)splits;
+  hipError_t e = c->run(QWM_K_QU, [&] {
+    return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
+                          c->stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "qU");
+  e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_attend(c->D, c->dtype, a, p, c->stream); });
+  if (e != hipSuccess) return fail_hip(e, "attend");
+  if (a.splits > 1) {
+    e = c->run(QWM_K_MERGE, [&] { return qwm::launch_merge(c->D, a, c->stream); });
+    if (e != hipSuccess) return fail_hip(e, "merge");
+  }
+  return QWM_OK;
+}
+
+qwm_status qwm_attend_logits(qwm_cache* c, const void* q, int64_t n_q, int32_t head, float softmax_scale,
+                             float* logits) {
+  qwm_status st;
+  if ((st = check_cache(c)) != QWM_OK) return st;
+  if ((st = check_ptr(q, "q")) != QWM_OK) return st;
+  if ((st = check_ptr(logits, "logits")) != QWM_OK) return st;
+  if (n_q < 1) return fail(QWM_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (n_q > c->desc.max_query_tokens) return fail(QWM_ERR_CAPACITY, "n_q exceeds max_query_tokens");
+  if (head < 0 || head >= c->H) return fail(QWM_ERR_INVALID_ARG, "head out of range");
+  if (!std::isfinite(softmax_scale)) return fail(QWM_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (c->epoch_start.empty() || c->length == 0) return fail(QWM_ERR_STATE, "empty cache");
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  qwm::AttnPlan p;
+  make_plan(c, 0, false, p);
+  const int T = p.tile_prefix[p.n_seg];
+  const int E = (int)c->epoch_start.size();
+  qwm::AttnArgs a = base_args(c);
+  a.q = q;
+  a.qU = c->qU();
+  a.nq = n_q;
+  a.scale = softmax_scale;
+  a.n_epoch_slots = E;
+  a.logits = logits;
+  a.logit_head = head;
+  a.logit_len = c->length;
+  a.splits = T < 64 ? T : 64;
+  hipError_t e = c->run(QWM_K_QU, [&] {
+    return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
+                          c->stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "qU");
+  e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_attend_logits(c->D, c->dtype, a, p, c->stream); });
+  if (e != hipSuccess) return fail_hip(e, "attend_logits");
+  return QWM_OK;
+}
+
+qwm_status qwm_length(const qwm_cache* c, int64_t* n_tokens) {
+  if (!c || !n_tokens) return fail(QWM_ERR_INVALID_ARG, "NULL argument");
+  *n_tokens = c->length;
+  return QWM_OK;
+}
+
+qwm_status qwm_epochs(const qwm_cache* c, int32_t* n_epochs) {
+  if (!c || !n_epochs) return fail(QWM_ERR_INVALID_ARG, "NULL argument");
+  *n_epochs = (int32_t)c->epoch_start.size();
+  return QWM_OK;
+}
+
+qwm_status qwm_truncate(qwm_cache* c, int64_t n_tokens) {
+  if (!c) return fail(QWM_ERR_INVALID_ARG, "cache is NULL");
+  if (n_tokens < 0 || n_tokens > c->length) return fail(QWM_ERR_INVALID_ARG, "n_tokens must be in [0, length]");
+  const size_t before = c->epoch_start.size();
+  c->length = n_tokens;
+  while (c->epoch_start.size() > 1 && c->epoch_start.back() > n_tokens) c->epoch_start.pop_back();
+  if (c->epoch_start.size() != before && !c->epoch_start.empty()) {
+    qwm_status st;
+    if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+    const int slot = (int)c->epoch_start.size() - 1;
+    hipError_t e = c->run(QWM_K_OTHER, [&] {
+      return qwm::launch_shadow(c->D, c->dtype, c->slotC(slot), c->slotU(slot), c->H, c->m, c->r, c->C32(),
+                                c->U64(), c->stream);
+    });
+    if (e != hipSuccess) return fail_hip(e, "shadow");
+  }
+  return QWM_OK;
+}
+
+qwm_status qwm_export_bytes(const qwm_cache* c, int64_t t0, int64_t t1, size_t* bytes) {
+  if (!c || !bytes) return fail(QWM_ERR_INVALID_ARG, "NULL argument");
+  if (t0 < 0 || t1 < t0 || t1 > c->length) return fail(QWM_ERR_INVALID_ARG, "need 0 <= t0 <= t1 <= length");
+  *bytes = (size_t)c->H * (size_t)(t1 - t0) * (size_t)(c->D / 2 + 8 * c->nG + 1 + 2 * c->r + 2);
+  return QWM_OK;
+}
+
+qwm_status qwm_export(const qwm_cache* cc, int64_t t0, int64_t t1, void* dev_buf) {
+  if (!cc) return fail(QWM_ERR_INVALID_ARG, "cache is NULL");
+  if (!dev_buf) return fail(QWM_ERR_INVALID_ARG, "dev_buf is NULL");
+  if (t0 < 0 || t1 < t0 || t1 > cc->length) return fail(QWM_ERR_INVALID_ARG, "need 0 <= t0 <= t1 <= length");
+  qwm_cache* c = const_cast<qwm_cache*>(cc);
+  qwm_status st;
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  qwm::ExportArgs a{};
+  a.cache = c->view;
+  a.t0 = t0;
+  a.n = t1 - t0;
+  a.n_epochs = (int)c->epoch_start.size();
+  for (int i = 0; i < a.n_epochs; ++i) a.epoch_start[i] = (int32_t)c->epoch_start[i];
+  a.H = c->H;
+  a.D = c->D;
+  a.nG = c->nG;
+  a.r = c->r;
+  a.out = reinterpret_cast<uint8_t*>(dev_buf);
+  hipError_t e = c->run(QWM_K_OTHER, [&] { return qwm::launch_export(a, c->stream); });
+  if (e != hipSuccess) return fail_hip(e, "export");
+  return QWM_OK;
+}
+
+qwm_status qwm_profile_enable(qwm_cache* c, int32_t enable) {
+  if (!c) return fail(QWM_ERR_INVALID_ARG, "cache is NULL");
+  for (auto& rec : c->pending) {
+    (void)hipEventDestroy(rec.a);
+    (void)hipEventDestroy(rec.b);
+  }
+  c->pending.clear();
+  for (int i = 0; i < QWM_K_COUNT; ++i) {
+    c->prof_ms[i] = 0.0;
+    c->prof_n[i] = 0;
+  }
+  c->profile = enable != 0;
+  return QWM_OK;
+}
+
+qwm_status qwm_profile_read(qwm_cache* c, int32_t kid, double* total_ms, int64_t* launches) {
+  if (!c || !total_ms || !launches) return fail(QWM_ERR_INVALID_ARG, "NULL argument");
+  if (kid < 0 || kid >= QWM_K_COUNT) return fail(QWM_ERR_INVALID_ARG, "bad kernel id");
+  qwm_status st;
+  if (!c->pending.empty() && (st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  for (auto& rec : c->pending) {
+    hipError_t e = hipEventSynchronize(rec.b);
+    if (e != hipSuccess) return fail_hip(e, "profile sync");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, rec.a, rec.b);
+    if (e != hipSuccess) return fail_hip(e, "profile elapsed");
+    c->prof_ms[rec.kid] += ms;
+    c->prof_n[rec.kid] += 1;
+    (void)hipEventDestroy(rec.a);
+    (void)hipEventDestroy(rec.b);
+  }
+  c->pending.clear();
+  *total_ms = c->prof_ms[kid];
+  *launches = c->prof_n[kid];
+  return QWM_OK;
+}
+
+}  // extern "C"

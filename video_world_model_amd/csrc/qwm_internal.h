@@ -1,0 +1,117 @@
+// Internal declarations shared by the host library and the kernel translation
+// units of the QuantWM 2-bit KV cache (gfx950). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qwm {
+
+constexpr int kGroup = 32;       // channels per INT2 group
+constexpr int kRankPad = 16;     // PSAC rank padded for the MFMA contraction
+constexpr int kTileKV = 64;      // tokens per attention tile
+constexpr int kTileQ = 128;      // Queries per attention workgroup (4 waves x 32)
+constexpr int kMaxEpochs = 64;
+constexpr int kMaxSegments = kMaxEpochs + 1;  // epochs + the self segment
+constexpr int kQuantTokensPerBlock = 256;     // one token per lane, 4 waves
+
+// Per-head structure-of-arrays cache. Every per-head array holds capP token
+// slots (capacity rounded up to a tile multiple) so tile loads never leave the
+// head's rows.
+struct CacheView {
+  uint8_t* kcode;    // [H][capP][D/4]   canonical 2-bit packing
+  uint8_t* vcode;    // [H][capP][D/4]
+  uint32_t* kparam;  // [H][capP][nG]    zp fp16 bits | step fp16 bits << 16
+  uint32_t* vparam;  // [H][capP][nG]
+  uint8_t* ids;      // [H][capP]
+  uint16_t* coef;    // [H][capP][r]     fp16 bits
+  int64_t capP;
+};
+
+// Calibration of one epoch slot.
+struct EpochView {
+  const void* C;       // [H][m][D] cache dtype
+  const float* S;      // [H][nG]
+  const float* U;      // [H][D][r]
+};
+
+// ---------------------------------------------------------------- quantize
+struct QuantArgs {
+  const void* k;           // [H][n][D]
+  const void* v;           // [H][n][D] (nullptr: assignment only, for k-means)
+  int64_t n;               // tokens per head in this call
+  const float* C32;        // [H][m][D] float copy of the current centroid table
+  const float* S;          // [H][nG]
+  const double* U64;       // [H][D][r] float64 copy of U_r (nullptr: no PSAC)
+  CacheView cache;         // destination (ignored when v == nullptr)
+  int64_t pos0;            // first destination slot
+  uint8_t* ids_out;        // assignment-only output [H][n] (k-means)
+  int H, m, r;
+};
+hipError_t launch_quantize(int D, int dtype, const QuantArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- k-means
+hipError_t launch_kmeans_seed(int D, int dtype, const void* keys, int64_t n, int H, int m,
+                              void* C, float* C32, hipStream_t s);
+hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_t* ids, int64_t n,
+                                int H, int m, void* C, float* C32, hipStream_t s);
+// Float (and float64 U) shadows of a committed epoch, used by quantize.
+hipError_t launch_shadow(int D, int dtype, const void* C, const float* U, int H, int m, int r,
+                         float* C32, double* U64, hipStream_t s);
+
+// ---------------------------------------------------------------- calibration
+hipError_t launch_gram(int D, int dtype, const void* q, int64_t n, int H, double* gram, hipStream_t s);
+// Jacobi eigensolve of each head's Gram -> U_r [H][D][r]; also S_G [H][D/32].
+hipError_t launch_eigen(int D, const double* gram, int64_t n_hist, int H, int r, float* U, float* S,
+                        hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnPlan {
+  int n_seg;
+  int32_t seg_start[kMaxSegments];   // first token of the segment (self: index into self K/V)
+  int32_t seg_len[kMaxSegments];
+  int32_t seg_epoch[kMaxSegments];   // epoch slot, or -1 for the self segment
+  int32_t tile_prefix[kMaxSegments + 1];
+};
+
+struct AttnArgs {
+  const void* q;          // [H][nq][D]
+  const float* qU;        // [H][E][nq][16] float (q . U_r per epoch slot, zero padded)
+  const void* kself;      // [H][nself][D]
+  const void* vself;
+  int64_t nq, nself;
+  int causal_self;
+  float scale_log2;       // softmax_scale * log2(e)
+  float scale;            // softmax_scale
+  CacheView cache;
+  const void* Cbase;      // epoch slot 0 centroid table; slot e at + e * epoch_C_stride bytes
+  int64_t epoch_C_stride; // bytes
+  int n_epoch_slots;      // E of qU
+  int H, m, r;
+  int splits;
+  float* out;             // [H][nq][D] (splits == 1)
+  float* part_o;          // [splits][H][nq][D]
+  float* part_ml;         // [splits][H][nq][2]
+  float* logits;          // logits mode: [nq][len] of head `logit_head`
+  int logit_head;
+  int64_t logit_len;
+};
+hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, const float* Ubase,
+                     int64_t epoch_U_stride_floats, int E, float* qU, hipStream_t s);
+hipError_t launch_attend(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+hipError_t launch_attend_logits(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+hipError_t launch_merge(int D, const AttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- export
+struct ExportArgs {
+  CacheView cache;
+  int64_t t0, n;
+  const int32_t* epoch_of_token;  // not used; epochs passed as ranges below
+  int n_epochs;
+  int32_t epoch_start[kMaxEpochs + 1];
+  int H, D, nG, r;
+  uint8_t* out;
+};
+hipError_t launch_export(const ExportArgs& a, hipStream_t s);
+
+}  // namespace qwm
