@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Throughput of the QuantWM 2-bit KV-cache hot path on one MI355X.
+
+One step is one pass of the whole path over one chunk of synthetic input:
+  1. build_subspace   -- Gram of the historical Queries, Jacobi eigensolve
+                         (PSAC basis U_r) and QSAC sensitivity S_G;
+  2. build_centroids  -- QSAC k-means (seeding + 10 Lloyd iterations);
+  3. quantize_append  -- QSAC assignment, INT2 residual, PSAC coefficients
+                         and INT2 Values for every cached token;
+  4. attend           -- the Query chunk attends to the 2-bit cache (with
+                         the PSAC logit term) plus its own bf16 K/V.
+The default workload is the "small video chunk": 12 heads, head_dim 128,
+8 frames x 880 tokens cached, 64 centroids, rank 8, one 880-Query frame.
+
+Prints ONE JSON line. `value` = cache token-heads attended per second of
+whole-step time (H * N_kv / t_step). Per-kernel times come from HIP events
+the library records around each launch on its stream during the timed
+steps; `roofline` reports the kernel that takes the most time against the
+MI355X peak of the unit that bounds it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "KV tokens attended/s over 2-bit cache + quantize GB/s; % of HBM roofline"
+HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+# VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 T lane-instructions/s.
+# The QSAC cost loop retires 3 elementary ops (sub, max, min) per channel in
+# 2 lane-instructions (v_sub + half a v_max3 + half a v_min3), so its
+# arithmetic peak is 1.5 x 39.32 = 58.98 T ops/s.
+VALU_LANE_INSTR_PER_S = 256 * 4 * 16 * 2.4e9
+QSAC_OPS_PEAK = 1.5 * VALU_LANE_INSTR_PER_S
+
+KERNELS = ["quantize", "attend", "merge", "qu", "gram", "eigen", "assign", "update", "other"]
+KERNEL_SOURCES = {
+    "quantize": "kern_quant.hip", "assign": "kern_quant.hip", "update": "kern_quant.hip",
+    "attend": "kern_attend.hip", "merge": "kern_attend.hip", "qu": "kern_attend.hip",
+    "gram": "kern_calib.hip", "eigen": "kern_calib.hip", "other": "kern_quant.hip",
+}
+
+
+def source_hash(kernel: str) -> str:
+    p = os.path.join(ROOT, "video_world_model_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def bytes_per_token_head(d, g, r):
+    return 2 * (d // 4) + 2 * (d // g) * 4 + 1 + 2 * r
+
+
+def models(w: W.Workload):
+    """Algorithmic work per launch of each kernel class."""
+    H, d, g, m, r = w.heads, w.head_dim, w.group, w.n_centroids, w.rank
+    N, Nq, Ns, M = w.n_kv, w.n_q, w.n_self, w.n_hist
+    esz = 2 if w.dtype == "bf16" else 4
+    B = bytes_per_token_head(d, g, r)
+    return {
+        "quantize": dict(ops=H * N * 3 * m * d, bytes=H * N * (2 * d * esz + B)),
+        "assign": dict(ops=H * N * 3 * m * d, bytes=H * N * (d * esz + 1)),
+        "attend": dict(flops=H * Nq * (N * (4 * d + 2 * r) + Ns * 4 * d),
+                       bytes=H * (N * B + Nq * d * esz + Nq * d * 4 + Ns * 2 * d * esz)),
+        "gram": dict(flops=2 * H * M * d * d, bytes=H * M * d * esz),
+    }
+
+
+# ----------------------------------------------------------------- CPU oracle
+
+def _oracle_head(args):
+    name, head = args
+    from threadpoolctl import threadpool_limits
+
+    import oracle.qwm_oracle as O
+    w = W.workload(name)
+    hg = W.HeadGen(w, head)
+    keys, vals = hg.cache_keys(), hg.cache_values()
+    qh, q = hg.hist_queries(), hg.current_queries()
+    ks = vs = None
+    if w.n_self:
+        ks, vs = hg.self_keys(), hg.self_values()
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        S = O.sensitivity(qh, w.group)
+        U = O.subspace(qh, w.rank)
+        C = O.build_centroids(keys, S, w.n_centroids, w.group, w.kmeans_iters, w.dtype)
+        hc = O.HeadCache(w.group, w.dtype)
+        hc.add_epoch(C, S, U)
+        hc.append(keys, vals)
+        O.attend(q, hc, ks, vs, mask=w.self_mask)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w: W.Workload, n_heads: int):
+    """The oracle's full step on `n_heads` heads, one forked worker per head
+    (run before the GPU is initialized), scaled to cache tokens/s."""
+    import multiprocessing as mp
+    n_heads = min(n_heads, w.heads)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(n_heads) as pool:
+        times = pool.map(_oracle_head, [(w.name, h) for h in range(n_heads)])
+    wall = time.perf_counter() - t0
+    busy = max(times)
+    return {
+        "value": n_heads * w.n_kv / busy,
+        "unit": "KV tokens/s",
+        "cores": n_heads,
+        "kind": "oracle",
+        "sample": (f"one full {w.name} step (subspace, {w.kmeans_iters}-iteration centroid build, quantize of "
+                   f"{w.n_kv} tokens, attention of {w.n_q} Queries) on {n_heads} of {w.heads} heads, one forked "
+                   f"process per head, BLAS 1 thread; slowest head {busy:.2f} s, pool wall {wall:.2f} s"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "numpy": np.__version__,
+    }
+
+
+# ----------------------------------------------------------------- GPU
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video_chunk", choices=["tiny", "video_chunk", "wm_layer"])
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's timed sample (0: skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain elementwise copy (torch.neg) over this many MiB first, as a known-size "
+                         "reference for HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this path uses no cross-GPU work); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    w = W.workload(args.workload)
+    cpu = cpu_baseline(w, args.cpu_heads) if args.cpu_heads > 0 else None
+
+    import torch
+    from video_world_model_amd import Cache
+
+    torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib * (1 << 18), dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    gens = [W.HeadGen(w, h) for h in range(w.heads)]
+
+    def dev(arrs):
+        x = np.ascontiguousarray(np.stack(arrs))
+        if w.dtype == "bf16":
+            return torch.from_numpy(W.bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(x).cuda()
+
+    keys = dev([g.cache_keys() for g in gens])
+    vals = dev([g.cache_values() for g in gens])
+    qh = dev([g.hist_queries() for g in gens])
+    q = dev([g.current_queries() for g in gens])
+    ks = vs = None
+    if w.n_self:
+        ks = dev([g.self_keys() for g in gens])
+        vs = dev([g.self_values() for g in gens])
+    cache = Cache(w.heads, w.head_dim, w.n_centroids, w.rank, w.n_kv,
+                  dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                  max_query_tokens=w.n_q, max_build_tokens=w.n_kv)
+    out = torch.empty((w.heads, w.n_q, w.head_dim), dtype=torch.float32, device="cuda")
+
+    def step():
+        cache.truncate(0)
+        cache.build_subspace(qh)
+        cache.build_centroids(keys, w.kmeans_iters)
+        cache.quantize_append(keys, vals)
+        cache.attend(q, ks, vs, mask=w.self_mask, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cache.profile_enable(True)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    kern = {}
+    for k in KERNELS:
+        ms, n = cache.profile_read(k)
+        if n:
+            kern[k] = dict(ms_per_step=ms / args.steps, launches_per_step=n / args.steps, avg_launch_ms=ms / n)
+    cache.profile_enable(False)
+
+    mdl = models(w)
+    dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
+    avg_s = kern[dom]["avg_launch_ms"] * 1e-3
+    if dom in ("quantize", "assign"):
+        achieved = mdl[dom]["ops"] / avg_s / 1e12
+        roof = dict(bound="alu", achieved=achieved, peak=QSAC_OPS_PEAK / 1e12, unit="Top/s",
+                    frac=achieved * 1e12 / QSAC_OPS_PEAK)
+    elif dom == "attend":
+        achieved = mdl[dom]["flops"] / avg_s / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / MFMA_F16_PEAK_TFLOPS)
+    else:
+        roof = dict(bound="alu", achieved=None, peak=None, unit=None, frac=None)
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    pmc_path = os.path.join(ROOT, "profiles", f"{dom}_{w.name}_pmc.json")
+    if os.path.exists(pmc_path):
+        with open(pmc_path) as f:
+            pmc = json.load(f)
+        if pmc.get("source_sha256_16") == source_hash(dom):
+            roof["traffic"] = pmc.get("hbm_bytes_per_launch")
+
+    extras = {}
+    if "quantize" in kern:
+        t = kern["quantize"]["avg_launch_ms"] * 1e-3
+        gbps = mdl["quantize"]["bytes"] / t / 1e9
+        extras["quantize"] = dict(GBps=gbps, hbm_frac=gbps / HBM_PEAK_GBPS,
+                                  alu_frac=mdl["quantize"]["ops"] / t / QSAC_OPS_PEAK, ms=t * 1e3)
+    if "attend" in kern:
+        t = sum(kern[k]["ms_per_step"] for k in ("qu", "attend", "merge") if k in kern) * 1e-3
+        ta = kern["attend"]["avg_launch_ms"] * 1e-3
+        extras["attend"] = dict(kv_tokens_per_s=w.heads * w.n_kv / t, ms=t * 1e3,
+                                pair_per_s=w.heads * w.n_q * (w.n_kv + w.n_self) / t,
+                                mfma_frac=mdl["attend"]["flops"] / ta / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                                hbm_frac=mdl["attend"]["bytes"] / ta / 1e9 / HBM_PEAK_GBPS)
+    extras["calibration_ms"] = sum(kern[k]["ms_per_step"] for k in ("gram", "eigen", "assign", "update", "other")
+                                   if k in kern)
+
+    rec = {
+        "metric": METRIC,
+        "value": w.heads * w.n_kv / (ms_step * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32-valu+f16-mfma",
+        "data": "synthetic",
+        "config": {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim, "group": w.group,
+                   "n_centroids": w.n_centroids, "rank": w.rank, "n_kv": w.n_kv, "n_q": w.n_q,
+                   "n_self": w.n_self, "n_hist": w.n_hist, "kmeans_iters": w.kmeans_iters,
+                   "input_dtype": w.dtype, "query_alpha": W.QUERY_ALPHA},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kern,
+        "phases": extras,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
