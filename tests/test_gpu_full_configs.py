@@ -1,0 +1,143 @@
+"""Parity at the full sizes of the three large workloads, in the launch
+configuration the bench uses, on outputs the oracle can recompute one by one:
+
+* wm_layer: 40 heads x 32,760 tokens, 256 centroids, rank 16; records of
+  sampled tokens of 4 heads bit-exact; attention and logits of 64 sampled
+  Queries of one head (the oracle quantizes that head's whole cache).
+* streaming: a 100,000-token cache built in 12,480-token epochs (9 epochs),
+  then one 1,560-token frame appended; the frame's records bit-exact on 8
+  heads; 32 sampled Queries of one head attend over all 101,560 tokens.
+* long_horizon: 131,072 tokens with per-frame mean drift, 11 epochs; 32
+  sampled Queries of a 390-Query chunk on one head.
+
+Calibration is imported (oracle-made: sensitivity and subspace from the
+epoch's historical Queries, centroids seeded from the epoch's first frame)
+so that records can be compared bit for bit."""
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle.qwm_oracle as O
+import workloads as W
+from tests.gpu_helpers import ROW_TOL, compare_records, import_calibration, log, row_rel_err, to_dev, torch_dtype
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _calibration(w, hg, e):
+    """Oracle calibration of epoch e: S_G and U_r from the epoch's historical
+    Queries, centroids = seeds from the epoch's first frame."""
+    qh = hg.hist_queries(e)
+    a, b = w.centroid_keys_range(e)
+    keys = hg.keys(a, b)
+    return O.init_centroids(keys, w.n_centroids), O.sensitivity(qh, w.group), O.subspace(qh, w.rank)
+
+
+def _build_cache(w, n_tokens, gens):
+    """GPU cache of the first n_tokens stream tokens, epoch by epoch."""
+    from video_world_model_amd import Cache
+    cache = Cache(w.heads, w.head_dim, w.n_centroids, w.rank, w.n_kv, dtype=torch_dtype(w.dtype),
+                  max_epochs=max(1, w.n_epochs), max_query_tokens=w.n_q, max_build_tokens=w.frame_tokens)
+    cals_all = []
+    with ThreadPoolExecutor(8) as ex:
+        for e in range(w.n_epochs):
+            s, t = w.epoch_start(e), min(w.epoch_end(e), n_tokens)
+            if t <= s:
+                break
+            cals = list(ex.map(lambda g: _calibration(w, g, e), gens))
+            cals_all.append(cals)
+            import_calibration(cache, cals, w.dtype)
+            keys = list(ex.map(lambda g: g.keys(s, t), gens))
+            vals = list(ex.map(lambda g: g.values(s, t), gens))
+            cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+            del keys, vals
+    assert cache.length() == n_tokens
+    return cache, cals_all
+
+
+def _oracle_head(w, hg, cals_all, n_tokens):
+    hc = O.HeadCache(w.group, w.dtype)
+    for e, cals in enumerate(cals_all):
+        s, t = w.epoch_start(e), min(w.epoch_end(e), n_tokens)
+        hc.add_epoch(*cals[hg.head])
+        hc.append(hg.keys(s, t), hg.values(s, t))
+    return hc
+
+
+def _check_attention(w, cache, gens, cals_all, head, q_idx, n_tokens):
+    q_all = [g.current_queries() for g in gens]
+    out = cache.attend(to_dev(q_all, w.dtype)).cpu().numpy()
+    logits = cache.attend_logits(to_dev(q_all, w.dtype), head).cpu().numpy()
+    hc = _oracle_head(w, gens[head], cals_all, n_tokens)
+    q = q_all[head][q_idx]
+    ref = O.attend(q, hc)
+    e = row_rel_err(out[head][q_idx], ref)
+    log(f"  head {head}: worst output row error {e.max():.3e} over {len(q_idx)} Queries")
+    assert e.max() <= ROW_TOL
+    refl = O.cache_logits(q, hc, 1.0 / np.sqrt(w.head_dim))
+    el = row_rel_err(logits[q_idx], refl)
+    log(f"  head {head}: worst logit row error {el.max():.3e}")
+    assert el.max() <= ROW_TOL
+    assert np.isfinite(out).all()
+
+
+@pytest.mark.timeout(900)
+def test_wm_layer_full_size():
+    w = W.workload("wm_layer")
+    log(f"[full] wm_layer H={w.heads} n={w.n_kv} m={w.n_centroids} r={w.rank}")
+    gens = [W.HeadGen(w, h) for h in range(w.heads)]
+    cache, cals_all = _build_cache(w, w.n_kv, gens)
+    dec = cache.decode_export(cache.export().cpu().numpy(), w.n_kv)
+    rng = np.random.default_rng(0)
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(w.n_kv - 64, w.n_kv), rng.integers(0, w.n_kv, 1920)]))
+    sub = {k: v[:, idx] for k, v in dec.items()}
+    for h in (0, 13, 27, 39):
+        k = gens[h].keys(0, w.n_kv)[idx]
+        v = gens[h].values(0, w.n_kv)[idx]
+        compare_records(sub, h, O.quantize_tokens(k, v, *cals_all[0][h], w.group))
+    log(f"  records of {len(idx)} sampled tokens x 4 heads bit-exact")
+    q_idx = np.unique(np.concatenate([[0, w.n_q - 1], rng.integers(0, w.n_q, 62)]))
+    _check_attention(w, cache, gens, cals_all, 7, q_idx, w.n_kv)
+
+
+@pytest.mark.timeout(900)
+def test_streaming_step_full_size():
+    w = W.workload("streaming")
+    base = w.n_kv - w.n_append
+    log(f"[full] streaming H={w.heads} base={base} +{w.n_append} epochs={w.n_epochs}")
+    gens = [W.HeadGen(w, h) for h in range(w.heads)]
+    cache, cals_all = _build_cache(w, base, gens)
+    # the streaming step: one new frame appended to the current epoch
+    keys = [g.keys(base, w.n_kv) for g in gens]
+    vals = [g.values(base, w.n_kv) for g in gens]
+    cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+    assert cache.length() == w.n_kv and cache.epochs() == w.n_epochs
+    dec = cache.decode_export(cache.export(base, w.n_kv).cpu().numpy(), w.n_append)
+    for h in range(0, w.heads, 5):
+        compare_records(dec, h, O.quantize_tokens(keys[h], vals[h], *cals_all[-1][h], w.group))
+        assert np.all(dec["epoch"][h] == w.n_epochs - 1)
+    log("  appended frame bit-exact on 8 heads")
+    rng = np.random.default_rng(1)
+    q_idx = np.unique(np.concatenate([[0, w.n_q - 1], rng.integers(0, w.n_q, 30)]))
+    _check_attention(w, cache, gens, cals_all, 21, q_idx, w.n_kv)
+
+
+@pytest.mark.timeout(900)
+def test_long_horizon_full_size():
+    w = W.workload("long_horizon")
+    log(f"[full] long_horizon H={w.heads} n={w.n_kv} epochs={w.n_epochs}")
+    gens = [W.HeadGen(w, h) for h in range(w.heads)]
+    cache, cals_all = _build_cache(w, w.n_kv, gens)
+    assert cache.epochs() == w.n_epochs
+    rng = np.random.default_rng(2)
+    t0 = w.n_kv - 2000  # last epoch's tail, where the drift is largest
+    dec = cache.decode_export(cache.export(t0, w.n_kv).cpu().numpy(), 2000)
+    for h in (3, 30):
+        k, v = gens[h].keys(t0, w.n_kv), gens[h].values(t0, w.n_kv)
+        compare_records(dec, h, O.quantize_tokens(k, v, *cals_all[-1][h], w.group))
+    log("  last 2,000 tokens bit-exact on 2 heads")
+    q_idx = np.unique(np.concatenate([[0, w.n_q - 1], rng.integers(0, w.n_q, 30)]))
+    _check_attention(w, cache, gens, cals_all, 11, q_idx, w.n_kv)

@@ -9,11 +9,11 @@
 // over all visible tokens and o_i = sum_j p_ij vhat_j.
 //
 // Mapping to CDNA4:
-//  * one workgroup = 4 waves = 128 Queries of one head, one split of the KV
+//  * one workgroup = 8 waves = 256 Queries of one head, one split of the KV
 //    sequence; the KV sequence is walked in 64-token tiles that never cross an
 //    epoch boundary or the cache/self boundary;
-//  * each tile is dequantized ONCE per workgroup into LDS (shared by the 4
-//    waves): khat as float16 hi + lo pairs (hi = fp16(x), lo = fp16(x - hi),
+//  * each tile is dequantized ONCE per workgroup into LDS (shared by the 8
+//    waves; waves 0-3 build khat, waves 4-7 build vhat^T): khat as float16 hi + lo pairs (hi = fp16(x), lo = fp16(x - hi),
 //    22 significant bits), the r PSAC coefficients next to them, and vhat^T
 //    as hi + lo;
 //  * logits come from v_mfma_f32_16x16x32_f16 with the contraction dimension
@@ -76,20 +76,26 @@ __device__ __forceinline__ void split_hilo(float x, _Float16& hi, _Float16& lo) 
 }
 
 template <int D, int DT, bool LOGITS>
-__global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const AttnPlan p) {
+__global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, const AttnPlan p) {
   using Sh = AttnShape<D>;
   constexpr int KS = Sh::KS, KROW = Sh::KROW, VROW = Sh::VROW, NG = Sh::NG;
   constexpr bool QLO = (DT == 1);  // float32 Queries also carry a lo part
   constexpr int VSZ = LOGITS ? 8 : D * VROW;
+  constexpr int KITEMS = kTileKV * NG;               // (token, group) items of the khat tile
+  constexpr int VITEMS = (kTileKV / 4) * (D / 8);    // (4-token quad, 8-channel octet) items
+  constexpr int VBASE = kAttnThreads / 2;            // threads [VBASE, VBASE + VITEMS) dequantize V
+  static_assert(KITEMS <= VBASE && VITEMS <= kAttnThreads - VBASE, "dequant items must fit one pass");
   __shared__ __attribute__((aligned(16))) _Float16 Ks[kTileKV * KROW];
   __shared__ __attribute__((aligned(16))) _Float16 Vh[VSZ];
   __shared__ __attribute__((aligned(16))) _Float16 Vl[VSZ];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int h = LOGITS ? a.logit_head : (int)blockIdx.z;
   const int split = blockIdx.y;
   const int64_t qw0 = (int64_t)blockIdx.x * kTileQ + wave * 32;
+  const bool wave_live = qw0 < a.nq;  // waves whose 32 Queries are all padding skip the math
 
   const int T = p.tile_prefix[p.n_seg];
   const int tlo = (int)(((int64_t)T * split) / a.splits);
@@ -141,9 +147,11 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const Att
     const int tcount = (tend - tstart) < kTileKV ? (tend - tstart) : kTileKV;
 
     __syncthreads();  // previous tile's LDS reads are complete
-    // ---- khat rows: item = (token, 32-channel group)
-    for (int it = tid; it < kTileKV * NG; it += 256) {
-      const int t = it / NG, G = it % NG;
+    if (tid < KITEMS) {
+      // ---- khat row segment: item = (token t = it % 64, group G = it / 64); a wave
+      // writes 64 consecutive rows of one group (row pitch 140 dwords spreads
+      // 16 rows over all 64 banks).
+      const int t = tid % kTileKV, G = tid / kTileKV;
       _Float16* row = Ks + t * KROW;
       half8 hv[4], lv[4];
       if (t < tcount) {
@@ -159,9 +167,8 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const Att
 #pragma unroll
           for (int j = 0; j < 32; ++j) {
             const uint32_t w = j < 16 ? cw.x : cw.y;
-            const uint32_t code = (w >> (2 * (j & 15))) & 3u;
-            const float rh = zpf + (float)code * scf;
-            x[j] = x[j] + rh;
+            const float code = (float)((w >> (2 * (j & 15))) & 3u);
+            x[j] = x[j] + __builtin_fmaf(code, scf, zpf);  // zp + code*step: the product is exact
           }
         } else {
           load_span<DT, 32>(a.kself, ((int64_t)h * a.nself + tstart + t) * D + 32 * G, x);
@@ -207,10 +214,12 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const Att
         *reinterpret_cast<half8*>(row + 2 * D + 8) = c1;
       }
     }
-    // ---- vhat^T: item = (4-token quad, 8-channel octet)
     if constexpr (!LOGITS) {
-      for (int it = tid; it < (kTileKV / 4) * (D / 8); it += 256) {
-        const int tq = it / (D / 8), co = it % (D / 8);
+      if (tid >= VBASE && tid < VBASE + VITEMS) {
+        // ---- vhat^T: item = (quad tq = it % 16, octet co = it / 16); the 16 quads
+        // of a wave land on 16 different bank pairs of each row.
+        const int it = tid - VBASE;
+        const int tq = it % (kTileKV / 4), co = it / (kTileKV / 4);
         half4 vh4[8], vl4[8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const Att
               const uint32_t pr = a.cache.vparam[slot * NG + (co >> 2)];
               const float zpf = half_bits_to_float(pr & 0xFFFFu), scf = half_bits_to_float(pr >> 16);
 #pragma unroll
-              for (int s = 0; s < 8; ++s) x[s] = zpf + (float)((cw >> (2 * s)) & 3u) * scf;
+              for (int s = 0; s < 8; ++s) x[s] = __builtin_fmaf((float)((cw >> (2 * s)) & 3u), scf, zpf);
             } else {
               load_span<DT, 8>(a.vself, ((int64_t)h * a.nself + tstart + t) * D + 8 * co, x);
             }
@@ -247,6 +256,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const Att
       }
     }
     __syncthreads();
+    if (!wave_live) continue;
 
     // ---- per-epoch PSAC Query fragment: lanes g<2 hold qU_hi, g>=2 qU_lo
     if (ep != cur_epoch) {
@@ -311,7 +321,10 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const Att
       }
       continue;
     } else {
-      // ---- online softmax (log2 domain)
+      // ---- online softmax (log2 domain). The running max is only raised when
+      // a row's new max exceeds it by more than 8 (p <= 2^8 stays exact
+      // enough in fp16 and float32), so the output rescale is rare.
+      const bool full = (tcount == kTileKV) && !(ep < 0 && a.causal_self);
       half8 pf[2][2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -322,31 +335,39 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const Att
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int j = 16 * tb + 4 * g + v;
-            bool ok = j < tcount;
-            if (ep < 0 && a.causal_self) ok = ok && ((int64_t)(tstart + j) <= qi);
-            const float x = ok ? S[qb][tb][v] * a.scale_log2 : -__builtin_inff();
+            float x = S[qb][tb][v] * a.scale_log2;
+            if (!full) {
+              const int j = 16 * tb + 4 * g + v;
+              bool ok = j < tcount;
+              if (ep < 0 && a.causal_self) ok = ok && ((int64_t)(tstart + j) <= qi);
+              x = ok ? x : -__builtin_inff();
+            }
             sv[tb][v] = x;
             mx = fmaxf(mx, x);
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrow[qb], mx);
-        const bool none = (mnew == -__builtin_inff());
-        const float alpha = none ? 1.0f : exp2f(mrow[qb] - mnew);
+        const bool raise = mx > mrow[qb] + 8.0f;
+        if (__ballot(raise)) {  // wave-uniform: rescale every lane (alpha = 1 where unchanged)
+          const float mnew = raise ? mx : mrow[qb];
+          const float alpha = (mrow[qb] == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(mrow[qb] - mnew);
+          mrow[qb] = mnew;
+          lrow[qb] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < D / 16; ++cb) O[qb][cb] *= alpha;
+        }
+        const float mcur = mrow[qb];
+        const bool none = (mcur == -__builtin_inff());
         float ps = 0.0f;
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float pv = none ? 0.0f : exp2f(sv[tb][v] - mnew);
+            const float pv = none ? 0.0f : __builtin_amdgcn_exp2f(sv[tb][v] - mcur);
             sv[tb][v] = pv;
             ps += pv;
           }
-        lrow[qb] = lrow[qb] * alpha + ps;
-        mrow[qb] = mnew;
-#pragma unroll
-        for (int cb = 0; cb < D / 16; ++cb) O[qb][cb] *= alpha;
+        lrow[qb] += ps;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -377,6 +398,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttnArgs a, const Att
   }
 
   if constexpr (!LOGITS) {
+    if (!wave_live) return;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float l = lrow[qb];
@@ -464,7 +486,7 @@ hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, 
 template <bool LOGITS>
 static hipError_t launch_attend_impl(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   dim3 grid((unsigned)((a.nq + kTileQ - 1) / kTileQ), (unsigned)a.splits, LOGITS ? 1u : (unsigned)a.H);
-  dim3 block(256);
+  dim3 block(kAttnThreads);
   if (D == 128 && dtype == 0)
     hipLaunchKernelGGL((attend_kernel<128, 0, LOGITS>), grid, block, 0, s, a, p);
   else if (D == 128)

@@ -8,13 +8,13 @@
 // remaining error is projected on the PSAC basis (r fp16 coefficients), and
 // the Value is stored as plain per-group INT2.
 //
-// Mapping to CDNA4: one lane owns one token (64 tokens per wave), so the
-// objective, the argmin and the group min/max all run lane-sequentially in
-// exactly the order of the definition, with no cross-lane reduction. The
-// centroid row being scored is the same for every lane of the wave; it is
-// loaded through the scalar path (one copy per wave in SGPRs) and consumed as
-// an SGPR operand of v_sub, so the candidate loop is pure VALU (sub, max3,
-// min3) with no LDS traffic. Builds use -ffp-contract=off so no multiply-add
+// Mapping to CDNA4: in the assignment one lane owns one token, so the
+// objective and its running argmin run lane-sequentially in exactly the order
+// of the definition. The centroid row being scored is the same for every lane
+// of a wave; it is loaded through the scalar path (one copy per wave in
+// SGPRs) and consumed as an SGPR operand of v_sub, so the candidate loop is
+// pure VALU (sub, max3, min3). The four waves of a block split the candidate
+// list of the same 64 tokens (see quantize_kernel). Builds use -ffp-contract=off so no multiply-add
 // is fused: every float32 operation rounds exactly as in the definition.
 #include "qwm_dev.h"
 #include "qwm_internal.h"
@@ -98,6 +98,34 @@ __device__ __forceinline__ void load_row(const void* base, int64_t off, float (&
   }
 }
 
+// N consecutive input elements (bf16 or float) -> float, 16-byte loads.
+template <int N, int DT>
+__device__ __forceinline__ void load_row_span(const void* base, int64_t off, float (&x)[N]) {
+  if constexpr (DT == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const uint4 w = p[i];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * i + 2 * k] = __uint_as_float(ww[k] << 16);
+        x[8 * i + 2 * k + 1] = __uint_as_float(ww[k] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const float4 w = p[i];
+      x[4 * i] = w.x;
+      x[4 * i + 1] = w.y;
+      x[4 * i + 2] = w.z;
+      x[4 * i + 3] = w.w;
+    }
+  }
+}
+
 // Plain per-group INT2 of one row x (Values): codes into words, params.
 template <int D>
 __device__ __forceinline__ void int2_row(const float (&x)[D], uint32_t (&words)[D / 16],
@@ -129,109 +157,161 @@ __device__ __forceinline__ void int2_row(const float (&x)[D], uint32_t (&words)[
   }
 }
 
+// Block = 4 waves, 64 tokens of one head.
+//  phase 1: wave w scans candidates [w*mq, (w+1)*mq) for all 64 tokens (lane =
+//           token), keeping its lexicographic (J, id) minimum;
+//  phase 2: the four quarter minima are combined in candidate order (lower
+//           quarter wins an exact tie), which equals the argmin over all
+//           candidates with ties to the smallest id;
+//  phase 3: one lane per (token, 32-channel group) quantizes the residual and
+//           the Value group and forms the group's PSAC partial sums; the group
+//           partials of a token are added in group order (lanes of a token are
+//           adjacent), and all records are written with contiguous stores.
+constexpr int kQTok = 64;
+
 template <int D, int DT, bool ASSIGN_ONLY>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   constexpr int NG = D / kGroup;
-  const int h = blockIdx.y;
-  const int64_t t = (int64_t)blockIdx.x * kQuantTokensPerBlock + threadIdx.x;
-  if (t >= a.n) return;  // the kernel has no barrier
+  __shared__ float bj[4][kQTok];
+  __shared__ int bi[4][kQTok];
+  // PSAC basis as [i][group][33]: the 4 group rows read together sit 2 banks apart
+  constexpr int UGP = kGroup + 1;
+  __shared__ double us[ASSIGN_ONLY ? 1 : kRankPad * NG * UGP];
 
-  float kf[D];
-  load_row<D, DT>(a.k, ((int64_t)h * a.n + t) * D, kf);
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: candidate rows load as scalars
+  const int64_t t0 = (int64_t)blockIdx.x * kQTok;
+  const int nt = (int)((a.n - t0) < kQTok ? (a.n - t0) : kQTok);
 
-  float SG[NG];
+  // ---- phase 1: QSAC objective over this wave's candidate quarter. It runs
+  // before any barrier so that the wave-uniform candidate rows are fetched
+  // with scalar loads (a barrier would make them possibly clobbered).
+  {
+    float kf[D];
+    load_row_span<D, DT>(a.k, ((int64_t)h * a.n + t0 + (lane < nt ? lane : 0)) * D, kf);
+    float SG[NG];
 #pragma unroll
-  for (int G = 0; G < NG; ++G) SG[G] = a.S[h * NG + G];
-
-  // QSAC assignment: ascending candidates; strict < keeps the smallest id on ties.
-  const float* __restrict__ Ch = a.C32 + (int64_t)h * a.m * D;
-  float bestJ = __builtin_inff();
-  int best = 0;
-  for (int c = 0; c < a.m; ++c) {
-    const float J = qsac_cost<D>(kf, Ch + (int64_t)c * D, SG);
-    if (J < bestJ) {
-      bestJ = J;
-      best = c;
+    for (int G = 0; G < NG; ++G) SG[G] = a.S[h * NG + G];
+    const int mq = (a.m + 3) / 4;
+    const int c0 = wave * mq, c1 = (c0 + mq) < a.m ? (c0 + mq) : a.m;
+    const float* __restrict__ Ch = a.C32 + (int64_t)h * a.m * D;
+    float bestJ = __builtin_inff();
+    int best = c0;
+    for (int c = c0; c < c1; ++c) {
+      const float J = qsac_cost<D>(kf, Ch + (int64_t)c * D, SG);
+      if (J < bestJ) {  // strict: the smallest id keeps an exact tie
+        bestJ = J;
+        best = c;
+      }
+    }
+    bj[wave][lane] = bestJ;
+    bi[wave][lane] = best;
+  }
+  if constexpr (!ASSIGN_ONLY) {
+    const double* Uh = a.U64 + (int64_t)h * D * a.r;
+    for (int i = tid; i < D * kRankPad; i += 256) {
+      const int row = i / kRankPad, col = i % kRankPad;  // row = channel
+      us[(col * NG + row / kGroup) * UGP + row % kGroup] = (col < a.r) ? Uh[row * a.r + col] : 0.0;
     }
   }
+  __syncthreads();
+
+  // ---- phase 2: combine the quarters in candidate order
+  auto combined = [&](int t) {
+    float J = bj[0][t];
+    int id = bi[0][t];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (bj[w][t] < J) {
+        J = bj[w][t];
+        id = bi[w][t];
+      }
+    return id;
+  };
   if constexpr (ASSIGN_ONLY) {
-    a.ids_out[(int64_t)h * a.n + t] = (uint8_t)best;
+    if (tid < nt) a.ids_out[(int64_t)h * a.n + t0 + tid] = (uint8_t)combined(tid);
+    return;
   } else {
-    const int64_t slot = (int64_t)h * a.cache.capP + a.pos0 + t;
-    const float* crow = Ch + (int64_t)best * D;
-    const double* __restrict__ Uh = a.U64 + (int64_t)h * D * a.r;
-    double acc[kRankPad];
+    // ---- phase 3: one lane per (token, group)
+    if (tid >= kQTok * NG) return;  // no barrier below
+    const int t = tid / NG, G = tid % NG;
+    const bool valid = t < nt;
+    const int best = combined(t);
+    const int64_t slot = (int64_t)h * a.cache.capP + a.pos0 + t0 + t;
+    const float* crow = a.C32 + ((int64_t)h * a.m + best) * D + G * kGroup;
+    float c[kGroup], k[kGroup];
 #pragma unroll
-    for (int i = 0; i < kRankPad; ++i) acc[i] = 0.0;
-
-    uint32_t kparam[NG];
-    uint32_t kwords[D / 16];  // 16 channels (2 bits each) per 32-bit word
-#pragma unroll
-    for (int G = 0; G < NG; ++G) {
-      float mx, mn;
-      {
-        const float r0 = kf[G * kGroup] - crow[G * kGroup];
-        mx = r0;
-        mn = r0;
-      }
-#pragma unroll
-      for (int j = 1; j < kGroup; ++j) {
-        const float r = kf[G * kGroup + j] - crow[G * kGroup + j];
-        mx = fmaxf(mx, r);
-        mn = fminf(mn, r);
-      }
-      uint32_t zpb, scb;
-      float zpf, scf;
-      int2_params(mn, mx, zpb, scb, zpf, scf);
-      kparam[G] = zpb | (scb << 16);
-      uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        const int ch = G * kGroup + j;
-        const float c = crow[ch];
-        const float r = kf[ch] - c;
-        const uint32_t code = int2_code(r, zpf, scf);
-        if (j < 16)
-          w0 |= code << (2 * j);
-        else
-          w1 |= code << (2 * (j - 16));
-        // PSAC error e = k - (c + rhat), rhat = zp + code*step (the product is exact).
-        const float rhat = zpf + (float)code * scf;
-        const float tsum = c + rhat;
-        const float e = kf[ch] - tsum;
-        const double ed = (double)e;
-        const double* urow = Uh + (int64_t)ch * a.r;
-#pragma unroll
-        for (int i = 0; i < kRankPad; ++i)
-          if (i < a.r) acc[i] = fma(ed, urow[i], acc[i]);
-      }
-      kwords[2 * G] = w0;
-      kwords[2 * G + 1] = w1;
+    for (int j = 0; j < kGroup; j += 4) {
+      const float4 cv = *reinterpret_cast<const float4*>(crow + j);
+      c[j] = cv.x;
+      c[j + 1] = cv.y;
+      c[j + 2] = cv.z;
+      c[j + 3] = cv.w;
     }
-    uint32_t* kc = reinterpret_cast<uint32_t*>(a.cache.kcode + slot * (D / 4));
+    load_row_span<kGroup, DT>(a.k, ((int64_t)h * a.n + t0 + (valid ? t : 0)) * D + G * kGroup, k);
+    float mx = k[0] - c[0], mn = mx;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) kc[i] = kwords[i];
-    uint32_t* kp = a.cache.kparam + slot * NG;
+    for (int j = 1; j < kGroup; ++j) {
+      const float r = k[j] - c[j];
+      mx = fmaxf(mx, r);
+      mn = fminf(mn, r);
+    }
+    uint32_t zpb, scb;
+    float zpf, scf;
+    int2_params(mn, mx, zpb, scb, zpf, scf);
+    uint32_t w0 = 0, w1 = 0;
+    float e[kGroup];
 #pragma unroll
-    for (int G = 0; G < NG; ++G) kp[G] = kparam[G];
-    a.cache.ids[slot] = (uint8_t)best;
+    for (int j = 0; j < kGroup; ++j) {
+      const float r = k[j] - c[j];
+      const uint32_t code = int2_code(r, zpf, scf);
+      if (j < 16)
+        w0 |= code << (2 * j);
+      else
+        w1 |= code << (2 * (j - 16));
+      // PSAC error e = k - (c + rhat), rhat = zp + code*step (the product is exact).
+      const float rhat = zpf + (float)code * scf;
+      const float tsum = c[j] + rhat;
+      e[j] = k[j] - tsum;
+    }
+    // coef_i = sum over the token's groups (in group order) of sum_j e_j U_ji,
+    // each group's partial formed by its own lane in float64.
     uint16_t* cf = a.cache.coef + slot * a.r;
+    for (int i = 0; i < a.r; ++i) {
+      const double* urow = &us[(i * NG + G) * UGP];
+      double part = 0.0;
 #pragma unroll
-    for (int i = 0; i < kRankPad; ++i)
-      if (i < a.r) cf[i] = (uint16_t)f64_to_f16_bits(acc[i]);
-
-    // Value: plain per-group INT2.
-    float vf[D];
-    load_row<D, DT>(a.v, ((int64_t)h * a.n + t) * D, vf);
-    uint32_t vwords[D / 16];
-    uint32_t vparam[NG];
-    int2_row<D>(vf, vwords, vparam);
-    uint32_t* vc = reinterpret_cast<uint32_t*>(a.cache.vcode + slot * (D / 4));
+      for (int j = 0; j < kGroup; ++j) part = fma((double)e[j], urow[j], part);
+      const double coef = group_ordered_sum<NG>(part);
+      if (valid && (i % NG) == G) cf[i] = (uint16_t)f64_to_f16_bits(coef);
+    }
+    // Value group
+    float v[kGroup];
+    load_row_span<kGroup, DT>(a.v, ((int64_t)h * a.n + t0 + (valid ? t : 0)) * D + G * kGroup, v);
+    float vmx = v[0], vmn = v[0];
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) vc[i] = vwords[i];
-    uint32_t* vp = a.cache.vparam + slot * NG;
+    for (int j = 1; j < kGroup; ++j) {
+      vmx = fmaxf(vmx, v[j]);
+      vmn = fminf(vmn, v[j]);
+    }
+    uint32_t vzb, vsb;
+    float vzf, vsf;
+    int2_params(vmn, vmx, vzb, vsb, vzf, vsf);
+    uint32_t u0 = 0, u1 = 0;
 #pragma unroll
-    for (int G = 0; G < NG; ++G) vp[G] = vparam[G];
+    for (int j = 0; j < kGroup; ++j) {
+      const uint32_t code = int2_code(v[j], vzf, vsf);
+      if (j < 16)
+        u0 |= code << (2 * j);
+      else
+        u1 |= code << (2 * (j - 16));
+    }
+    if (!valid) return;
+    *reinterpret_cast<uint2*>(a.cache.kcode + slot * (D / 4) + 8 * G) = make_uint2(w0, w1);
+    *reinterpret_cast<uint2*>(a.cache.vcode + slot * (D / 4) + 8 * G) = make_uint2(u0, u1);
+    a.cache.kparam[slot * NG + G] = zpb | (scb << 16);
+    a.cache.vparam[slot * NG + G] = vzb | (vsb << 16);
+    if (G == 0) a.cache.ids[slot] = (uint8_t)best;
   }
 }
 
@@ -249,43 +329,82 @@ __global__ void seed_kernel(const void* keys, int64_t n, int m, void* C, float* 
   C32[di] = load_in<DT>(keys, si);
 }
 
-// k-means update: one wave per (centroid, head). The wave walks the ids in
-// token order (ballot of 64 at a time) and adds each member Key into float64
-// lane accumulators (D / 64 channels per lane), so the sum is formed in the
-// same token order on every run. The mean is rounded once to the cache dtype;
-// a centroid without members keeps its value.
+// k-means update: one wave per (centroid, head), four centroids per block.
+// The wave reads the head's ids 1,024 at a time (16 per lane), compacts the
+// members of its centroid into an LDS list in token order (wave prefix sum of
+// the per-lane match counts), then adds the member Key rows -- fetched 8 at a
+// time, each row read by the whole wave -- into float64 lane accumulators in
+// that order. The mean is rounded once to the cache dtype; a centroid without
+// members keeps its value. The sum is formed in token order on every run, and
+// sums of bf16 Keys are exact in float64.
+constexpr int kUpdScan = 1024;
+
 template <int D, int DT>
-__global__ __launch_bounds__(64) void update_kernel(const void* keys, const uint8_t* ids, int64_t n, int m,
-                                                    void* C, float* C32) {
-  constexpr int PER = D / 64;
-  const int c = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void update_kernel(const void* keys, const uint8_t* ids, int64_t n, int m,
+                                                     void* C, float* C32) {
+  constexpr int PER = D / 64;  // channels per lane
+  __shared__ int list[4][kUpdScan];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.x * 4 + wave, h = blockIdx.y;
+  if (c >= m) return;  // the kernel has no barrier
   const uint8_t* idh = ids + (int64_t)h * n;
+  int* lst = list[wave];
   double acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0;
   int64_t count = 0;
-  for (int64_t base = 0; base < n; base += 64) {
-    const int64_t t = base + lane;
-    const bool hit = (t < n) && (idh[t] == (uint8_t)c);
-    uint64_t mask = __ballot(hit);
-    while (mask) {
-      const int b = __ffsll((unsigned long long)mask) - 1;
-      mask &= mask - 1;
-      const int64_t row = ((int64_t)h * n + base + b) * D;
+  for (int64_t base = 0; base < n; base += kUpdScan) {
+    const int64_t t0 = base + 16 * lane;
+    uint32_t match = 0;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += (double)load_in<DT>(keys, row + lane + 64 * k);
-      ++count;
+    for (int b = 0; b < 16; ++b)
+      if (t0 + b < n && idh[t0 + b] == (uint8_t)c) match |= 1u << b;
+    const int cnt = __popc(match);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
     }
+    const int total = __shfl(incl, 63);
+    int pos = incl - cnt;
+    while (match) {
+      const int b = __ffs(match) - 1;
+      match &= match - 1;
+      lst[pos++] = (int)(16 * lane + b);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int u0 = 0; u0 < total; u0 += 8) {
+      float x[8][PER];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int uu = (u0 + u < total) ? u0 + u : u0;
+        const int64_t row = ((int64_t)h * n + base + lst[uu]) * D;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) x[u][k] = load_in<DT>(keys, row + PER * lane + k);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u0 + u < total) {
+#pragma unroll
+          for (int k = 0; k < PER; ++k) acc[k] += (double)x[u][k];
+        }
+    }
+    count += total;
+    __builtin_amdgcn_wave_barrier();
   }
   if (count == 0) return;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const double mean = acc[k] / (double)count;
-    const int64_t di = ((int64_t)h * m + c) * D + lane + 64 * k;
+    const int64_t di = ((int64_t)h * m + c) * D + PER * lane + k;
     if constexpr (DT == 0) {
-      const uint32_t b = f64_to_bf16_bits(mean);
-      reinterpret_cast<uint16_t*>(C)[di] = (uint16_t)b;
-      C32[di] = bf16_bits_to_float(b);
+      const uint32_t bb = f64_to_bf16_bits(mean);
+      reinterpret_cast<uint16_t*>(C)[di] = (uint16_t)bb;
+      C32[di] = bf16_bits_to_float(bb);
     } else {
       const float f = (float)mean;  // nearest-even
       reinterpret_cast<float*>(C)[di] = f;
@@ -305,8 +424,8 @@ __global__ void shadow_kernel(const void* C, const float* U, int64_t nC, int64_t
 
 hipError_t launch_quantize(int D, int dtype, const QuantArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  dim3 grid((unsigned)((a.n + kQuantTokensPerBlock - 1) / kQuantTokensPerBlock), (unsigned)a.H);
-  dim3 block(kQuantTokensPerBlock);
+  dim3 grid((unsigned)((a.n + kQTok - 1) / kQTok), (unsigned)a.H);
+  dim3 block(256);
   const bool assign = (a.v == nullptr);
 #define QWM_QLAUNCH(DD, TT)                                                   \
   if (assign)                                                                 \
@@ -342,13 +461,15 @@ hipError_t launch_kmeans_seed(int D, int dtype, const void* keys, int64_t n, int
 
 hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_t* ids, int64_t n, int H, int m,
                                 void* C, float* C32, hipStream_t s) {
-  dim3 grid((unsigned)m, (unsigned)H), block(64);
-  if (dtype == 0)
-    hipLaunchKernelGGL((D == 128 ? update_kernel<128, 0> : update_kernel<64, 0>), grid, block, 0, s, keys, ids, n,
-                       m, C, C32);
+  dim3 grid((unsigned)((m + 3) / 4), (unsigned)H), block(256);
+  if (D == 128 && dtype == 0)
+    hipLaunchKernelGGL((update_kernel<128, 0>), grid, block, 0, s, keys, ids, n, m, C, C32);
+  else if (D == 128)
+    hipLaunchKernelGGL((update_kernel<128, 1>), grid, block, 0, s, keys, ids, n, m, C, C32);
+  else if (dtype == 0)
+    hipLaunchKernelGGL((update_kernel<64, 0>), grid, block, 0, s, keys, ids, n, m, C, C32);
   else
-    hipLaunchKernelGGL((D == 128 ? update_kernel<128, 1> : update_kernel<64, 1>), grid, block, 0, s, keys, ids, n,
-                       m, C, C32);
+    hipLaunchKernelGGL((update_kernel<64, 1>), grid, block, 0, s, keys, ids, n, m, C, C32);
   return hipGetLastError();
 }
 

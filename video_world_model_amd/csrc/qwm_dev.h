@@ -79,4 +79,70 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) { return f32_to_bf16_bits(f64_to_f32_odd(x)); }
 
+// ---- wave64 reductions with DPP (VALU lane moves; no LDS round trip) ----
+// update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl): lanes outside
+// row_mask, or whose source lane is invalid, receive `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x, double old) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(old), __double2loint(x), CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(old), __double2hiint(x), CTRL, ROW_MASK, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets it.
+__device__ __forceinline__ double group8_sum(double x) {
+  x += dpp_f64<kDppQuadSwap1, 0xF>(x, 0.0);
+  x += dpp_f64<kDppQuadSwap2, 0xF>(x, 0.0);
+  x += dpp_f64<kDppRowHalfMirror, 0xF>(x, 0.0);
+  return x;
+}
+// Sum over the 64 lanes, returned to every lane (wave-uniform).
+__device__ __forceinline__ double wave_sum(double x) {
+  x = group8_sum(x);
+  x += dpp_f64<kDppRowMirror, 0xF>(x, 0.0);
+  x += dpp_f64<kDppRowBcast15, 0xA>(x, 0.0);
+  x += dpp_f64<kDppRowBcast31, 0xC>(x, 0.0);
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), 63);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), 63);
+  return __hiloint2double(hi, lo);
+}
+// Maximum over the 64 lanes, returned to every lane.
+__device__ __forceinline__ double wave_max(double x) {
+  x = fmax(x, dpp_f64<kDppQuadSwap1, 0xF>(x, x));
+  x = fmax(x, dpp_f64<kDppQuadSwap2, 0xF>(x, x));
+  x = fmax(x, dpp_f64<kDppRowHalfMirror, 0xF>(x, x));
+  x = fmax(x, dpp_f64<kDppRowMirror, 0xF>(x, x));
+  x = fmax(x, dpp_f64<kDppRowBcast15, 0xA>(x, x));
+  x = fmax(x, dpp_f64<kDppRowBcast31, 0xC>(x, x));
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), 63);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), 63);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_min(double x) { return -wave_max(-x); }
+
+// Sum of the values of the NG (2 or 4) adjacent lanes of an aligned lane
+// group, added in lane order ((x0 + x1) + x2) + x3; every lane of the group
+// gets the same bits.
+template <int NG>
+__device__ __forceinline__ double group_ordered_sum(double x) {
+  if constexpr (NG == 4) {
+    const double x0 = dpp_f64<0x00, 0xF>(x, 0.0);  // quad_perm [0,0,0,0]
+    const double x1 = dpp_f64<0x55, 0xF>(x, 0.0);  // quad_perm [1,1,1,1]
+    const double x2 = dpp_f64<0xAA, 0xF>(x, 0.0);  // quad_perm [2,2,2,2]
+    const double x3 = dpp_f64<0xFF, 0xF>(x, 0.0);  // quad_perm [3,3,3,3]
+    return ((x0 + x1) + x2) + x3;
+  } else {
+    static_assert(NG == 2, "groups of 2 or 4 lanes");
+    const double x0 = dpp_f64<0xA0, 0xF>(x, 0.0);  // quad_perm [0,0,2,2]
+    const double x1 = dpp_f64<0xF5, 0xF>(x, 0.0);  // quad_perm [1,1,3,3]
+    return x0 + x1;
+  }
+}
+
 }  // namespace qwm

@@ -85,7 +85,7 @@ Layout make_layout(const qwm_desc* d) {
   L.C32 = take((size_t)(H * m * D * 4));
   L.kmC32 = take((size_t)(H * m * D * 4));
   L.U64 = take((size_t)(H * D * r * 8));
-  L.gram = take((size_t)(H * D * D * 8));
+  L.gram = take((size_t)(H * qwm::kGramMaxChunks * D * D * 8));
   L.build_ids = take((size_t)(H * d->max_build_tokens));
   L.qU = take((size_t)(H * E * maxq * qwm::kRankPad * 4));
   L.part_o = take((size_t)(pr * D * 4));
@@ -335,7 +335,8 @@ qwm_status qwm_build_subspace(qwm_cache* c, const void* q_hist, int64_t n_hist) 
   });
   if (e != hipSuccess) return fail_hip(e, "gram");
   e = c->run(QWM_K_EIGEN, [&] {
-    return qwm::launch_eigen(c->D, c->gram(), n_hist, c->H, c->r, c->slotU(st_slot), c->slotS(st_slot), c->stream);
+    return qwm::launch_eigen(c->D, c->gram(), qwm::gram_chunks(n_hist), n_hist, c->H, c->r, c->slotU(st_slot),
+                             c->slotS(st_slot), c->stream);
   });
   if (e != hipSuccess) return fail_hip(e, "eigen");
   c->staged_subspace = true;

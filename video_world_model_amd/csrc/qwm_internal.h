@@ -10,10 +10,11 @@ namespace qwm {
 constexpr int kGroup = 32;       // channels per INT2 group
 constexpr int kRankPad = 16;     // PSAC rank padded for the MFMA contraction
 constexpr int kTileKV = 64;      // tokens per attention tile
-constexpr int kTileQ = 128;      // Queries per attention workgroup (4 waves x 32)
+constexpr int kTileQ = 256;      // Queries per attention workgroup (8 waves x 32)
+constexpr int kAttnThreads = 512;
 constexpr int kMaxEpochs = 64;
 constexpr int kMaxSegments = kMaxEpochs + 1;  // epochs + the self segment
-constexpr int kQuantTokensPerBlock = 256;     // one token per lane, 4 waves
+constexpr int kGramMaxChunks = 8;   // historical-Query chunks per head in the Gram
 
 // Per-head structure-of-arrays cache. Every per-head array holds capP token
 // slots (capacity rounded up to a tile multiple) so tile loads never leave the
@@ -60,9 +61,11 @@ hipError_t launch_shadow(int D, int dtype, const void* C, const float* U, int H,
                          float* C32, double* U64, hipStream_t s);
 
 // ---------------------------------------------------------------- calibration
+// Partial Grams [H][chunks][D][D] (chunks = gram_chunks(n) <= kGramMaxChunks).
+int gram_chunks(int64_t n);
 hipError_t launch_gram(int D, int dtype, const void* q, int64_t n, int H, double* gram, hipStream_t s);
-// Jacobi eigensolve of each head's Gram -> U_r [H][D][r]; also S_G [H][D/32].
-hipError_t launch_eigen(int D, const double* gram, int64_t n_hist, int H, int r, float* U, float* S,
+// Eigensolve of each head's Gram (sum of the chunk partials) -> U_r [H][D][r]; also S_G [H][D/32].
+hipError_t launch_eigen(int D, const double* gram, int nchunk, int64_t n_hist, int H, int r, float* U, float* S,
                         hipStream_t s);
 
 // ---------------------------------------------------------------- attention
