@@ -329,53 +329,63 @@ __global__ void seed_kernel(const void* keys, int64_t n, int m, void* C, float* 
   C32[di] = load_in<DT>(keys, si);
 }
 
-// k-means update: one wave per (centroid, head), four centroids per block.
-// The wave reads the head's ids 1,024 at a time (16 per lane), compacts the
-// members of its centroid into an LDS list in token order (wave prefix sum of
-// the per-lane match counts), then adds the member Key rows -- fetched 8 at a
-// time, each row read by the whole wave -- into float64 lane accumulators in
-// that order. The mean is rounded once to the cache dtype; a centroid without
-// members keeps its value. The sum is formed in token order on every run, and
-// sums of bf16 Keys are exact in float64.
-constexpr int kUpdScan = 1024;
+// k-means update: one block of 16 waves per (centroid, head). Wave w owns the
+// contiguous token range [w*span, (w+1)*span) (span = n/16 rounded up to a
+// multiple of 64); each lane reads a contiguous run of at most 16 ids per
+// round, so a wave prefix sum over the per-lane match counts lists the
+// centroid's members in token order in LDS. Member Key rows are fetched 8 at a
+// time (each row by the whole wave) and added into float64 lane accumulators;
+// the 16 wave sums are then added in wave order. The mean is rounded once to
+// the cache dtype; a centroid without members keeps its value. The order of
+// every addition is fixed, so repeated runs give the same bits.
+constexpr int kUpdWaves = 16;
+constexpr int kUpdLane = 16;  // ids per lane per round
 
 template <int D, int DT>
-__global__ __launch_bounds__(256) void update_kernel(const void* keys, const uint8_t* ids, int64_t n, int m,
-                                                     void* C, float* C32) {
+__global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys, const uint8_t* ids, int64_t n,
+                                                                int m, void* C, float* C32) {
   constexpr int PER = D / 64;  // channels per lane
-  __shared__ int list[4][kUpdScan];
+  __shared__ uint16_t list[kUpdWaves][64 * kUpdLane];
+  __shared__ double red[kUpdWaves][D];
+  __shared__ int cnt[kUpdWaves];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = blockIdx.x * 4 + wave, h = blockIdx.y;
-  if (c >= m) return;  // the kernel has no barrier
+  const int c = blockIdx.x, h = blockIdx.y;
   const uint8_t* idh = ids + (int64_t)h * n;
-  int* lst = list[wave];
+  uint16_t* lst = list[wave];
+
+  const int64_t span = ((n + kUpdWaves - 1) / kUpdWaves + 63) / 64 * 64;
+  const int per_lane = (int)(span / 64 < kUpdLane ? span / 64 : kUpdLane);
+  const int64_t round_len = 64 * (int64_t)per_lane;
+  const int64_t w0 = (int64_t)wave * span;
+  const int64_t w1 = (w0 + span < n) ? w0 + span : n;
+
   double acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0;
-  int64_t count = 0;
-  for (int64_t base = 0; base < n; base += kUpdScan) {
-    const int64_t t0 = base + 16 * lane;
+  int count = 0;
+  for (int64_t base = w0; base < w1; base += round_len) {
+    const int64_t t0 = base + (int64_t)per_lane * lane;
     uint32_t match = 0;
 #pragma unroll
-    for (int b = 0; b < 16; ++b)
-      if (t0 + b < n && idh[t0 + b] == (uint8_t)c) match |= 1u << b;
-    const int cnt = __popc(match);
-    int incl = cnt;
+    for (int b = 0; b < kUpdLane; ++b)
+      if (b < per_lane && t0 + b < w1 && idh[t0 + b] == (uint8_t)c) match |= 1u << b;
+    const int mc = __popc(match);
+    int incl = mc;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(incl, o);
       if (lane >= o) incl += y;
     }
     const int total = __shfl(incl, 63);
-    int pos = incl - cnt;
+    int pos = incl - mc;
     while (match) {
       const int b = __ffs(match) - 1;
       match &= match - 1;
-      lst[pos++] = (int)(16 * lane + b);
+      lst[pos++] = (uint16_t)(per_lane * lane + b);
     }
-    __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int u0 = 0; u0 < total; u0 += 8) {
       float x[8][PER];
@@ -394,22 +404,35 @@ __global__ __launch_bounds__(256) void update_kernel(const void* keys, const uin
         }
     }
     count += total;
+    // the list is rewritten next round: every lane must be done reading it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  if (count == 0) return;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const double mean = acc[k] / (double)count;
-    const int64_t di = ((int64_t)h * m + c) * D + PER * lane + k;
-    if constexpr (DT == 0) {
-      const uint32_t bb = f64_to_bf16_bits(mean);
-      reinterpret_cast<uint16_t*>(C)[di] = (uint16_t)bb;
-      C32[di] = bf16_bits_to_float(bb);
-    } else {
-      const float f = (float)mean;  // nearest-even
-      reinterpret_cast<float*>(C)[di] = f;
-      C32[di] = f;
-    }
+  for (int k = 0; k < PER; ++k) red[wave][PER * lane + k] = acc[k];
+  if (lane == 0) cnt[wave] = count;
+  __syncthreads();
+  if (threadIdx.x >= D) return;
+  const int j = threadIdx.x;
+  int total = 0;
+  double sum = 0.0;
+#pragma unroll
+  for (int w = 0; w < kUpdWaves; ++w) {
+    total += cnt[w];
+    sum += red[w][j];
+  }
+  if (total == 0) return;
+  const double mean = sum / (double)total;
+  const int64_t di = ((int64_t)h * m + c) * D + j;
+  if constexpr (DT == 0) {
+    const uint32_t bb = f64_to_bf16_bits(mean);
+    reinterpret_cast<uint16_t*>(C)[di] = (uint16_t)bb;
+    C32[di] = bf16_bits_to_float(bb);
+  } else {
+    const float f = (float)mean;  // nearest-even
+    reinterpret_cast<float*>(C)[di] = f;
+    C32[di] = f;
   }
 }
 
@@ -461,7 +484,7 @@ hipError_t launch_kmeans_seed(int D, int dtype, const void* keys, int64_t n, int
 
 hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_t* ids, int64_t n, int H, int m,
                                 void* C, float* C32, hipStream_t s) {
-  dim3 grid((unsigned)((m + 3) / 4), (unsigned)H), block(256);
+  dim3 grid((unsigned)m, (unsigned)H), block(kUpdWaves * 64);
   if (D == 128 && dtype == 0)
     hipLaunchKernelGGL((update_kernel<128, 0>), grid, block, 0, s, keys, ids, n, m, C, C32);
   else if (D == 128)
