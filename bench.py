@@ -2,7 +2,7 @@
 """Throughput of the QuantWM 2-bit KV-cache hot path on one MI355X.
 
 One step is one pass of the whole path over one chunk of synthetic input:
-  1. build_subspace   -- Gram of the historical Queries, Jacobi eigensolve
+  1. build_subspace   -- Gram of the historical Queries, eigensolve
                          (PSAC basis U_r) and QSAC sensitivity S_G;
   2. build_centroids  -- QSAC k-means (seeding + 10 Lloyd iterations);
   3. quantize_append  -- QSAC assignment, INT2 residual, PSAC coefficients

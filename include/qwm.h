@@ -29,7 +29,12 @@
  *   tensor). The handle itself is a small host object.
  * - Work is enqueued on the HIP stream given at qwm_create and every call is
  *   asynchronous with respect to the host; the caller keeps input buffers
- *   alive until the stream has passed the call. No call synchronizes.
+ *   alive until the stream has passed the call. No call synchronizes. The one
+ *   exception to the single stream is the eigensolve of qwm_build_subspace,
+ *   which runs on a stream of the library's own (default priority) so that
+ *   later work overlaps it; the cache stream waits for it before the staged
+ *   calibration is committed, imported over or exported, and before the next
+ *   qwm_build_subspace.
  * - A handle is not thread-safe; calls on one handle must not overlap.
  * - Every call returns a qwm_status and never throws. Arguments are checked
  *   on the host before anything is enqueued; a call that fails a check has
@@ -99,9 +104,12 @@ qwm_status qwm_destroy(qwm_cache* cache);
  * sensitivity", "dominant Query subspace"; roboind.com "Step 2": energy of
  * historical Queries concentrates in a few principal directions).
  * S_G = sum over the group's channels of mean q_j^2 (float64, stored float32);
- * U_r = top-r eigenvectors of the uncentered Gram Q^T Q (float64 Jacobi on the
- * device), largest-magnitude entry of each column positive. The result goes
- * to a staged epoch that qwm_build_centroids commits. 1 <= n_hist. */
+ * U_r = top-r eigenvectors of the uncentered Gram Q^T Q (float64 on the
+ * device: Householder tridiagonalization, multisection, twisted
+ * factorization), largest-magnitude entry of each column positive. The
+ * result goes to a staged epoch that qwm_build_centroids commits. S_G is
+ * ready on the cache stream when the call returns; U_r is computed on the
+ * library's eigensolve stream (see above). 1 <= n_hist. */
 qwm_status qwm_build_subspace(qwm_cache* cache, const void* q_hist, int64_t n_hist);
 
 /* QSAC centroid table from n_keys Keys [heads][n_keys][head_dim]
@@ -177,7 +185,7 @@ qwm_status qwm_export(const qwm_cache* cache, int64_t t0, int64_t t1, void* dev_
 qwm_status qwm_attend_logits(qwm_cache* cache, const void* q, int64_t n_q, int32_t head,
                              float softmax_scale, float* logits);
 
-/* ---- kernel timing (HIP events around each launch, on the cache stream) ---- */
+/* ---- kernel timing (HIP events around each launch, on the stream it runs on) ---- */
 
 typedef enum {
   QWM_K_QUANTIZE = 0,   /* quantize-append */
@@ -185,7 +193,7 @@ typedef enum {
   QWM_K_MERGE = 2,      /* split-KV merge */
   QWM_K_QU = 3,         /* per-epoch q . U_r prologue */
   QWM_K_GRAM = 4,       /* Gram matrix + sensitivity */
-  QWM_K_EIGEN = 5,      /* Jacobi eigensolver */
+  QWM_K_EIGEN = 5,      /* eigensolver (on the eigensolve stream) */
   QWM_K_ASSIGN = 6,     /* k-means assignment */
   QWM_K_UPDATE = 7,     /* k-means centroid update */
   QWM_K_OTHER = 8,      /* seeding, shadows, export */

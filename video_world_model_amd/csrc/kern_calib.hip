@@ -86,6 +86,25 @@ __global__ __launch_bounds__(256) void gram_kernel(const void* q, int64_t n, int
   }
 }
 
+// Sensitivity S_G = (sum over the group's channels of Gram_jj) / M, one
+// block per head: thread j adds the chunk partials of Gram_jj in chunk order,
+// then thread G adds its group's 32 diagonal entries in channel order.
+template <int N>
+__global__ __launch_bounds__(N) void sens_kernel(const double* gram, int nchunk, int64_t n_hist, float* S) {
+  __shared__ double diag[N];
+  const int h = blockIdx.x, j = threadIdx.x;
+  const double* G = gram + (int64_t)h * nchunk * N * N + (int64_t)j * N + j;
+  double x = 0.0;
+  for (int ch = 0; ch < nchunk; ++ch) x += G[(int64_t)ch * N * N];
+  diag[j] = x;
+  __syncthreads();
+  if (j < N / kGroup) {
+    double sg = 0.0;
+    for (int t = j * kGroup; t < (j + 1) * kGroup; ++t) sg += diag[t];
+    S[h * (N / kGroup) + j] = (float)(sg / (double)n_hist);
+  }
+}
+
 // ---------------------------------------------------------------- eigensolver
 //
 // Top-r eigenpairs of one head's float64 Gram, one 1024-thread workgroup per
@@ -98,9 +117,10 @@ __global__ __launch_bounds__(256) void gram_kernel(const void* q, int64_t n, int
 //     step costs two barriers. Reflectors are kept in LDS for step 4.
 //  2. Wave w finds the w-th largest eigenvalue of T by multisection: its 64
 //     lanes evaluate Sturm counts at 64 points of the current interval.
-//  3. Wave w computes the eigenvector of T by inverse iteration with a
-//     pivoted tridiagonal LU; the serial recurrences run wave-uniformly with
-//     the length-d arrays held two elements per lane (readlane to fetch).
+//  3. Wave w computes the eigenvector of T from the twisted factorization
+//     of T - lambda I (forward and backward pivots, twist at the smallest
+//     |gamma|), one pass each way; the serial recurrences run
+//     wave-uniformly with their arrays in LDS.
 //  4. Modified Gram-Schmidt across the r vectors (descending eigenvalues),
 //     back-transformation u = H_0 ... H_{d-3} z, sign rule.
 
@@ -110,20 +130,6 @@ __device__ __forceinline__ double readlane_f64(double x, int l) {
   return __hiloint2double(hi, lo);
 }
 
-// A length-N array held by one wave, element k in lane k % 64, slot k / 64.
-struct Dist {
-  double s0 = 0.0, s1 = 0.0;
-  __device__ __forceinline__ double get(int k) const { return readlane_f64(k < 64 ? s0 : s1, k & 63); }
-  __device__ __forceinline__ void put(int k, double v, int lane) {
-    if (lane == (k & 63)) {
-      if (k < 64)
-        s0 = v;
-      else
-        s1 = v;
-    }
-  }
-};
-
 constexpr int kEigThreads = 1024;
 
 __device__ __forceinline__ double rcp_f64(double x) {
@@ -131,14 +137,27 @@ __device__ __forceinline__ double rcp_f64(double x) {
   return r * fma(-x, r, 2.0);  // one Newton step
 }
 
+// Pivot guard shared by the Sturm count and the factorizations: a pivot of
+// magnitude below pivmin is replaced by -pivmin.
+__device__ __forceinline__ double guard_pivot(double q, double pivmin) { return fabs(q) < pivmin ? -pivmin : q; }
+
+// Makes the wave's own LDS writes visible to its other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int N>
-__global__ __launch_bounds__(kEigThreads) void eigen_kernel(const double* gram, int nchunk, int64_t n_hist, int r,
-                                                            float* U, float* S) {
-  constexpr int CPT = N / 8;  // columns of A per thread
-  __shared__ double Vst[N * N];  // reflector k in row k, columns k+1..N-1
-  __shared__ double vv[2][N], pp[2][N];
+__global__ __launch_bounds__(kEigThreads) void eigen_kernel(const double* gram, int nchunk, int r, float* U) {
+  constexpr int CPT = N / 8;               // columns of A per thread
+  constexpr int NV = N * (N - 1) / 2;      // packed reflectors
+  __shared__ double Vst[NV];               // reflector k: columns k+1..N-1 at vrow(k)
+  __shared__ double xrow[2][N], erow[2][N], pp[2][N];  // rows k and k+1 of A at step k; p
   __shared__ double dg[N], ev[N], e2[N], betas[N], zbuf[N];
-  __shared__ double misc[4];  // lo, hi, tnorm, pivmin
+  __shared__ double Dp[kRankPad][N], Dm[kRankPad][N];  // twisted-factorization pivots, one row per eigenvalue
+  __shared__ double misc[4];               // lo, hi, tnorm, pivmin
+  auto vrow = [](int k) { return k * (N - 1) - k * (k - 1) / 2 - k - 1; };  // + j for column j > k
 
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,101 +177,119 @@ __global__ __launch_bounds__(kEigThreads) void eigen_kernel(const double* gram, 
 #pragma unroll
       for (int u = 0; u < CPT; ++u) a[u] += Gc[colof(u)];
     }
-#pragma unroll
-    for (int u = 0; u < CPT; ++u)
-      if (colof(u) == i) zbuf[i] = a[u];
-  }
-  __syncthreads();
-  // Sensitivity from the Gram diagonal: S_G = (sum_{j in G} Gram_jj) / M.
-  if (tid < N / kGroup) {
-    double sg = 0.0;
-    for (int j = tid * kGroup; j < (tid + 1) * kGroup; ++j) sg += zbuf[j];
-    S[h * (N / kGroup) + tid] = (float)(sg / (double)n_hist);
   }
 
-  // Reflector of step k from row k (done by the 8 lanes owning row k):
-  // x = A[k][k+1..], alpha = -sign(x0)|x|, v = x - alpha e1, beta = 2 / v.v.
-  // v is written over the full length with zeros at 0..k, so the product and
-  // the update of the step need no masks.
-  auto reflector = [&](int k, int buf) {
-    if (i == k) {
-      double sq = 0.0, x0 = 0.0;
+  // ---- 1. Householder tridiagonalization, two barriers per step.
+  // Step k: x = A[k][k+1..], alpha = -sign(x0)|x|, v = x - alpha e_{k+1},
+  // beta = 2 / v.v = -1 / (alpha v0), p = beta A v,
+  // A -= v w^T + w v^T with w = p - (beta/2)(p.v) v, i.e.
+  // A -= v p^T + (p - beta (p.v) v) v^T.
+  // At the end of step k-1 the owners of row k publish x (entries <= k set
+  // to zero) and the diagonal, and the owners of row k+1 publish that row,
+  // which by symmetry is column k+1. Every wave then forms the reflector
+  // itself, and the products use x in place of v with one correction for the
+  // v0 entry: (A v)_i = (A x)_i - alpha A[k+1][i], p.v = p.x - alpha p_{k+1}.
+  // The update with x_{k+1} in place of v0 is wrong only in column k+1, which
+  // is finished after this step except for the diagonal of row k+1; its
+  // owners add the missing w_{k+1} alpha when they publish it.
+  // Rows and columns <= k are finished after step k and never read again
+  // (x and p are zero there, so they stay as they are); a wave whose 8 rows
+  // are all finished skips the step.
+  if (row_ok && i == 0) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int j = colof(u);
+      xrow[0][j] = (j > 0) ? a[u] : 0.0;
+      if (j == 0) dg[0] = a[u];
+    }
+  }
+  if (row_ok && i == 1) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) erow[0][colof(u)] = a[u];
+  }
+  __syncthreads();
+  const int writer = N / 8 - 1;  // owns row N-1, live on every step
+  for (int k = 0; k < N - 2; ++k) {
+    const int buf = k & 1;
+    const bool live = row_ok && (8 * wave + 7 > k);  // wave-uniform
+    double xj[CPT];
+    double alpha = 0.0, beta = 0.0, xi = 0.0;
+    if (live) {
+      const double x0 = xrow[buf][k + 1];
+      const double xl0 = xrow[buf][lane], xl1 = (lane + 64 < N) ? xrow[buf][lane + 64] : 0.0;
+      const double m0 = (lane > k + 1) ? xl0 : 0.0, m1 = (lane + 64 > k + 1) ? xl1 : 0.0;
+      double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        const int j = colof(u);
-        x0 += (j == k + 1) ? a[u] : 0.0;
-        sq = fma((j > k + 1) ? a[u] : 0.0, a[u], sq);
+        xj[u] = xrow[buf][colof(u)];
+        s4[u & 3] = fma(a[u], xj[u], s4[u & 3]);
       }
-      sq = group8_sum(sq);
-      x0 = group8_sum(x0);
-      double alpha = x0, v0 = x0, beta = 0.0;
+      const double ei = erow[buf][i];
+      xi = xrow[buf][i];
+      const double sq = wave_sum(fma(m0, m0, m1 * m1));
+      alpha = x0;
+      double v0 = 0.0;
       if (sq != 0.0) {
         const double nrm = sqrt(fma(x0, x0, sq));
         alpha = x0 >= 0.0 ? -nrm : nrm;
         v0 = x0 - alpha;
-        beta = 2.0 / fma(v0, v0, sq);
+        beta = -rcp_f64(alpha * v0);
       }
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) {
-        const int j = colof(u);
-        const double v = (j > k + 1) ? a[u] : ((j == k + 1) ? v0 : 0.0);
-        vv[buf][j] = v;
-        Vst[k * N + j] = v;
-        if (j == k) dg[k] = a[u];
+      if (wave == writer) {
+        const double vl0 = (lane == k + 1) ? v0 : m0, vl1 = (lane + 64 == k + 1) ? v0 : m1;
+        if (lane > k) Vst[vrow(k) + lane] = vl0;
+        if (lane + 64 > k && lane + 64 < N) Vst[vrow(k) + lane + 64] = vl1;
+        if (lane == 0) {
+          ev[k] = alpha;
+          betas[k] = beta;
+        }
       }
-      if (c == 0) {
-        ev[k] = alpha;
-        betas[k] = beta;
-      }
+      const double acc = fma(-alpha, ei, group8_sum((s4[0] + s4[1]) + (s4[2] + s4[3])));
+      if (c == 0) pp[buf][i] = (i > k) ? beta * acc : 0.0;
+    } else if (row_ok && c == 0) {
+      pp[buf][i] = 0.0;
     }
-  };
-
-  // ---- 1. tridiagonalization, two barriers per step
-  reflector(0, 0);
-  __syncthreads();
-  for (int k = 0; k < N - 2; ++k) {
-    const int buf = k & 1;
-    const double beta = betas[k];
-    if (beta != 0.0) {
-      // p = beta * A22 v (rows <= k get p = 0)
-      double acc = 0.0;
+    __syncthreads();
+    if (live) {
+      double t4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int u = 0; u < CPT; ++u) acc = fma(a[u], vv[buf][colof(u)], acc);
-      acc = group8_sum(acc);
-      if (row_ok && c == 0) pp[buf][i] = (i > k) ? beta * acc : 0.0;
-      __syncthreads();
-      // w = p - (beta/2)(p.v) v ; A22 -= v w^T + w v^T
-      double t = 0.0;
+      for (int u = 0; u < CPT; ++u) t4[u & 3] = fma(pp[buf][colof(u)], xj[u], t4[u & 3]);
+      const double pt = group8_sum((t4[0] + t4[1]) + (t4[2] + t4[3]));
+      const double K2 = beta * fma(-alpha, pp[buf][k + 1], pt);
+      const double vi = (i == k + 1) ? xi - alpha : xi;
+      const double wi = fma(-K2, vi, pp[buf][i]);
+      // p is read again below rather than kept from the loop above: holding
+      // both copies would exceed the 128 registers a 1,024-thread block allows
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int j = lane; j < N; j += 64) t = fma(pp[buf][j], vv[buf][j], t);
-      const double K = 0.5 * beta * wave_sum(t);
-      if (row_ok) {
-        const double vi = vv[buf][i], wi = fma(-K, vi, pp[buf][i]);
+      for (int u = 0; u < CPT; ++u) a[u] = fma(-vi, pp[buf][colof(u)], fma(-wi, xj[u], a[u]));
+      // publish rows k+1 and k+2 for the next step
+      if (i == k + 1) {
 #pragma unroll
         for (int u = 0; u < CPT; ++u) {
           const int j = colof(u);
-          const double vj = vv[buf][j], wj = fma(-K, vj, pp[buf][j]);
-          a[u] = fma(-vi, wj, fma(-wi, vj, a[u]));
+          xrow[buf ^ 1][j] = (j > k + 1) ? a[u] : 0.0;
+          if (j == k + 1) dg[k + 1] = fma(wi, alpha, a[u]);
         }
       }
+      if (i == k + 2) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) erow[buf ^ 1][colof(u)] = a[u];
+      }
     }
-    // the next reflector needs only row k+1, which its owners just updated
-    if (k + 1 < N - 2) reflector(k + 1, buf ^ 1);
     __syncthreads();
   }
+  // dg[N-2] was published by step N-3
   if (row_ok && i >= N - 2) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int j = colof(u);
-      if (j == i) dg[i] = a[u];
+      if (i == N - 1 && j == N - 1) dg[N - 1] = a[u];
       if (i == N - 2 && j == N - 1) ev[N - 2] = a[u];
     }
   }
-  if (tid == 0) {
-    ev[N - 1] = 0.0;
-    betas[N - 2] = 0.0;
-    betas[N - 1] = 0.0;
-  }
+
+  if (tid == 0) ev[N - 1] = 0.0;
   __syncthreads();
   for (int ii = tid; ii < N; ii += kEigThreads) e2[ii] = ev[ii] * ev[ii];
   if (wave == 0) {
@@ -279,22 +316,21 @@ __global__ __launch_bounds__(kEigThreads) void eigen_kernel(const double* gram, 
   }
   __syncthreads();
 
-  Dist y;
+  double y0 = 0.0, y1 = 0.0;  // wave w's vector: entry l in y0 of lane l, entry 64+l in y1
   if (wave < r) {
-    // ---- 2. the wave-th largest eigenvalue by 64-way multisection
+    // ---- 2. the wave-th largest eigenvalue by 64-way multisection, to an
+    // absolute accuracy of a few ulps of |T|
     const int j = N - 1 - wave;  // ascending index
     double lo = misc[0], hi = misc[1];
     const double tn = misc[2], pivmin = misc[3];
+    const double tol = 4.0 * 2.220446049250313e-16 * tn + pivmin;
     for (int it = 0; it < 64; ++it) {
-      if (hi - lo <= 4.0 * 2.220446049250313e-16 * fmax(fabs(lo), fabs(hi)) + pivmin) break;
+      if (hi - lo <= tol) break;
       const double x = lo + (hi - lo) * (double)(lane + 1) / 65.0;
       double q = dg[0] - x;
       int cnt = q < 0.0;
-      for (int i = 1; i < N; ++i) {
-        if (fabs(q) < pivmin) q = -pivmin;
-        double rq = __builtin_amdgcn_rcp(q);
-        rq = rq * fma(-q, rq, 2.0);  // one Newton step: a count is insensitive to the last bits
-        q = (dg[i] - x) - e2[i - 1] * rq;
+      for (int ii = 1; ii < N; ++ii) {
+        q = (dg[ii] - x) - e2[ii - 1] * rcp_f64(guard_pivot(q, pivmin));  // a count is insensitive to the last bits
         cnt += q < 0.0;
       }
       const uint64_t mask = __ballot(cnt > j);
@@ -306,105 +342,82 @@ __global__ __launch_bounds__(kEigThreads) void eigen_kernel(const double* gram, 
     }
     const double lam = 0.5 * (lo + hi);
 
-    // ---- 3. inverse iteration: pivoted LU of T - lam I (pivot reciprocals
-    // kept), then solves until the growth shows convergence (at most 3).
-    const double tol = 2.220446049250313e-16 * tn;
-    Dist Ai, Bb, Cc, Dd;  // Ai holds 1 / pivot
-    uint64_t piv0 = 0, piv1 = 0;
-    double a_cur = dg[0] - lam, b_cur = ev[0];
-    for (int k = 0; k < N - 1; ++k) {
-      const double ck = ev[k];
-      const double a_next = dg[k + 1] - lam;
-      const double b_next = (k + 1 < N - 1) ? ev[k + 1] : 0.0;
-      double sai, sb, sc, sd;
-      if (fabs(a_cur) >= fabs(ck)) {
-        if (a_cur == 0.0) a_cur = tol;
-        sai = rcp_f64(a_cur);
-        const double mult = ck * sai;
-        sb = b_cur;
-        sc = mult;
-        sd = 0.0;
-        a_cur = a_next - mult * b_cur;
-        b_cur = b_next;
-      } else {
-        sai = rcp_f64(ck);
-        const double mult = a_cur * sai;
-        sb = a_next;
-        sc = mult;
-        sd = b_next;
-        if (k < 64)
-          piv0 |= 1ull << k;
-        else
-          piv1 |= 1ull << (k - 64);
-        a_cur = b_cur - mult * a_next;
-        b_cur = -mult * b_next;
-      }
-      Ai.put(k, sai, lane);
-      Bb.put(k, sb, lane);
-      Cc.put(k, sc, lane);
-      Dd.put(k, sd, lane);
+    // ---- 3. eigenvector of T by the twisted factorization of T - lam I:
+    // forward pivots D+ (top down) and backward pivots D- (bottom up), twist
+    // index t = argmin |D+_t + D-_t - (d_t - lam)|, then z_t = 1,
+    // z_i = -(e_i / D+_i) z_{i+1} above t and z_{i+1} = -(e_i / D-_{i+1}) z_i below.
+    double* dp = Dp[wave];
+    double* dm = Dm[wave];
+    double qf = guard_pivot(dg[0] - lam, pivmin), qb = guard_pivot(dg[N - 1] - lam, pivmin);
+    if (lane == 0) {
+      dp[0] = qf;
+      dm[N - 1] = qb;
     }
-    if (a_cur == 0.0) a_cur = tol;
-    Ai.put(N - 1, rcp_f64(a_cur), lane);
-
-    y.s0 = 1.0;
-    y.s1 = (lane + 64 < N) ? 1.0 : 0.0;
-    for (int iter = 0; iter < 3; ++iter) {
-      double ycur = y.get(0);
-      for (int k = 0; k < N - 1; ++k) {
-        const double ynext = y.get(k + 1);
-        const double ck = Cc.get(k);
-        const bool pk = (k < 64) ? ((piv0 >> k) & 1ull) : ((piv1 >> (k - 64)) & 1ull);
-        if (!pk) {
-          y.put(k, ycur, lane);
-          ycur = ynext - ck * ycur;
-        } else {
-          y.put(k, ynext, lane);
-          ycur = ycur - ck * ynext;
-        }
+    for (int st = 1; st < N; ++st) {
+      const int ib = N - 1 - st;
+      qf = guard_pivot((dg[st] - lam) - e2[st - 1] * rcp_f64(qf), pivmin);
+      qb = guard_pivot((dg[ib] - lam) - e2[ib] * rcp_f64(qb), pivmin);
+      if (lane == 0) {
+        dp[st] = qf;
+        dm[ib] = qb;
       }
-      double y1 = ycur * Ai.get(N - 1);
-      y.put(N - 1, y1, lane);
-      double y0 = (y.get(N - 2) - Bb.get(N - 2) * y1) * Ai.get(N - 2);
-      y.put(N - 2, y0, lane);
-      double y2 = y1;
-      y1 = y0;
-      for (int k = N - 3; k >= 0; --k) {
-        const double yk = (y.get(k) - Bb.get(k) * y1 - Dd.get(k) * y2) * Ai.get(k);
-        y.put(k, yk, lane);
-        y2 = y1;
-        y1 = yk;
-      }
-      // the start vector had max-norm 1: a growth near 1 / (eps |T|) means lam
-      // is an eigenvalue to working precision and y has converged
-      const double mx = wave_max(fmax(fabs(y.s0), fabs(y.s1)));
-      if (mx > 0.0) {
-        const double inv = 1.0 / mx;
-        y.s0 *= inv;
-        y.s1 *= inv;
-      }
-      if (mx * tol >= 0.03) break;
     }
+    wave_lds_sync();
+    double best = __builtin_inf();
+    int bt = 0;
+    for (int t = lane; t < N; t += 64) {
+      const double g = fabs(dp[t] + dm[t] - (dg[t] - lam));
+      if (g < best) {
+        best = g;
+        bt = t;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ov = __shfl_xor(best, o);
+      const int ot = __shfl_xor(bt, o);
+      if (ov < best || (ov == best && ot < bt)) {
+        best = ov;
+        bt = ot;
+      }
+    }
+    bt = __builtin_amdgcn_readfirstlane(bt);
+    wave_lds_sync();
+    // z overwrites dp: entry i of dp is read before z_i is stored there
+    double zu = 1.0, zd = 1.0;
+    for (int st = 1; st < N; ++st) {
+      const int iu = bt - st, id = bt + st;
+      if (iu >= 0) zu = -(ev[iu] * rcp_f64(dp[iu])) * zu;
+      if (id < N) zd = -(ev[id - 1] * rcp_f64(dm[id])) * zd;
+      if (lane == 0) {
+        if (iu >= 0) dp[iu] = zu;
+        if (id < N) dp[id] = zd;
+      }
+    }
+    if (lane == 0) dp[bt] = 1.0;
+    wave_lds_sync();
+    y0 = dp[lane];
+    y1 = (lane + 64 < N) ? dp[lane + 64] : 0.0;
   }
   __syncthreads();
 
   // ---- 4a. modified Gram-Schmidt in descending-eigenvalue order
   for (int k = 0; k < r; ++k) {
     if (wave == k) {
-      const double nrm = sqrt(wave_sum(y.s0 * y.s0 + y.s1 * y.s1));
+      const double nrm = sqrt(wave_sum(y0 * y0 + y1 * y1));
       if (nrm > 0.0) {
-        y.s0 /= nrm;
-        y.s1 /= nrm;
+        y0 /= nrm;
+        y1 /= nrm;
       }
-      zbuf[lane] = y.s0;
-      if (lane + 64 < N) zbuf[lane + 64] = y.s1;
+      zbuf[lane] = y0;
+      if (lane + 64 < N) zbuf[lane + 64] = y1;
     }
     __syncthreads();
     if (wave > k && wave < r) {
       const double z0 = zbuf[lane], z1 = (lane + 64 < N) ? zbuf[lane + 64] : 0.0;
-      const double dot = wave_sum(y.s0 * z0 + y.s1 * z1);
-      y.s0 -= dot * z0;
-      y.s1 -= dot * z1;
+      const double dot = wave_sum(y0 * z0 + y1 * z1);
+      y0 -= dot * z0;
+      y1 -= dot * z1;
     }
     __syncthreads();
   }
@@ -413,19 +426,22 @@ __global__ __launch_bounds__(kEigThreads) void eigen_kernel(const double* gram, 
     // ---- 4b. back-transformation u = H_0 H_1 ... H_{N-3} z
     for (int k = N - 3; k >= 0; --k) {
       const double beta = betas[k];
-      if (beta == 0.0) continue;
       const int i0 = lane, i1 = lane + 64;
-      const double v0 = Vst[k * N + i0];  // zero at and left of the diagonal
-      const double v1 = (i1 < N) ? Vst[k * N + i1] : 0.0;
-      const double f = beta * wave_sum(v0 * y.s0 + v1 * y.s1);
-      y.s0 -= f * v0;
-      y.s1 -= f * v1;
+      // reflector k is zero at and left of the diagonal; indexes are clamped
+      // into its stored row before the select
+      const double s0 = Vst[vrow(k) + (i0 > k ? i0 : k + 1)];
+      const double s1 = Vst[vrow(k) + (i1 > k && i1 < N ? i1 : k + 1)];
+      const double v0 = (i0 > k) ? s0 : 0.0;
+      const double v1 = (i1 > k && i1 < N) ? s1 : 0.0;
+      const double f = beta * wave_sum(v0 * y0 + v1 * y1);
+      y0 -= f * v0;
+      y1 -= f * v1;
     }
     // ---- sign rule: largest-magnitude entry positive (lowest index on ties)
-    double bv = fabs(y.s0);
+    double bv = fabs(y0);
     int bi = lane;
-    if (lane + 64 < N && fabs(y.s1) > bv) {
-      bv = fabs(y.s1);
+    if (lane + 64 < N && fabs(y1) > bv) {
+      bv = fabs(y1);
       bi = lane + 64;
     }
 #pragma unroll
@@ -437,11 +453,11 @@ __global__ __launch_bounds__(kEigThreads) void eigen_kernel(const double* gram, 
         bi = oi;
       }
     }
-    const double pivot = (bi < 64) ? readlane_f64(y.s0, bi) : readlane_f64(y.s1, bi - 64);
+    const double pivot = (bi < 64) ? readlane_f64(y0, bi) : readlane_f64(y1, bi - 64);
     const double sg = pivot < 0.0 ? -1.0 : 1.0;
     float* Uh = U + (int64_t)h * N * r;
-    Uh[lane * r + wave] = (float)(sg * y.s0);
-    if (lane + 64 < N) Uh[(lane + 64) * r + wave] = (float)(sg * y.s1);
+    Uh[lane * r + wave] = (float)(sg * y0);
+    if (lane + 64 < N) Uh[(lane + 64) * r + wave] = (float)(sg * y1);
   }
 }
 
@@ -468,13 +484,21 @@ hipError_t launch_gram(int D, int dtype, const void* q, int64_t n, int H, double
   return hipGetLastError();
 }
 
-hipError_t launch_eigen(int D, const double* gram, int nchunk, int64_t n_hist, int H, int r, float* U, float* S,
-                        hipStream_t s) {
+hipError_t launch_sens(int D, const double* gram, int nchunk, int64_t n_hist, int H, float* S, hipStream_t s) {
+  dim3 grid((unsigned)H), block((unsigned)D);
+  if (D == 128)
+    hipLaunchKernelGGL((sens_kernel<128>), grid, block, 0, s, gram, nchunk, n_hist, S);
+  else
+    hipLaunchKernelGGL((sens_kernel<64>), grid, block, 0, s, gram, nchunk, n_hist, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_eigen(int D, const double* gram, int nchunk, int H, int r, float* U, hipStream_t s) {
   dim3 grid((unsigned)H), block(kEigThreads);
   if (D == 128)
-    hipLaunchKernelGGL((eigen_kernel<128>), grid, block, 0, s, gram, nchunk, n_hist, r, U, S);
+    hipLaunchKernelGGL((eigen_kernel<128>), grid, block, 0, s, gram, nchunk, r, U);
   else
-    hipLaunchKernelGGL((eigen_kernel<64>), grid, block, 0, s, gram, nchunk, n_hist, r, U, S);
+    hipLaunchKernelGGL((eigen_kernel<64>), grid, block, 0, s, gram, nchunk, r, U);
   return hipGetLastError();
 }
 

@@ -124,6 +124,13 @@ struct qwm_cache {
   int64_t length = 0;
   std::vector<int64_t> epoch_start;  // committed epoch i lives in slot i
   bool staged_subspace = false;
+  // The eigensolve of build_subspace runs on `side` (created on first use,
+  // default priority) so the k-means of build_centroids, which needs only the
+  // sensitivity, overlaps it; `stream` waits for `join_ev` before the staged
+  // U is read or the Gram buffer is written again.
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  bool side_pending = false;
   bool profile = false;
   std::vector<ProfRec> pending;
   double prof_ms[QWM_K_COUNT] = {};
@@ -148,20 +155,30 @@ struct qwm_cache {
   float* part_o() const { return reinterpret_cast<float*>(arena + L.part_o); }
   float* part_ml() const { return reinterpret_cast<float*>(arena + L.part_ml); }
 
-  // Launch wrapper: optional event timing around one launch.
+  // Launch wrapper: optional event timing around one launch on stream `s`.
   template <class F>
-  hipError_t run(int kid, F&& f) {
+  hipError_t run_on(hipStream_t s, int kid, F&& f) {
     hipEvent_t a = nullptr, b = nullptr;
     if (profile) {
       if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return hipErrorOutOfMemory;
-      (void)hipEventRecord(a, stream);
+      (void)hipEventRecord(a, s);
     }
     hipError_t e = f();
     if (profile) {
-      (void)hipEventRecord(b, stream);
+      (void)hipEventRecord(b, s);
       pending.push_back({kid, a, b});
     }
     return e;
+  }
+  template <class F>
+  hipError_t run(int kid, F&& f) {
+    return run_on(stream, kid, f);
+  }
+  // Make the cache stream wait for an eigensolve still running on `side`.
+  hipError_t join_side() {
+    if (!side_pending) return hipSuccess;
+    side_pending = false;
+    return hipStreamWaitEvent(stream, join_ev, 0);
   }
 };
 
@@ -186,6 +203,8 @@ qwm_status check_ptr(const void* p, const char* name) {
 // Commit the staged calibration as a new epoch (or in place of an epoch that
 // holds no token yet). Capacity was checked by the caller.
 qwm_status commit_staged(qwm_cache* c) {
+  hipError_t je = c->join_side();
+  if (je != hipSuccess) return fail_hip(je, "join eigensolve");
   int slot = (int)c->epoch_start.size();
   if (!c->epoch_start.empty() && c->epoch_start.back() == c->length) slot -= 1;
   const int st = c->staged();
@@ -313,6 +332,13 @@ qwm_status qwm_create(const qwm_desc* desc, void* dev_arena, size_t arena_bytes,
 
 qwm_status qwm_destroy(qwm_cache* c) {
   if (!c) return fail(QWM_ERR_INVALID_ARG, "cache is NULL");
+  if (c->side) {
+    DeviceGuard g(c->device);
+    (void)hipStreamSynchronize(c->side);
+    (void)hipEventDestroy(c->fork_ev);
+    (void)hipEventDestroy(c->join_ev);
+    (void)hipStreamDestroy(c->side);
+  }
   for (auto& rec : c->pending) {
     (void)hipEventDestroy(rec.a);
     (void)hipEventDestroy(rec.b);
@@ -329,16 +355,36 @@ qwm_status qwm_build_subspace(qwm_cache* c, const void* q_hist, int64_t n_hist) 
   if (n_hist > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_CAPACITY, "n_hist too large");
   if ((st = need_device(c)) != QWM_OK) return st;
   DeviceGuard g(c->device);
+  hipError_t e;
+  if (!c->side) {
+    if ((e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess) {
+      c->side = nullptr;
+      return fail_hip(e, "create eigensolve stream");
+    }
+    if ((e = hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming)) != hipSuccess)
+      return fail_hip(e, "create eigensolve events");
+  }
+  // the previous eigensolve may still read the Gram buffer
+  if ((e = c->join_side()) != hipSuccess) return fail_hip(e, "join eigensolve");
   const int st_slot = c->staged();
-  hipError_t e = c->run(QWM_K_GRAM, [&] {
+  const int nchunk = qwm::gram_chunks(n_hist);
+  e = c->run(QWM_K_GRAM, [&] {
     return qwm::launch_gram(c->D, c->dtype, q_hist, n_hist, c->H, c->gram(), c->stream);
   });
   if (e != hipSuccess) return fail_hip(e, "gram");
-  e = c->run(QWM_K_EIGEN, [&] {
-    return qwm::launch_eigen(c->D, c->gram(), qwm::gram_chunks(n_hist), n_hist, c->H, c->r, c->slotU(st_slot),
-                             c->slotS(st_slot), c->stream);
+  e = c->run(QWM_K_GRAM, [&] {
+    return qwm::launch_sens(c->D, c->gram(), nchunk, n_hist, c->H, c->slotS(st_slot), c->stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "sensitivity");
+  if ((e = hipEventRecord(c->fork_ev, c->stream)) != hipSuccess) return fail_hip(e, "fork eigensolve");
+  if ((e = hipStreamWaitEvent(c->side, c->fork_ev, 0)) != hipSuccess) return fail_hip(e, "fork eigensolve");
+  e = c->run_on(c->side, QWM_K_EIGEN, [&] {
+    return qwm::launch_eigen(c->D, c->gram(), nchunk, c->H, c->r, c->slotU(st_slot), c->side);
   });
   if (e != hipSuccess) return fail_hip(e, "eigen");
+  if ((e = hipEventRecord(c->join_ev, c->side)) != hipSuccess) return fail_hip(e, "join eigensolve");
+  c->side_pending = true;
   c->staged_subspace = true;
   return QWM_OK;
 }
@@ -392,6 +438,7 @@ qwm_status qwm_import_calibration(qwm_cache* c, const void* C, const float* S_G,
   DeviceGuard g(c->device);
   const int stg = c->staged();
   hipError_t e;
+  if ((e = c->join_side()) != hipSuccess) return fail_hip(e, "join eigensolve");
   if ((e = hipMemcpyAsync(c->slotC(stg), C, (size_t)c->H * c->m * c->D * c->esz, hipMemcpyDeviceToDevice,
                           c->stream)) != hipSuccess)
     return fail_hip(e, "import C");
@@ -413,6 +460,7 @@ qwm_status qwm_export_calibration(const qwm_cache* cc, int32_t epoch, void* C, f
   if ((st = need_device(c)) != QWM_OK) return st;
   DeviceGuard g(c->device);
   hipError_t e;
+  if ((e = c->join_side()) != hipSuccess) return fail_hip(e, "join eigensolve");
   if (C && (e = hipMemcpyAsync(C, c->slotC(slot), (size_t)c->H * c->m * c->D * c->esz, hipMemcpyDeviceToDevice,
                                c->stream)) != hipSuccess)
     return fail_hip(e, "export C");
@@ -575,7 +623,7 @@ qwm_status qwm_truncate(qwm_cache* c, int64_t n_tokens) {
   if (c->epoch_start.size() != before && !c->epoch_start.empty()) {
     qwm_status st;
     if ((st = need_device(c)) != QWM_OK) return st;
-  DeviceGuard g(c->device);
+    DeviceGuard g(c->device);
     const int slot = (int)c->epoch_start.size() - 1;
     hipError_t e = c->run(QWM_K_OTHER, [&] {
       return qwm::launch_shadow(c->D, c->dtype, c->slotC(slot), c->slotU(slot), c->H, c->m, c->r, c->C32(),
