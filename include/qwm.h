@@ -4,12 +4,12 @@
  * QuantWM (arXiv 2609.26425; abstracts on fugumt.com and ai.info, article
  * on roboind.com) keeps the KV cache of an autoregressive video world model
  * in 2 bits per element:
- *   - QSAC ("Step 1" of the roboind.com article; "quantization-sensitivity-
- *     aware clustering" in the abstracts): each Key takes a high-precision
+ *   - QSAC (roboind.com article, section "Step 1"; the abstracts name it as
+ *     clustering aware of quantization sensitivity): each Key takes a high-precision
  *     centroid chosen by historical-Query sensitivity and residual range, and
  *     the Key-centroid residual is stored as per-group INT2;
  *   - Values are stored as plain per-group INT2;
- *   - PSAC ("Step 2"; "principal-subspace attention compensation"): the Key
+ *   - PSAC (section "Step 2"; attention compensation in a principal subspace): the Key
  *     error left after quantization is projected on the top-r principal
  *     directions of historical Queries, r coefficients per token are kept,
  *     and (q . U_r) . coef is added back to every attention logit.
@@ -81,7 +81,7 @@ typedef struct {
   int32_t n_centroids;      /* 1..256 (ids are stored as u8) */
   int32_t rank;             /* PSAC rank r: 1..16 */
   int32_t max_epochs;       /* calibration epochs kept: 1..64 */
-  int64_t capacity_tokens;  /* tokens per head the cache can hold */
+  int64_t capacity_tokens;  /* tokens per head the cache can hold, 1 .. 2^26 */
   int32_t dtype;            /* qwm_dtype of K/V/Q inputs and of the centroid table */
   int32_t reserved;         /* must be 0 */
   int64_t max_query_tokens; /* largest n_q of qwm_attend (sizes split-KV scratch) */
@@ -100,9 +100,10 @@ qwm_status qwm_create(const qwm_desc* desc, void* dev_arena, size_t arena_bytes,
 qwm_status qwm_destroy(qwm_cache* cache);
 
 /* PSAC basis and QSAC sensitivity from n_hist historical Queries q_hist
- * [heads][n_hist][head_dim] (fugumt.com abstract: "historical Query
- * sensitivity", "dominant Query subspace"; roboind.com "Step 2": energy of
- * historical Queries concentrates in a few principal directions).
+ * [heads][n_hist][head_dim] (fugumt.com abstract: QSAC weighs channels by how
+ * sensitive historical Queries are to them, PSAC works in their dominant
+ * subspace; roboind.com "Step 2": the energy of historical Queries sits in a
+ * few principal directions).
  * S_G = sum over the group's channels of mean q_j^2 (float64, stored float32);
  * U_r = top-r eigenvectors of the uncentered Gram Q^T Q (float64 on the
  * device: Householder tridiagonalization, multisection, twisted
@@ -139,8 +140,9 @@ qwm_status qwm_quantize_append(qwm_cache* cache, const void* k, const void* v, i
  * (all of them are in the chunk's past) plus an optional self segment of
  * n_self full-precision tokens k_self/v_self [heads][n_self][head_dim]. The
  * logit of cached token j is (q . khat_j + (q . U_r^(e(j))) . coef_j) *
- * softmax_scale, khat = c_id + zp + code * step (fugumt.com abstract: "restores
- * the remaining Key errors ... to stabilize attention logits"); self logits
+ * softmax_scale, khat = c_id + zp + code * step (fugumt.com abstract: PSAC puts
+ * the Key error left after quantization back along the dominant Query
+ * subspace so the logits stay stable); self logits
  * are q . k_self * softmax_scale. Softmax over all visible tokens, output the
  * probability-weighted sum of the dequantized / self Values into out
  * [heads][n_q][head_dim] float. 1 <= n_q <= max_query_tokens; k_self and

@@ -7,10 +7,10 @@ The product path (the HIP library and its Python binding) never imports,
 links or calls it, and this module imports nothing from the product path.
 
 Sources. The method is QuantWM (arXiv 2609.26425): the English abstract on
-fugumt.com ("QSAC ... jointly considers historical Query sensitivity and
-residual ranges to select INT2-friendly Key centroids"; "PSAC restores the
-remaining Key errors along the dominant Query subspace using low-rank
-projections"), the Italian author abstract on ai.info (same two techniques,
+fugumt.com (QSAC picks Key centroids that suit INT2 by weighing both the
+sensitivity of historical Queries and the range of the residual; PSAC puts the
+Key error that remains back along the dominant Query subspace through a
+low-rank projection), the Italian author abstract on ai.info (same two techniques,
 training-free and strictly causal), and the roboind.com article, sections
 "Step 1" (a Key is assigned a high-precision centroid and the Key-centroid
 residual is quantized to 2 bits; the nearest centroid is not necessarily the
@@ -116,8 +116,9 @@ def f64_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
 def sensitivity(q_hist: np.ndarray, g: int) -> np.ndarray:
     """Per-group Query sensitivity S_G (float32, shape [d // g]).
 
-    The abstracts say QSAC weighs "historical Query sensitivity" so as to cut
-    quantization error "in channels that are more critical to attention"; the
+    The abstracts say QSAC weighs the sensitivity of historical Queries so as
+    to cut the quantization error in the channels that matter most to
+    attention; the
     article's "Step 1" says what matters is which channels' errors reach the
     attention score. The reading taken: a Key error e changes the logit q.e,
     whose mean square over historical Queries is, under a diagonal
@@ -339,7 +340,7 @@ def build_centroids(keys, S, m: int, g: int, iters: int, dtype: str) -> np.ndarr
     """Centroid table C [m][d] (float32 values in the stored dtype).
 
     The article clusters the Keys around high-precision centers ("Step 1";
-    the compression figure counts the "aggregation centers" as stored
+    the compression figure, "Figure 4", counts the centers as stored
     overhead). The pages give no clustering details; the reading taken is
     Lloyd's algorithm with the QSAC assignment: start from
     ``init_centroids``, then ``iters`` times assign every Key by

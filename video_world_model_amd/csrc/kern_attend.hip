@@ -1,8 +1,8 @@
 // Attention over the 2-bit QuantWM cache with PSAC logit compensation (gfx950).
 //
-// Method (QuantWM; fugumt.com abstract: PSAC "restores the remaining Key
-// errors along the dominant Query subspace ... to stabilize attention
-// logits"; roboind.com "Step 2"): for cached token j of epoch e(j)
+// Method (QuantWM; fugumt.com abstract: PSAC puts the Key error left after
+// quantization back along the dominant Query subspace so the attention logits
+// stay stable; roboind.com "Step 2"): for cached token j of epoch e(j)
 //   l_ij = (q_i . khat_j + (q_i U_r^(e(j))) . coef_j) * scale,
 //   khat_j = c_id(j) + zp + code * step   (per 32-channel group),
 // plus optional full-precision self tokens of the attending chunk; softmax
@@ -37,10 +37,27 @@ struct AttnShape {
   static constexpr int KROW = 2 * D + 16 + 8;   // halfs per khat row: hi | lo | coef[16] | pad
   static constexpr int VROW = kTileKV + 8;      // halfs per vhat^T row
   static constexpr int NG = D / kGroup;
+  static constexpr int KITEMS = kTileKV * NG * 2;         // (token, 16-channel half group) items
+  static constexpr int VITEMS = (kTileKV / 4) * (D / 4);  // (4-token quad, 4-channel quad) items
+  static constexpr int KST = kTileKV * KROW;              // halfs of one khat stage
+  static constexpr int VST = D * VROW;                    // halfs of one vhat^T (hi or lo) stage
 };
 
 __device__ __forceinline__ floatx4 mfma16(const half8& a, const half8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// Two floats -> two fp16 (round to nearest even), one v_cvt_pk_f16_f32.
+__device__ __forceinline__ half2v pk_f16(float x, float y) { return __builtin_convertvector(float2v{x, y}, half2v); }
+
+// x -> hi = fp16(x), lo = fp16(x - hi) for a pair of floats: hi + lo carries
+// 22 significant bits of x.
+__device__ __forceinline__ void split2(float x0, float x1, half2v& hi, half2v& lo) {
+  hi = pk_f16(x0, x1);
+  lo = pk_f16(x0 - (float)hi[0], x1 - (float)hi[1]);
 }
 
 template <int DT, int N>
@@ -70,24 +87,70 @@ __device__ __forceinline__ void load_span(const void* base, int64_t off, float (
   }
 }
 
-__device__ __forceinline__ void split_hilo(float x, _Float16& hi, _Float16& lo) {
-  hi = (_Float16)x;
-  lo = (_Float16)(x - (float)hi);
+// Raw words of N input-dtype values -> floats (bf16: two per word).
+template <int DT, int N>
+__device__ __forceinline__ void unpack_span(const uint4* w, float (&x)[N]) {
+  if constexpr (DT == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * i + 2 * k] = __uint_as_float(ww[k] << 16);
+        x[8 * i + 2 * k + 1] = __uint_as_float(ww[k] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      x[4 * i] = __uint_as_float(w[i].x);
+      x[4 * i + 1] = __uint_as_float(w[i].y);
+      x[4 * i + 2] = __uint_as_float(w[i].z);
+      x[4 * i + 3] = __uint_as_float(w[i].w);
+    }
+  }
 }
 
+struct TileInfo {
+  int ep;      // epoch slot, -1 for the self segment
+  int tstart;  // first token (cache position, or index into the self K/V)
+  int tcount;  // tokens in the tile (<= 64)
+};
+
+__device__ __forceinline__ TileInfo tile_info(const AttnPlan& p, int tile) {
+  int sg = 0;
+  while (p.tile_prefix[sg + 1] <= tile) ++sg;
+  TileInfo ti;
+  ti.ep = p.seg_epoch[sg];
+  ti.tstart = p.seg_start[sg] + (tile - p.tile_prefix[sg]) * kTileKV;
+  const int tend = p.seg_start[sg] + p.seg_len[sg];
+  ti.tcount = (tend - ti.tstart) < kTileKV ? (tend - ti.tstart) : kTileKV;
+  return ti;
+}
+
+// Attention workgroup: 8 waves = 256 Queries of one head over the tiles
+// [tlo, thi) of one split. Two LDS stages: while the waves run the MFMA and
+// softmax work of tile i from one stage, the packed words of tile i+1 are
+// already in registers (loaded before that work) and are dequantized into the
+// other stage after it, so global latency hides behind the MFMA chains and
+// one barrier per tile suffices. Threads 0..KITEMS-1 build khat rows, threads
+// 256.. build vhat^T.
 template <int D, int DT, bool LOGITS>
 __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, const AttnPlan p) {
   using Sh = AttnShape<D>;
   constexpr int KS = Sh::KS, KROW = Sh::KROW, VROW = Sh::VROW, NG = Sh::NG;
   constexpr bool QLO = (DT == 1);  // float32 Queries also carry a lo part
-  constexpr int VSZ = LOGITS ? 8 : D * VROW;
-  constexpr int KITEMS = kTileKV * NG;               // (token, group) items of the khat tile
-  constexpr int VITEMS = (kTileKV / 4) * (D / 8);    // (4-token quad, 8-channel octet) items
-  constexpr int VBASE = kAttnThreads / 2;            // threads [VBASE, VBASE + VITEMS) dequantize V
-  static_assert(KITEMS <= VBASE && VITEMS <= kAttnThreads - VBASE, "dequant items must fit one pass");
-  __shared__ __attribute__((aligned(16))) _Float16 Ks[kTileKV * KROW];
-  __shared__ __attribute__((aligned(16))) _Float16 Vh[VSZ];
-  __shared__ __attribute__((aligned(16))) _Float16 Vl[VSZ];
+  constexpr int KST = Sh::KST, VST = LOGITS ? 0 : Sh::VST;
+  constexpr int KITEMS = Sh::KITEMS, VITEMS = Sh::VITEMS;
+  static_assert(KITEMS <= kAttnThreads && VITEMS <= kAttnThreads, "dequant items must fit one pass");
+  // Raw words one thread holds for the next tile: khat values (16 cache-dtype
+  // values), khat code/param word, 8 coefficients, vhat codes + params of 4
+  // tokens, and the 4x4 self Values.
+  constexpr int NK = (DT == 0) ? 2 : 4;  // uint4 words of 16 input values
+  constexpr int RK = 0, RKW = NK, RCF = NK + 1, RVC = NK + 2, RVS = NK + 4;
+  constexpr int NVS = (DT == 0) ? 2 : 4;  // uint4 words of 4 tokens x 4 channels
+  constexpr int NR = RVS + NVS;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2 * (KST + 2 * VST) + 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,10 +159,212 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
   const int split = blockIdx.y;
   const int64_t qw0 = (int64_t)blockIdx.x * kTileQ + wave * 32;
   const bool wave_live = qw0 < a.nq;  // waves whose 32 Queries are all padding skip the math
+  // wave-uniform producer roles (items are whole waves)
+  const bool is_k = wave < KITEMS / 64;
+  const bool is_v = !LOGITS && wave < VITEMS / 64;
+  // softmax in the log2 domain with a positive factor; a negative scale is
+  // carried by negated Queries (exact in fp16)
+  const float qsign = (!LOGITS && a.scale_log2 < 0.0f) ? -1.0f : 1.0f;
+  const float cl2 = a.scale_log2 * qsign;
 
   const int T = p.tile_prefix[p.n_seg];
   const int tlo = (int)(((int64_t)T * split) / a.splits);
   const int thi = (int)(((int64_t)T * (split + 1)) / a.splits);
+
+  // producer items: khat (token kt, channels 16*kq .. 16*kq+15, group kq/2);
+  // vhat (tokens 4*vtq .. 4*vtq+3, channels 4*vc4 .. 4*vc4+3)
+  const int kt = lane, kq = wave;
+  const int vtq = tid % (kTileKV / 4), vc4 = tid / (kTileKV / 4);
+
+  uint4 raw[NR];
+  int id_next = 0;
+
+  // Per-head bases (wave-uniform, scalar registers) and 32-bit per-thread
+  // offsets: every per-head region is below 4 GiB (capacity <= 2^26 tokens).
+  constexpr int ESZ = (DT == 0) ? 2 : 4;
+  const uint8_t* kcode_h = a.cache.kcode + (size_t)h * a.cache.capP * (D / 4);
+  const uint8_t* vcode_h = a.cache.vcode + (size_t)h * a.cache.capP * (D / 4);
+  const uint32_t* kparam_h = a.cache.kparam + (size_t)h * a.cache.capP * NG;
+  const uint32_t* vparam_h = a.cache.vparam + (size_t)h * a.cache.capP * NG;
+  const uint8_t* ids_h = a.cache.ids + (size_t)h * a.cache.capP;
+  const uint16_t* coef_h = a.cache.coef + (size_t)h * a.cache.capP * a.r;
+  const char* kself_h = reinterpret_cast<const char*>(a.kself) + (size_t)h * a.nself * D * ESZ;
+  const char* vself_h = reinterpret_cast<const char*>(a.vself) + (size_t)h * a.nself * D * ESZ;
+  const char* C_h = reinterpret_cast<const char*>(a.Cbase) + (size_t)h * a.m * D * ESZ;
+
+  // Token indices are clamped into the tile (tcount >= 1), so every load is
+  // unconditional and lands straight in its register: a register that is
+  // the target of a load still in flight must not be written on another path,
+  // or the wait for it would also wait for the whole prefetch. Rows past
+  // tcount hold a copy of the last token: finite values whose logits the
+  // softmax masks to -inf, so they get p = 0 and add nothing.
+  auto load_id = [&](const TileInfo& ti) -> int {
+    const int t = kt < ti.tcount ? kt : ti.tcount - 1;
+    return ids_h[ti.ep >= 0 ? (uint32_t)(ti.tstart + t) : 0u];  // self tiles: a valid dummy
+  };
+  // Issue the global loads of one tile's packed words (no use of the data).
+  // Every load is issued on every tile; the ones a tile does not need read a
+  // valid dummy address (the head's first cache slot), so no register is
+  // written on one path and left alone on another.
+  auto load_raw = [&](const TileInfo& ti, int id) {
+    const bool cache = ti.ep >= 0;  // wave-uniform
+    if (is_k) {
+      const uint32_t slot = (uint32_t)(ti.tstart + (kt < ti.tcount ? kt : ti.tcount - 1));
+      const uint32_t cs = cache ? slot : 0u;
+      const char* Ce = C_h + (size_t)(cache ? ti.ep : 0) * a.epoch_C_stride;  // uniform
+      const uint4* src = cache ? reinterpret_cast<const uint4*>(Ce + ((uint32_t)id * D + 16 * kq) * ESZ)
+                               : reinterpret_cast<const uint4*>(kself_h + (slot * D + 16 * kq) * ESZ);
+#pragma unroll
+      for (int i = 0; i < NK; ++i) raw[RK + i] = src[i];
+      raw[RKW].x = *reinterpret_cast<const uint32_t*>(kcode_h + cs * (D / 4) + 4 * kq);
+      raw[RKW].y = kparam_h[cs * NG + (kq >> 1)];
+      // coefficients 8*kq .. 8*kq+7 of the token (halves past r are zeroed at
+      // store); r even: four dword loads, r odd: halves one by one
+      const uint16_t* cf = coef_h + cs * (uint32_t)a.r + (kq < 2 ? 8 * kq : 0);
+      if ((a.r & 1) == 0) {
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(cf);
+        raw[RCF] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      } else {
+        uint32_t cc[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int j = (kq < 2 ? 8 * kq : 0) + 2 * s2;
+          const uint32_t lo = (j < a.r) ? cf[2 * s2] : 0u;
+          const uint32_t hi = (j + 1 < a.r) ? cf[2 * s2 + 1] : 0u;
+          cc[s2] = lo | (hi << 16);
+        }
+        raw[RCF] = make_uint4(cc[0], cc[1], cc[2], cc[3]);
+      }
+    }
+    if (is_v) {
+      uint32_t slot[4], cs[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = 4 * vtq + u;
+        slot[u] = (uint32_t)(ti.tstart + (t < ti.tcount ? t : ti.tcount - 1));
+        cs[u] = cache ? slot[u] : 0u;
+      }
+      // channels 4*vc4 .. +3 of a token: one byte of codes, group vc4/8
+      raw[RVC] = make_uint4(vcode_h[cs[0] * (D / 4) + vc4], vcode_h[cs[1] * (D / 4) + vc4],
+                            vcode_h[cs[2] * (D / 4) + vc4], vcode_h[cs[3] * (D / 4) + vc4]);
+      raw[RVC + 1] = make_uint4(vparam_h[cs[0] * NG + (vc4 >> 3)], vparam_h[cs[1] * NG + (vc4 >> 3)],
+                                vparam_h[cs[2] * NG + (vc4 >> 3)], vparam_h[cs[3] * NG + (vc4 >> 3)]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const char* src = cache ? reinterpret_cast<const char*>(vcode_h) : vself_h + (slot[u] * D + 4 * vc4) * ESZ;
+        if constexpr (DT == 0) {
+          const uint2 w = *reinterpret_cast<const uint2*>(src);
+          if (u & 1) {
+            raw[RVS + u / 2].z = w.x;
+            raw[RVS + u / 2].w = w.y;
+          } else {
+            raw[RVS + u / 2].x = w.x;
+            raw[RVS + u / 2].y = w.y;
+          }
+        } else {
+          raw[RVS + u] = *reinterpret_cast<const uint4*>(src);
+        }
+      }
+    }
+  };
+  // Dequantize the loaded words into LDS stage `st`.
+  auto store_stage = [&](const TileInfo& ti, int st) {
+    _Float16* Ks = lds + st * (KST + 2 * VST);
+    if (is_k) {
+      _Float16* row = Ks + kt * KROW;
+      const bool cache = ti.ep >= 0;
+      const float zpf = half_bits_to_float(raw[RKW].y & 0xFFFFu), scf = half_bits_to_float(raw[RKW].y >> 16);
+      const uint32_t w = raw[RKW].x;  // codes of channels 16*kq .. +15
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        half8 h8, l8;
+        float x[8];
+        unpack_span<DT, 8>(raw + RK + u * (NK / 2), x);
+        if (cache) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float code = (float)((w >> (16 * u + 2 * c)) & 3u);
+            x[c] = x[c] + __builtin_fmaf(code, scf, zpf);  // zp + code*step: exact
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          half2v hi, lo;
+          split2(x[2 * c], x[2 * c + 1], hi, lo);
+          h8[2 * c] = hi[0];
+          h8[2 * c + 1] = hi[1];
+          l8[2 * c] = lo[0];
+          l8[2 * c + 1] = lo[1];
+        }
+        *reinterpret_cast<half8*>(row + 16 * kq + 8 * u) = h8;
+        *reinterpret_cast<half8*>(row + D + 16 * kq + 8 * u) = l8;
+      }
+      if (kq < 2) {
+        uint4 cfw = raw[RCF];
+        const int j0 = 8 * kq;  // halves j0 .. j0+7; keep those below r
+        const bool use = cache;
+        cfw.x = (use && j0 + 0 < a.r) ? (j0 + 1 < a.r ? cfw.x : cfw.x & 0xFFFFu) : 0u;
+        cfw.y = (use && j0 + 2 < a.r) ? (j0 + 3 < a.r ? cfw.y : cfw.y & 0xFFFFu) : 0u;
+        cfw.z = (use && j0 + 4 < a.r) ? (j0 + 5 < a.r ? cfw.z : cfw.z & 0xFFFFu) : 0u;
+        cfw.w = (use && j0 + 6 < a.r) ? (j0 + 7 < a.r ? cfw.w : cfw.w & 0xFFFFu) : 0u;
+        *reinterpret_cast<uint4*>(row + 2 * D + 8 * kq) = cfw;
+      }
+    }
+    if constexpr (!LOGITS) {
+      if (is_v) {
+        _Float16* Vh = Ks + KST;
+        _Float16* Vl = Vh + VST;
+        // token 4*vtq+u of the tile goes to column 32*ks + 8*gg + 4*b + u of the
+        // row, the order in which the P fragment of lane group gg holds tokens
+        // {4gg..4gg+3, 16+4gg..16+4gg+3} of each 32-token step ks
+        const int ks = vtq / 8, b = (vtq % 8) / 4, gg = vtq % 4;
+        const int col = 32 * ks + 8 * gg + 4 * b;
+        const bool cache = ti.ep >= 0;
+        const uint32_t cws[4] = {raw[RVC].x, raw[RVC].y, raw[RVC].z, raw[RVC].w};
+        const uint32_t prs[4] = {raw[RVC + 1].x, raw[RVC + 1].y, raw[RVC + 1].z, raw[RVC + 1].w};
+        float xs[4][4];  // [token][channel]
+        if (!cache) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if constexpr (DT == 0) {
+              const uint4 wq = raw[RVS + u / 2];
+              const uint32_t w0 = (u & 1) ? wq.z : wq.x, w1 = (u & 1) ? wq.w : wq.y;
+              xs[u][0] = __uint_as_float(w0 << 16);
+              xs[u][1] = __uint_as_float(w0 & 0xFFFF0000u);
+              xs[u][2] = __uint_as_float(w1 << 16);
+              xs[u][3] = __uint_as_float(w1 & 0xFFFF0000u);
+            } else {
+              const uint4 wq = raw[RVS + u];
+              xs[u][0] = __uint_as_float(wq.x);
+              xs[u][1] = __uint_as_float(wq.y);
+              xs[u][2] = __uint_as_float(wq.z);
+              xs[u][3] = __uint_as_float(wq.w);
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float xv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float x;
+            if (cache) {
+              const float zp = half_bits_to_float(prs[u] & 0xFFFFu), sc = half_bits_to_float(prs[u] >> 16);
+              x = __builtin_fmaf((float)((cws[u] >> (2 * c)) & 3u), sc, zp);
+            } else {
+              x = xs[u][c];
+            }
+            xv[u] = x;
+          }
+          half2v h0, l0, h1, l1;
+          split2(xv[0], xv[1], h0, l0);
+          split2(xv[2], xv[3], h1, l1);
+          *reinterpret_cast<half4*>(Vh + (4 * vc4 + c) * VROW + col) = half4{h0[0], h0[1], h1[0], h1[1]};
+          *reinterpret_cast<half4*>(Vl + (4 * vc4 + c) * VROW + col) = half4{l0[0], l0[1], l1[0], l1[1]};
+        }
+      }
+    }
+  };
 
   // Query fragments (B operand): Query qw0 + 16*qb + l16, channels 32*ks + 8*g .. +7.
   half8 qh[2][KS];
@@ -114,12 +379,16 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
       float x[8];
       load_span<DT, 8>(a.q, base + 32 * ks + 8 * g, x);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float xv = qv ? x[s] : 0.0f;
-        _Float16 hi, lo;
-        split_hilo(xv, hi, lo);
-        qh[qb][ks][s] = hi;
-        if constexpr (QLO) ql[qb][ks][s] = lo;
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const float x0 = qv ? qsign * x[2 * s2] : 0.0f, x1 = qv ? qsign * x[2 * s2 + 1] : 0.0f;
+        half2v hi, lo;
+        split2(x0, x1, hi, lo);
+        qh[qb][ks][2 * s2] = hi[0];
+        qh[qb][ks][2 * s2 + 1] = hi[1];
+        if constexpr (QLO) {
+          ql[qb][ks][2 * s2] = lo[0];
+          ql[qb][ks][2 * s2 + 1] = lo[1];
+        }
       }
     }
   }
@@ -127,274 +396,216 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qu[qb][s] = (_Float16)0.0f;
+    for (int s2 = 0; s2 < 8; ++s2) qu[qb][s2] = (_Float16)0.0f;
   int cur_epoch = -2;
 
-  floatx4 O[2][D / 16];
+  floatx4 O[2][LOGITS ? 1 : D / 16];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb) O[qb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-__builtin_inff(), -__builtin_inff()};
+    for (int cb = 0; cb < (LOGITS ? 1 : D / 16); ++cb) O[qb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // per lane: this lane's share of the row sum of the fp16 P (the values the
+  // PV product uses), float32
   float lrow[2] = {0.0f, 0.0f};
+  float mrow[2] = {-__builtin_inff(), -__builtin_inff()};
+  const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
+
+  // Waves 0-3 and 4-7 share the four SIMDs pairwise and run the tile in
+  // opposite orders so that one wave's MFMA chains overlap the other's
+  // dequantization: group 0 loads tile i+1, computes tile i, then writes tile
+  // i+1 to LDS; group 1 writes tile i+1 (loaded during the previous tile),
+  // computes tile i, then loads tile i+2.
+  const bool late = (wave >> 2) & 1;  // wave-uniform
+
+  // prologue: tile tlo into stage 0; group 1 also has tile tlo+1 in registers
+  if (tlo < thi) {
+    const TileInfo t0 = tile_info(p, tlo);
+    load_raw(t0, load_id(t0));
+    store_stage(t0, 0);
+    if (!late) {
+      if (tlo + 1 < thi) id_next = load_id(tile_info(p, tlo + 1));
+    } else if (tlo + 1 < thi) {
+      const TileInfo t1 = tile_info(p, tlo + 1);
+      load_raw(t1, load_id(t1));
+      if (tlo + 2 < thi) id_next = load_id(tile_info(p, tlo + 2));
+    }
+  }
+  __syncthreads();
 
   for (int tile = tlo; tile < thi; ++tile) {
-    int sg = 0;
-    while (p.tile_prefix[sg + 1] <= tile) ++sg;
-    const int ep = p.seg_epoch[sg];
-    const int tstart = p.seg_start[sg] + (tile - p.tile_prefix[sg]) * kTileKV;
-    const int tend = p.seg_start[sg] + p.seg_len[sg];
-    const int tcount = (tend - tstart) < kTileKV ? (tend - tstart) : kTileKV;
-
-    __syncthreads();  // previous tile's LDS reads are complete
-    if (tid < KITEMS) {
-      // ---- khat row segment: item = (token t = it % 64, group G = it / 64); a wave
-      // writes 64 consecutive rows of one group (row pitch 140 dwords spreads
-      // 16 rows over all 64 banks).
-      const int t = tid % kTileKV, G = tid / kTileKV;
-      _Float16* row = Ks + t * KROW;
-      half8 hv[4], lv[4];
-      if (t < tcount) {
-        float x[32];
-        if (ep >= 0) {
-          const int64_t slot = (int64_t)h * a.cache.capP + tstart + t;
-          const uint2 cw = *reinterpret_cast<const uint2*>(a.cache.kcode + slot * (D / 4) + 8 * G);
-          const uint32_t pr = a.cache.kparam[slot * NG + G];
-          const float zpf = half_bits_to_float(pr & 0xFFFFu), scf = half_bits_to_float(pr >> 16);
-          const int id = a.cache.ids[slot];
-          const void* Cb = reinterpret_cast<const char*>(a.Cbase) + (int64_t)ep * a.epoch_C_stride;
-          load_span<DT, 32>(Cb, ((int64_t)h * a.m + id) * D + 32 * G, x);
-#pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            const uint32_t w = j < 16 ? cw.x : cw.y;
-            const float code = (float)((w >> (2 * (j & 15))) & 3u);
-            x[j] = x[j] + __builtin_fmaf(code, scf, zpf);  // zp + code*step: the product is exact
-          }
-        } else {
-          load_span<DT, 32>(a.kself, ((int64_t)h * a.nself + tstart + t) * D + 32 * G, x);
-        }
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          _Float16 hi, lo;
-          split_hilo(x[j], hi, lo);
-          hv[j >> 3][j & 7] = hi;
-          lv[j >> 3][j & 7] = lo;
-        }
+    const int st = (tile - tlo) & 1;
+    const TileInfo ti = tile_info(p, tile);
+    TileInfo tn{};
+    if (tile + 1 < thi) tn = tile_info(p, tile + 1);
+    if (tile + 1 < thi) {
+      if (!late) {
+        load_raw(tn, id_next);
+        if (tile + 2 < thi) id_next = load_id(tile_info(p, tile + 2));
       } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            hv[u][s] = (_Float16)0.0f;
-            lv[u][s] = (_Float16)0.0f;
-          }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        *reinterpret_cast<half8*>(row + 32 * G + 8 * u) = hv[u];
-        *reinterpret_cast<half8*>(row + D + 32 * G + 8 * u) = lv[u];
-      }
-      if (G == 0) {
-        half8 c0, c1;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          c0[s] = (_Float16)0.0f;
-          c1[s] = (_Float16)0.0f;
-        }
-        if (t < tcount && ep >= 0) {
-          const int64_t slot = (int64_t)h * a.cache.capP + tstart + t;
-          const uint16_t* cf = a.cache.coef + slot * a.r;
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            if (s < a.r) c0[s] = (_Float16)half_bits_to_float(cf[s]);
-            if (s + 8 < a.r) c1[s] = (_Float16)half_bits_to_float(cf[s + 8]);
-          }
-        }
-        *reinterpret_cast<half8*>(row + 2 * D) = c0;
-        *reinterpret_cast<half8*>(row + 2 * D + 8) = c1;
+        store_stage(tn, st ^ 1);
       }
     }
-    if constexpr (!LOGITS) {
-      if (tid >= VBASE && tid < VBASE + VITEMS) {
-        // ---- vhat^T: item = (quad tq = it % 16, octet co = it / 16); the 16 quads
-        // of a wave land on 16 different bank pairs of each row.
-        const int it = tid - VBASE;
-        const int tq = it % (kTileKV / 4), co = it / (kTileKV / 4);
-        half4 vh4[8], vl4[8];
+
+    if (wave_live) {
+      const _Float16* Ks = lds + st * (KST + 2 * VST);
+      const int ep = ti.ep;
+      // ---- per-epoch PSAC Query fragment: lanes g<2 hold qU_hi, g>=2 qU_lo
+      if (ep != cur_epoch) {
+        cur_epoch = ep;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int t = 4 * tq + u;
-          float x[8];
-          if (t < tcount) {
-            if (ep >= 0) {
-              const int64_t slot = (int64_t)h * a.cache.capP + tstart + t;
-              const uint32_t cw = *reinterpret_cast<const uint16_t*>(a.cache.vcode + slot * (D / 4) + 2 * co);
-              const uint32_t pr = a.cache.vparam[slot * NG + (co >> 2)];
-              const float zpf = half_bits_to_float(pr & 0xFFFFu), scf = half_bits_to_float(pr >> 16);
+        for (int qb = 0; qb < 2; ++qb) {
+          const int64_t qi = qw0 + 16 * qb + l16;
+          if (ep >= 0 && qi < a.nq) {
+            const float* src =
+                a.qU + (((int64_t)h * a.n_epoch_slots + ep) * a.nq + qi) * kRankPad + 8 * (g & 1);
 #pragma unroll
-              for (int s = 0; s < 8; ++s) x[s] = __builtin_fmaf((float)((cw >> (2 * s)) & 3u), scf, zpf);
-            } else {
-              load_span<DT, 8>(a.vself, ((int64_t)h * a.nself + tstart + t) * D + 8 * co, x);
+            for (int s2 = 0; s2 < 4; ++s2) {
+              half2v hi, lo;
+              split2(qsign * src[2 * s2], qsign * src[2 * s2 + 1], hi, lo);
+              qu[qb][2 * s2] = (g < 2) ? hi[0] : lo[0];
+              qu[qb][2 * s2 + 1] = (g < 2) ? hi[1] : lo[1];
             }
           } else {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) x[s] = 0.0f;
+            for (int s2 = 0; s2 < 8; ++s2) qu[qb][s2] = (_Float16)0.0f;
           }
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            _Float16 hi, lo;
-            split_hilo(x[s], hi, lo);
-            vh4[s][u] = hi;
-            vl4[s][u] = lo;
-          }
-        }
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          *reinterpret_cast<half4*>(Vh + (8 * co + s) * VROW + 4 * tq) = vh4[s];
-          *reinterpret_cast<half4*>(Vl + (8 * co + s) * VROW + 4 * tq) = vl4[s];
         }
       }
-    }
-    __syncthreads();
-    if (!wave_live) continue;
 
-    // ---- per-epoch PSAC Query fragment: lanes g<2 hold qU_hi, g>=2 qU_lo
-    if (ep != cur_epoch) {
-      cur_epoch = ep;
+      // ---- logits: S^T blocks [16 tokens x 16 Queries]
+      floatx4 S[2][4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int64_t qi = qw0 + 16 * qb + l16;
-        if (ep >= 0 && qi < a.nq) {
-          const float* src = a.qU + (((int64_t)h * a.n_epoch_slots + ep) * a.nq + qi) * kRankPad + 8 * (g & 1);
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            _Float16 hi, lo;
-            split_hilo(src[s], hi, lo);
-            qu[qb][s] = (g < 2) ? hi : lo;
-          }
-        } else {
+        for (int tb = 0; tb < 4; ++tb) S[qb][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 8; ++s) qu[qb][s] = (_Float16)0.0f;
-        }
-      }
-    }
-
-    // ---- logits: S^T blocks [16 tokens x 16 Queries]
-    floatx4 S[2][4];
+      for (int ks = 0; ks < KS; ++ks) {
+        // keep the scheduler from hoisting every operand read of the loop
+        // (register pressure): one 32-channel step at a time
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) S[qb][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const _Float16* r0 = Ks + (16 * tb + l16) * KROW + 32 * ks + 8 * g;
-        const half8 ahi = *reinterpret_cast<const half8*>(r0);
-        const half8 alo = *reinterpret_cast<const half8*>(r0 + D);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          S[qb][tb] = mfma16(ahi, qh[qb][ks], S[qb][tb]);
-          S[qb][tb] = mfma16(alo, qh[qb][ks], S[qb][tb]);
-          if constexpr (QLO) S[qb][tb] = mfma16(ahi, ql[qb][ks], S[qb][tb]);
-        }
-      }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const half8 ac = *reinterpret_cast<const half8*>(Ks + (16 * tb + l16) * KROW + 2 * D + 8 * (g & 1));
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) S[qb][tb] = mfma16(ac, qu[qb], S[qb][tb]);
-    }
-
-    if constexpr (LOGITS) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int64_t qi = qw0 + 16 * qb + l16;
-        if (qi >= a.nq) continue;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int j = 16 * tb + 4 * g + v;
-            if (j < tcount) a.logits[qi * a.logit_len + tstart + j] = S[qb][tb][v] * a.scale;
-          }
-      }
-      continue;
-    } else {
-      // ---- online softmax (log2 domain). The running max is only raised when
-      // a row's new max exceeds it by more than 8 (p <= 2^8 stays exact
-      // enough in fp16 and float32), so the output rescale is rare.
-      const bool full = (tcount == kTileKV) && !(ep < 0 && a.causal_self);
-      half8 pf[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int64_t qi = qw0 + 16 * qb + l16;
-        float sv[4][4];
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float x = S[qb][tb][v] * a.scale_log2;
-            if (!full) {
-              const int j = 16 * tb + 4 * g + v;
-              bool ok = j < tcount;
-              if (ep < 0 && a.causal_self) ok = ok && ((int64_t)(tstart + j) <= qi);
-              x = ok ? x : -__builtin_inff();
-            }
-            sv[tb][v] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool raise = mx > mrow[qb] + 8.0f;
-        if (__ballot(raise)) {  // wave-uniform: rescale every lane (alpha = 1 where unchanged)
-          const float mnew = raise ? mx : mrow[qb];
-          const float alpha = (mrow[qb] == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(mrow[qb] - mnew);
-          mrow[qb] = mnew;
-          lrow[qb] *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < D / 16; ++cb) O[qb][cb] *= alpha;
-        }
-        const float mcur = mrow[qb];
-        const bool none = (mcur == -__builtin_inff());
-        float ps = 0.0f;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float pv = none ? 0.0f : __builtin_amdgcn_exp2f(sv[tb][v] - mcur);
-            sv[tb][v] = pv;
-            ps += pv;
-          }
-        lrow[qb] += ps;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            pf[qb][ks][v] = (_Float16)sv[2 * ks][v];
-            pf[qb][ks][4 + v] = (_Float16)sv[2 * ks + 1][v];
-          }
-      }
-      // ---- o^T += vhat^T P^T (tokens {4g..4g+3, 16+4g..16+4g+3} of each 32-token step)
-#pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int off = (16 * cb + l16) * VROW + 32 * ks + 4 * g;
-          const half4 h0 = *reinterpret_cast<const half4*>(Vh + off);
-          const half4 h1 = *reinterpret_cast<const half4*>(Vh + off + 16);
-          const half4 l0 = *reinterpret_cast<const half4*>(Vl + off);
-          const half4 l1 = *reinterpret_cast<const half4*>(Vl + off + 16);
-          const half8 ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-          const half8 al = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        for (int tb = 0; tb < 4; ++tb) {
+          const _Float16* r0 = Ks + (16 * tb + l16) * KROW + 32 * ks + 8 * g;
+          const half8 ahi = *reinterpret_cast<const half8*>(r0);
+          const half8 alo = *reinterpret_cast<const half8*>(r0 + D);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
-            O[qb][cb] = mfma16(ah, pf[qb][ks], O[qb][cb]);
-            O[qb][cb] = mfma16(al, pf[qb][ks], O[qb][cb]);
+            S[qb][tb] = mfma16(ahi, qh[qb][ks], S[qb][tb]);
+            S[qb][tb] = mfma16(alo, qh[qb][ks], S[qb][tb]);
+            if constexpr (QLO) S[qb][tb] = mfma16(ahi, ql[qb][ks], S[qb][tb]);
           }
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const half8 ac = *reinterpret_cast<const half8*>(Ks + (16 * tb + l16) * KROW + 2 * D + 8 * (g & 1));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) S[qb][tb] = mfma16(ac, qu[qb], S[qb][tb]);
+      }
+
+      if constexpr (LOGITS) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int64_t qi = qw0 + 16 * qb + l16;
+          if (qi < a.nq) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int j = 16 * tb + 4 * g + v;
+                if (j < ti.tcount) a.logits[qi * a.logit_len + ti.tstart + j] = S[qb][tb][v] * a.scale;
+              }
+          }
+        }
+      } else {
+        // ---- online softmax (log2 domain). The running max is only raised
+        // when a row's new max exceeds it by more than 8 (p <= 2^8 stays exact
+        // enough in fp16 and float32), so the output rescale is rare.
+        const bool full = (ti.tcount == kTileKV) && !(ep < 0 && a.causal_self);
+        half8 pf[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int64_t qi = qw0 + 16 * qb + l16;
+          if (!full) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int j = 16 * tb + 4 * g + v;
+                bool ok = j < ti.tcount;
+                if (ep < 0 && a.causal_self) ok = ok && ((int64_t)(ti.tstart + j) <= qi);
+                if (!ok) S[qb][tb][v] = -__builtin_inff();
+              }
+          }
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, S[qb][tb][v]);
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          mx *= cl2;
+          const bool raise = mx > mrow[qb] + 8.0f;
+          if (__ballot(raise)) {  // wave-uniform: rescale every lane (alpha = 1 where unchanged)
+            const float mnew = raise ? mx : mrow[qb];
+            const float alpha = (mrow[qb] == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(mrow[qb] - mnew);
+            mrow[qb] = mnew;
+            lrow[qb] *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < D / 16; ++cb) O[qb][cb] *= alpha;
+          }
+          // mrow is finite as soon as any logit of the row is: a row still at
+          // -inf has only masked (-inf) logits, and exp2(-inf * c + 0) = 0
+          const float nm = (mrow[qb] == -__builtin_inff()) ? 0.0f : -mrow[qb];
+          float pv[4][4];
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pv[tb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][tb][v], cl2, nm));
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const half2v p0 = pk_f16(pv[2 * ks][0], pv[2 * ks][1]), p1 = pk_f16(pv[2 * ks][2], pv[2 * ks][3]);
+            const half2v p2 = pk_f16(pv[2 * ks + 1][0], pv[2 * ks + 1][1]);
+            const half2v p3 = pk_f16(pv[2 * ks + 1][2], pv[2 * ks + 1][3]);
+            pf[qb][ks] = half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            // exact fp16 values summed in float32: v_dot2_f32_f16 with (1, 1)
+            float l = lrow[qb];
+            l = __builtin_amdgcn_fdot2(p0, one2, l, false);
+            l = __builtin_amdgcn_fdot2(p1, one2, l, false);
+            l = __builtin_amdgcn_fdot2(p2, one2, l, false);
+            l = __builtin_amdgcn_fdot2(p3, one2, l, false);
+            lrow[qb] = l;
+          }
+        }
+        // ---- o^T += vhat^T P^T
+        const _Float16* Vh = Ks + KST;
+        const _Float16* Vl = Vh + VST;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int cb = 0; cb < D / 16; ++cb) {
+            if (cb % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+            const int off = (16 * cb + l16) * VROW + 32 * ks + 8 * g;
+            const half8 ah = *reinterpret_cast<const half8*>(Vh + off);
+            const half8 al = *reinterpret_cast<const half8*>(Vl + off);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              O[qb][cb] = mfma16(ah, pf[qb][ks], O[qb][cb]);
+              O[qb][cb] = mfma16(al, pf[qb][ks], O[qb][cb]);
+            }
+          }
+        }
+      }
     }
+
+    if (!late) {
+      if (tile + 1 < thi) store_stage(tn, st ^ 1);
+    } else if (tile + 2 < thi) {
+      load_raw(tile_info(p, tile + 2), id_next);
+      if (tile + 3 < thi) id_next = load_id(tile_info(p, tile + 3));
+    }
+    __syncthreads();
   }
 
   if constexpr (!LOGITS) {
@@ -431,22 +642,32 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
   }
 }
 
-// Log-sum-exp merge of the split-KV partials (log2 domain).
+// Log-sum-exp merge of the split-KV partials (log2 domain): one thread per
+// (head, Query, 4 channels), every split's partial row read once.
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const AttnArgs a) {
-  const int64_t qi = blockIdx.x;
-  const int h = blockIdx.y, c = threadIdx.x;
+__global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)a.H * a.nq;
+  if (idx >= rows * (D / 4)) return;
+  const int64_t row = idx / (D / 4);  // h * nq + qi
+  const int c4 = (int)(idx % (D / 4));
   float M = -__builtin_inff();
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[(((int64_t)s * a.H + h) * a.nq + qi) * 2]);
-  float L = 0.0f, o = 0.0f;
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[(s * rows + row) * 2]);
+  float L = 0.0f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < a.splits; ++s) {
-    const int64_t row = ((int64_t)s * a.H + h) * a.nq + qi;
-    const float m = a.part_ml[row * 2];
+    const int64_t pr = s * rows + row;
+    const float m = a.part_ml[pr * 2];
     const float w = (m == -__builtin_inff()) ? 0.0f : exp2f(m - M);
-    L += a.part_ml[row * 2 + 1] * w;
-    o += a.part_o[row * D + c] * w;
+    L += a.part_ml[pr * 2 + 1] * w;
+    const float4 po = *reinterpret_cast<const float4*>(a.part_o + pr * D + 4 * c4);
+    o.x += po.x * w;
+    o.y += po.y * w;
+    o.z += po.z * w;
+    o.w += po.w * w;
   }
-  a.out[((int64_t)h * a.nq + qi) * D + c] = o / L;
+  const float inv = 1.0f / L;
+  *reinterpret_cast<float4*>(a.out + row * D + 4 * c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
 // q . U_r for every epoch slot: qU[h][e][i][k] (k < 16, zero for k >= r).
@@ -506,7 +727,8 @@ hipError_t launch_attend_logits(int D, int dtype, const AttnArgs& a, const AttnP
 }
 
 hipError_t launch_merge(int D, const AttnArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)a.nq, (unsigned)a.H), block((unsigned)D);
+  const int64_t n = (int64_t)a.H * a.nq * (D / 4);
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
   if (D == 128)
     hipLaunchKernelGGL((merge_kernel<128>), grid, block, 0, s, a);
   else

@@ -2,7 +2,8 @@
 //
 // Method (QuantWM; roboind.com article "Step 2": the energy of historical
 // Queries concentrates in a few principal directions; fugumt.com abstract:
-// "dominant Query subspace", "historical Query sensitivity"):
+// QSAC weighs channels by the sensitivity of historical Queries, PSAC works
+// in their dominant subspace):
 //   Gram = Q^T Q (uncentered, float64),
 //   S_G  = (sum over the group's channels of Gram_jj) / M, stored float32,
 //   U_r  = eigenvectors of Gram with the r largest eigenvalues, descending,

@@ -50,8 +50,8 @@ qwm_status check_desc(const qwm_desc* d) {
   if (d->n_centroids < 1 || d->n_centroids > 256) return fail(QWM_ERR_UNSUPPORTED, "n_centroids must be 1..256");
   if (d->rank < 1 || d->rank > qwm::kRankPad) return fail(QWM_ERR_UNSUPPORTED, "rank must be 1..16");
   if (d->max_epochs < 1 || d->max_epochs > qwm::kMaxEpochs) return fail(QWM_ERR_UNSUPPORTED, "max_epochs must be 1..64");
-  if (d->capacity_tokens > (int64_t)INT32_MAX - 2 * qwm::kTileKV)
-    return fail(QWM_ERR_UNSUPPORTED, "capacity_tokens beyond 2^31 - 128");
+  if (d->capacity_tokens > ((int64_t)1 << 26))
+    return fail(QWM_ERR_UNSUPPORTED, "capacity_tokens beyond 2^26 per head");
   if (d->max_query_tokens > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_UNSUPPORTED, "max_query_tokens too large");
   if (d->max_build_tokens > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_UNSUPPORTED, "max_build_tokens too large");
   return QWM_OK;
@@ -64,7 +64,7 @@ Layout make_layout(const qwm_desc* d) {
   const int64_t maxq = d->max_query_tokens;
   L.capP = (d->capacity_tokens + qwm::kTileKV - 1) / qwm::kTileKV * qwm::kTileKV;
   const int64_t big = 1 << 18;
-  int64_t pr = 2 * H * maxq > big ? 2 * H * maxq : big;
+  int64_t pr = 8 * H * maxq > big ? 8 * H * maxq : big;
   if (pr > 16 * H * maxq) pr = 16 * H * maxq;
   L.part_rows = pr;
   size_t off = 0;
@@ -118,6 +118,7 @@ struct qwm_cache {
   Layout L{};
   int H = 0, D = 0, nG = 0, m = 0, r = 0, dtype = 0, esz = 0;
   int device = 0;
+  int ncu = 256;  // compute units of the device
   hipStream_t stream = nullptr;
   uint8_t* arena = nullptr;
   qwm::CacheView view{};
@@ -317,6 +318,10 @@ qwm_status qwm_create(const qwm_desc* desc, void* dev_arena, size_t arena_bytes,
   c->dtype = desc->dtype;
   c->esz = desc->dtype == QWM_BF16 ? 2 : 4;
   c->device = dev;
+  if (dev >= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) c->ncu = n;
+  }
   c->stream = reinterpret_cast<hipStream_t>(stream);
   c->arena = reinterpret_cast<uint8_t*>(dev_arena);
   c->view.kcode = c->arena + L.kcode;
@@ -519,7 +524,7 @@ qwm_status qwm_attend(qwm_cache* c, const void* q, int64_t n_q, const void* k_se
     if (n_self != 0) return fail(QWM_ERR_INVALID_ARG, "n_self must be 0 with QWM_SELF_NONE");
   } else {
     if (n_self < 1) return fail(QWM_ERR_INVALID_ARG, "a self mask needs n_self >= 1");
-    if (n_self > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_CAPACITY, "n_self too large");
+    if (n_self > ((int64_t)1 << 22)) return fail(QWM_ERR_CAPACITY, "n_self beyond 2^22");
     if ((st = check_ptr(k_self, "k_self")) != QWM_OK) return st;
     if ((st = check_ptr(v_self, "v_self")) != QWM_OK) return st;
     if (mask == QWM_SELF_CAUSAL && n_self != n_q) return fail(QWM_ERR_INVALID_ARG, "causal self needs n_self == n_q");
@@ -544,12 +549,22 @@ qwm_status qwm_attend(qwm_cache* c, const void* q, int64_t n_q, const void* k_se
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.n_epoch_slots = E;
   a.out = out;
+  // Split the KV tiles so that the workgroups fill the device in as few
+  // rounds as possible: cost = rounds x (tiles per workgroup + 2 for its
+  // prologue and epilogue) + 2 for the merge pass when split; one 145 KB-LDS
+  // workgroup per CU for head_dim 128.
   const int64_t qtiles = (n_q + qwm::kTileQ - 1) / qwm::kTileQ;
-  int64_t splits = (1024 + qtiles * c->H - 1) / (qtiles * c->H);
-  if (splits > 16) splits = 16;
-  if (splits > T) splits = T;
-  while (splits > 1 && splits * c->H * n_q > c->L.part_rows) --splits;
-  if (splits < 1) splits = 1;
+  const int64_t slots = (int64_t)c->ncu * (c->D == 128 ? 1 : 2);
+  int64_t splits = 1, best = -1;
+  for (int64_t sp = 1; sp <= 16 && sp <= T; ++sp) {
+    if (sp > 1 && sp * c->H * n_q > c->L.part_rows) break;
+    const int64_t rounds = (qtiles * c->H * sp + slots - 1) / slots;
+    const int64_t cost = rounds * ((T + sp - 1) / sp + 2) + (sp > 1 ? 2 : 0);
+    if (best < 0 || cost < best) {
+      best = cost;
+      splits = sp;
+    }
+  }
   a.splits = (int)splits;
   hipError_t e = c->run(QWM_K_QU, [&] {
     return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
