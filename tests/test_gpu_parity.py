@@ -205,7 +205,8 @@ def test_determinism():
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
 
-@pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1024, 10), ("video_chunk", 4, 1760, 4)])
+@pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1024, 10), ("video_chunk", 4, 1760, 4),
+                                                     ("wm_layer", 2, 6000, 5)])
 def test_build_calibration(name, heads, n_keys, iters):
     """GPU-built calibration: S_G bit-exact (exact float64 sums of bf16/fp32
     squares), U_r spans the oracle's subspace (projector within 1e-4), and the

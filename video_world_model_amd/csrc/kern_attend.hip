@@ -12,16 +12,18 @@
 //  * one workgroup = 8 waves = 256 Queries of one head, one split of the KV
 //    sequence; the KV sequence is walked in 64-token tiles that never cross an
 //    epoch boundary or the cache/self boundary;
-//  * each tile is dequantized ONCE per workgroup into LDS (shared by the 8
-//    waves; waves 0-3 build khat, waves 4-7 build vhat^T): khat as float16 hi + lo pairs (hi = fp16(x), lo = fp16(x - hi),
-//    22 significant bits), the r PSAC coefficients next to them, and vhat^T
-//    as hi + lo;
+//  * each tile is dequantized ONCE per workgroup into one of two LDS stages
+//    (every thread: one 16-channel half group of one token's khat and a
+//    4-token x 4-channel block of vhat^T): khat as float16 hi + lo pairs
+//    (hi = fp16(x), lo = fp16(x - hi), 22 significant bits) with the r PSAC
+//    coefficients next to them, vhat^T as hi + lo; the packed words of the
+//    next tile are loaded into registers before the current tile's MFMA work;
 //  * logits come from v_mfma_f32_16x16x32_f16 with the contraction dimension
 //    [khat_hi | khat_lo | coef] x [q | q | qU_hi, qU_lo]: one MFMA chain per
 //    16x16 block computes q.khat and the PSAC term together;
-//  * online softmax in float32 with cross-lane max/sum over the 4 lane groups
-//    that share a Query (shuffles), P in fp16, o += vhat^T P^T by MFMA with
-//    vhat hi and lo.
+//  * online softmax in float32 with cross-lane max over the 4 lane groups
+//    that share a Query, P in fp16, o += vhat^T P^T by MFMA with vhat hi and
+//    lo, row sums of the same fp16 P by v_dot2_f32_f16.
 // The hi/lo splits keep logits within ~1e-6 and outputs within ~5e-4 (row
 // max relative) of float64.
 #include "qwm_dev.h"

@@ -436,6 +436,172 @@ __global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys
   }
 }
 
+// ---- pruned k-means assignment (iterations after the first)
+//
+// sqrt(J) is a seminorm of r = k - c: each group range R_G is one (it is
+// subadditive and absolutely homogeneous) and sqrt(sum_G S_G R_G^2) is a
+// weighted 2-norm of them. Hence, for a token x last assigned to centroid b,
+// N(x - c) >= N(c - b) - N(x - b), and every candidate with
+// N(c - b) > 2 N(x - b) has J(x, c) > J(x, b) strictly: it can neither win
+// nor tie. Tokens are grouped by their previous centroid, 64 to a wave; a
+// candidate is skipped by the whole wave when its distance to b exceeds
+// twice the largest N(x - b) of the wave, with a 1e-3 relative margin for the
+// float32 evaluation. All other candidates are scored exactly as in the full
+// assignment, so the ids are the same bits as an assignment over all
+// candidates.
+
+// Tokens grouped by centroid id: perm[h][off[c] .. off[c+1]) are the tokens of
+// centroid c (any order), woff[c] = sum over c' < c of ceil(count(c') / 64).
+__global__ __launch_bounds__(1024) void bucket_kernel(const uint8_t* ids, int64_t n, int m, int32_t* perm,
+                                                      int32_t* off, int32_t* woff) {
+  __shared__ int cnt[256], cur[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const uint8_t* idh = ids + (int64_t)h * n;
+  if (tid < 256) cnt[tid] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += 1024) atomicAdd(&cnt[idh[i]], 1);
+  __syncthreads();
+  if (tid < 64) {
+    // exclusive scans of the counts and of the per-centroid wave counts, 4
+    // centroids per lane
+    int c4[4], w4[4], cs = 0, ws = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 4 * tid + k;
+      c4[k] = (c < m) ? cnt[c] : 0;
+      w4[k] = (c4[k] + 63) / 64;
+      cs += c4[k];
+      ws += w4[k];
+    }
+    int ci = cs, wi = ws;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int yc = __shfl_up(ci, o), yw = __shfl_up(wi, o);
+      if (tid >= o) {
+        ci += yc;
+        wi += yw;
+      }
+    }
+    int co = ci - cs, wo = wi - ws;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 4 * tid + k;
+      if (c <= m) {
+        off[h * 257 + c] = co;
+        woff[h * 257 + c] = wo;
+      }
+      if (c < 256) cur[c] = co;
+      co += c4[k];
+      wo += w4[k];
+    }
+    if (tid == 63 && m == 256) {  // the end of the last centroid's range
+      off[h * 257 + 256] = co;
+      woff[h * 257 + 256] = wo;
+    }
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += 1024) {
+    const int p = atomicAdd(&cur[idh[i]], 1);
+    perm[(int64_t)h * n + p] = (int32_t)i;
+  }
+}
+
+// One block of 4 waves per (previous centroid b, chunk of 64 of its tokens):
+// every wave forms the same keep mask, takes every 4th kept candidate, and
+// the four (J, id) minima are combined lexicographically, which is the
+// argmin with ties to the smallest id. The candidate rows are wave-uniform
+// scalar loads, so nothing before them may look like a memory clobber: the
+// centroid distances N(C_c - C_b) are recomputed by every wave (one lane per
+// candidate) instead of being shared through LDS behind a barrier.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, int64_t n, int m, const float* C32,
+                                                            const float* S, const int32_t* perm, const int32_t* off,
+                                                            const int32_t* woff, uint8_t* ids_out) {
+  constexpr int NG = D / kGroup;
+  __shared__ float bj[4][64];
+  __shared__ int bi[4][64];
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = blockIdx.x;
+  const int32_t* wo = woff + h * 257;
+  const int32_t* of = off + h * 257;
+  if (w >= wo[m]) return;  // the whole block: no barrier is reached
+  // centroid b with wo[b] <= w < wo[b+1]
+  int lo = 0, hi = m - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (wo[mid] <= w)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int b = __builtin_amdgcn_readfirstlane(lo);
+  const int start = of[b] + 64 * (w - wo[b]);
+  const int cnt = (of[b + 1] - start) < 64 ? (of[b + 1] - start) : 64;
+  const float* __restrict__ Ch = C32 + (int64_t)h * m * D;
+  const float* __restrict__ Cb = Ch + (int64_t)b * D;
+  float SG[NG];
+#pragma unroll
+  for (int G = 0; G < NG; ++G) SG[G] = S[h * NG + G];
+
+  // N(C_c - C_b) for c = 64*round + lane
+  float ccd[4];
+#pragma unroll
+  for (int rd = 0; rd < 4; ++rd) {
+    ccd[rd] = 0.0f;
+    const int c = 64 * rd + lane;
+    if (64 * rd < m) {
+      float x[D];
+      load_row_span<D, 1>(Ch, (int64_t)(c < m ? c : 0) * D, x);
+      ccd[rd] = sqrtf(qsac_cost<D>(x, Cb, SG));
+    }
+  }
+
+  const int tok = perm[(int64_t)h * n + start + (lane < cnt ? lane : cnt - 1)];
+  float kf[D];
+  load_row_span<D, DT>(keys, ((int64_t)h * n + tok) * D, kf);
+  const float Jb = qsac_cost<D>(kf, Cb, SG);
+  float d = (lane < cnt) ? sqrtf(Jb) : 0.0f;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) d = fmaxf(d, __shfl_xor(d, o));
+  const float bound = 2.0f * d * 1.001f;
+
+  float bestJ = (wave == 0) ? Jb : __builtin_inff();
+  int best = (wave == 0) ? b : 0x7fffffff;
+  int rank = 0;  // position in the kept list, to deal the candidates to the waves
+#pragma unroll
+  for (int rd = 0; rd < 4; ++rd) {
+    if (64 * rd >= m) break;
+    const int cl = 64 * rd + lane;
+    uint64_t keep = __ballot(cl < m && cl != b && !(ccd[rd] > bound));
+    while (keep) {
+      const int c = 64 * rd + __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(keep));
+      keep &= keep - 1;
+      if ((rank++ & 3) != wave) continue;
+      const float J = qsac_cost<D>(kf, Ch + (int64_t)c * D, SG);
+      if (J < bestJ || (J == bestJ && c < best)) {
+        bestJ = J;
+        best = c;
+      }
+    }
+  }
+  bj[wave][lane] = bestJ;
+  bi[wave][lane] = best;
+  __syncthreads();
+  if (tid < cnt) {
+    float J = bj[0][tid];
+    int id = bi[0][tid];
+#pragma unroll
+    for (int v = 1; v < 4; ++v)
+      if (bj[v][tid] < J || (bj[v][tid] == J && bi[v][tid] < id)) {
+        J = bj[v][tid];
+        id = bi[v][tid];
+      }
+    const int t2 = perm[(int64_t)h * n + start + tid];
+    ids_out[(int64_t)h * n + t2] = (uint8_t)id;
+  }
+}
+
 template <int DT>
 __global__ void shadow_kernel(const void* C, const float* U, int64_t nC, int64_t nU, float* C32, double* U64) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -479,6 +645,30 @@ hipError_t launch_kmeans_seed(int D, int dtype, const void* keys, int64_t n, int
   else
     hipLaunchKernelGGL((D == 128 ? seed_kernel<128, 1> : seed_kernel<64, 1>), grid, block, 0, s, keys, n, m, C,
                        C32);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_bucket(const uint8_t* ids, int64_t n, int H, int m, int32_t* perm, int32_t* off,
+                                int32_t* woff, hipStream_t s) {
+  hipLaunchKernelGGL(bucket_kernel, dim3((unsigned)H), dim3(1024), 0, s, ids, n, m, perm, off, woff);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_assign_pruned(int D, int dtype, const void* keys, int64_t n, int H, int m, const float* C32,
+                                       const float* S, const int32_t* perm, const int32_t* off, const int32_t* woff,
+                                       uint8_t* ids_out, hipStream_t s) {
+  dim3 grid((unsigned)((n + 63) / 64 + m), (unsigned)H), block(256);
+#define QWM_PLAUNCH(DD, TT) \
+  hipLaunchKernelGGL((assign_pruned_kernel<DD, TT>), grid, block, 0, s, keys, n, m, C32, S, perm, off, woff, ids_out)
+  if (D == 128 && dtype == 0)
+    QWM_PLAUNCH(128, 0);
+  else if (D == 128)
+    QWM_PLAUNCH(128, 1);
+  else if (dtype == 0)
+    QWM_PLAUNCH(64, 0);
+  else
+    QWM_PLAUNCH(64, 1);
+#undef QWM_PLAUNCH
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Layout {
   size_t kcode, vcode, kparam, vparam, ids, coef;
-  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, build_ids, qU, part_o, part_ml;
+  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, build_ids, km_perm, km_off, km_woff, qU, part_o, part_ml;
   size_t total;
   int64_t capP, part_rows;
 };
@@ -87,6 +87,9 @@ Layout make_layout(const qwm_desc* d) {
   L.U64 = take((size_t)(H * D * r * 8));
   L.gram = take((size_t)(H * qwm::kGramMaxChunks * D * D * 8));
   L.build_ids = take((size_t)(H * d->max_build_tokens));
+  L.km_perm = take((size_t)(H * d->max_build_tokens * 4));
+  L.km_off = take((size_t)(H * 257 * 4));
+  L.km_woff = take((size_t)(H * 257 * 4));
   L.qU = take((size_t)(H * E * maxq * qwm::kRankPad * 4));
   L.part_o = take((size_t)(pr * D * 4));
   L.part_ml = take((size_t)(pr * 2 * 4));
@@ -152,6 +155,9 @@ struct qwm_cache {
   double* U64() const { return reinterpret_cast<double*>(arena + L.U64); }
   double* gram() const { return reinterpret_cast<double*>(arena + L.gram); }
   uint8_t* build_ids() const { return arena + L.build_ids; }
+  int32_t* km_perm() const { return reinterpret_cast<int32_t*>(arena + L.km_perm); }
+  int32_t* km_off() const { return reinterpret_cast<int32_t*>(arena + L.km_off); }
+  int32_t* km_woff() const { return reinterpret_cast<int32_t*>(arena + L.km_woff); }
   float* qU() const { return reinterpret_cast<float*>(arena + L.qU); }
   float* part_o() const { return reinterpret_cast<float*>(arena + L.part_o); }
   float* part_ml() const { return reinterpret_cast<float*>(arena + L.part_ml); }
@@ -411,18 +417,33 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
   });
   if (e != hipSuccess) return fail_hip(e, "kmeans seed");
   for (int it = 0; it < iters; ++it) {
-    qwm::QuantArgs a{};
-    a.k = keys;
-    a.v = nullptr;
-    a.n = n_keys;
-    a.C32 = c->kmC32();
-    a.S = c->slotS(stg);
-    a.ids_out = c->build_ids();
-    a.H = c->H;
-    a.m = c->m;
-    a.r = c->r;
-    e = c->run(QWM_K_ASSIGN, [&] { return qwm::launch_quantize(c->D, c->dtype, a, c->stream); });
-    if (e != hipSuccess) return fail_hip(e, "kmeans assign");
+    // Pruning pays for its grouping pass only with many centroids: below 128
+    // about half the candidates survive and the full pass is as fast.
+    if (it == 0 || c->m < 128) {  // every candidate for every Key
+      qwm::QuantArgs a{};
+      a.k = keys;
+      a.v = nullptr;
+      a.n = n_keys;
+      a.C32 = c->kmC32();
+      a.S = c->slotS(stg);
+      a.ids_out = c->build_ids();
+      a.H = c->H;
+      a.m = c->m;
+      a.r = c->r;
+      e = c->run(QWM_K_ASSIGN, [&] { return qwm::launch_quantize(c->D, c->dtype, a, c->stream); });
+      if (e != hipSuccess) return fail_hip(e, "kmeans assign");
+    } else {  // the same ids, skipping candidates the triangle inequality rules out
+      e = c->run(QWM_K_OTHER, [&] {
+        return qwm::launch_kmeans_bucket(c->build_ids(), n_keys, c->H, c->m, c->km_perm(), c->km_off(), c->km_woff(),
+                                         c->stream);
+      });
+      if (e != hipSuccess) return fail_hip(e, "kmeans bucket");
+      e = c->run(QWM_K_ASSIGN, [&] {
+        return qwm::launch_kmeans_assign_pruned(c->D, c->dtype, keys, n_keys, c->H, c->m, c->kmC32(), c->slotS(stg),
+                                                c->km_perm(), c->km_off(), c->km_woff(), c->build_ids(), c->stream);
+      });
+      if (e != hipSuccess) return fail_hip(e, "kmeans assign");
+    }
     e = c->run(QWM_K_UPDATE, [&] {
       return qwm::launch_kmeans_update(c->D, c->dtype, keys, c->build_ids(), n_keys, c->H, c->m, c->slotC(stg),
                                        c->kmC32(), c->stream);

@@ -56,6 +56,14 @@ hipError_t launch_kmeans_seed(int D, int dtype, const void* keys, int64_t n, int
                               void* C, float* C32, hipStream_t s);
 hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_t* ids, int64_t n,
                                 int H, int m, void* C, float* C32, hipStream_t s);
+// Pruned assignment for k-means iterations after the first: tokens grouped
+// by their previous id (perm [H][n], off/woff [H][257]), then the assignment
+// skipping candidates that provably lose.
+hipError_t launch_kmeans_bucket(const uint8_t* ids, int64_t n, int H, int m, int32_t* perm, int32_t* off,
+                                int32_t* woff, hipStream_t s);
+hipError_t launch_kmeans_assign_pruned(int D, int dtype, const void* keys, int64_t n, int H, int m, const float* C32,
+                                       const float* S, const int32_t* perm, const int32_t* off, const int32_t* woff,
+                                       uint8_t* ids_out, hipStream_t s);
 // Float (and float64 U) shadows of a committed epoch, used by quantize.
 hipError_t launch_shadow(int D, int dtype, const void* C, const float* U, int H, int m, int r,
                          float* C32, double* U64, hipStream_t s);
