@@ -85,7 +85,7 @@ typedef struct {
   int32_t dtype;            /* qwm_dtype of K/V/Q inputs and of the centroid table */
   int32_t reserved;         /* must be 0 */
   int64_t max_query_tokens; /* largest n_q of qwm_attend (sizes split-KV scratch) */
-  int64_t max_build_tokens; /* largest n_keys of qwm_build_centroids */
+  int64_t max_build_tokens; /* largest n_keys of qwm_build_centroids, 1 .. 2^22 */
 } qwm_desc;
 
 /* Bytes of device arena a cache with this description needs (alignment 256). */

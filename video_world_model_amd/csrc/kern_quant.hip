@@ -353,6 +353,9 @@ __global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys
   const int c = blockIdx.x, h = blockIdx.y;
   const uint8_t* idh = ids + (int64_t)h * n;
   uint16_t* lst = list[wave];
+  // per-head Key base (uniform); row offsets fit 32 bits (n <= 2^22)
+  const uint16_t* kh16 = reinterpret_cast<const uint16_t*>(keys) + (size_t)h * n * D;
+  const float* kh32 = reinterpret_cast<const float*>(keys) + (size_t)h * n * D;
 
   const int64_t span = ((n + kUpdWaves - 1) / kUpdWaves + 63) / 64 * 64;
   const int per_lane = (int)(span / 64 < kUpdLane ? span / 64 : kUpdLane);
@@ -387,14 +390,30 @@ __global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // member rows 8 at a time (one 32- or 64-bit load per row and lane)
     for (int u0 = 0; u0 < total; u0 += 8) {
       float x[8][PER];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int uu = (u0 + u < total) ? u0 + u : u0;
-        const int64_t row = ((int64_t)h * n + base + lst[uu]) * D;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) x[u][k] = load_in<DT>(keys, row + PER * lane + k);
+        const int uu = (u0 + u < total) ? u0 + u : total - 1;
+        const uint32_t row = (uint32_t)(base + lst[uu]) * (uint32_t)D + PER * lane;
+        if constexpr (DT == 0) {
+          if constexpr (PER == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(kh16 + row);
+            x[u][0] = __uint_as_float(w << 16);
+            x[u][1] = __uint_as_float(w & 0xFFFF0000u);
+          } else {
+            x[u][0] = __uint_as_float((uint32_t)kh16[row] << 16);
+          }
+        } else {
+          if constexpr (PER == 2) {
+            const float2 w = *reinterpret_cast<const float2*>(kh32 + row);
+            x[u][0] = w.x;
+            x[u][1] = w.y;
+          } else {
+            x[u][0] = kh32[row];
+          }
+        }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)

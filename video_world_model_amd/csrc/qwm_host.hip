@@ -53,7 +53,7 @@ qwm_status check_desc(const qwm_desc* d) {
   if (d->capacity_tokens > ((int64_t)1 << 26))
     return fail(QWM_ERR_UNSUPPORTED, "capacity_tokens beyond 2^26 per head");
   if (d->max_query_tokens > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_UNSUPPORTED, "max_query_tokens too large");
-  if (d->max_build_tokens > (int64_t)INT32_MAX / 2) return fail(QWM_ERR_UNSUPPORTED, "max_build_tokens too large");
+  if (d->max_build_tokens > ((int64_t)1 << 22)) return fail(QWM_ERR_UNSUPPORTED, "max_build_tokens beyond 2^22");
   return QWM_OK;
 }
 
