@@ -216,11 +216,68 @@ def qsac_assign(k: np.ndarray, C: np.ndarray, S: np.ndarray, g: int, chunk: int 
 
 
 def nearest_assign(k: np.ndarray, C: np.ndarray) -> np.ndarray:
-    """Euclidean-nearest centroid (the QVG baseline's rule), float64."""
+    """Euclidean-nearest centroid in float64 (used to pin the float32 rule below)."""
     k = np.asarray(k, dtype=F64)
     C = np.asarray(C, dtype=F64)
     d2 = ((k[:, None, :] - C[None, :, :]) ** 2).sum(axis=2)
     return np.argmin(d2, axis=1)
+
+
+def nearest_objective(k: np.ndarray, C: np.ndarray, g: int) -> np.ndarray:
+    """Squared Euclidean distance D[n, c] of Key n to centroid c (float32 [N][m]).
+
+    The baseline the article compares against (QVG, "Step 1") gives each Key
+    its nearest high-precision centroid. The pages fix no arithmetic for it;
+    the reading taken mirrors the QSAC objective's structure so that the same
+    kernels can evaluate either: r = k - c in float32; per group G a running
+    sum p_G = t_0 + t_1 + ... + t_{g-1} of t_j = r_j * r_j taken channel by
+    channel in ascending order (no fused multiply-add); then
+    D = ((p_0 + p_1) + p_2) + ... left to right.
+    """
+    k = np.asarray(k, dtype=F32)
+    C = np.asarray(C, dtype=F32)
+    N, d = k.shape
+    nG = d // g
+    D = None
+    for G in range(nG):
+        p = None
+        for j in range(G * g, (G + 1) * g):
+            r = k[:, None, j] - C[None, :, j]
+            t = r * r
+            p = t if p is None else p + t
+        D = p if D is None else D + p
+    assert D is not None and D.shape == (N, C.shape[0])
+    return D
+
+
+def nearest_assign32(k: np.ndarray, C: np.ndarray, g: int, chunk: int = 2048) -> np.ndarray:
+    """QVG's rule: argmin_c of ``nearest_objective``, ties to the smallest id."""
+    k = np.asarray(k, dtype=F32)
+    out = np.empty(k.shape[0], np.int64)
+    for a in range(0, k.shape[0], chunk):
+        out[a:a + chunk] = np.argmin(nearest_objective(k[a:a + chunk], C, g), axis=1)
+    return out
+
+
+OBJECTIVES = ("qsac", "nearest")
+
+
+def objective_values(k, C, S, g: int, objective: str) -> np.ndarray:
+    """Assignment cost matrix of the chosen rule (float32 [N][m])."""
+    if objective == "qsac":
+        return qsac_objective(k, C, S, g)
+    if objective == "nearest":
+        return nearest_objective(k, C, g)
+    raise ValueError(objective)
+
+
+def assign(k, C, S, g: int, objective: str = "qsac") -> np.ndarray:
+    """Centroid id per Key under the chosen rule (QSAC, or QVG's nearest centroid)."""
+    if objective == "qsac":
+        return qsac_assign(k, C, S, g)
+    if objective == "nearest":
+        return nearest_assign32(k, C, g)
+    raise ValueError(objective)
 
 
 # ---------------------------------------------------------------------------
@@ -303,17 +360,20 @@ def psac_coef(k, c, rhat, U) -> np.ndarray:
 # O2-O8 -- quantize-on-insert of a block of tokens (one head)
 # ---------------------------------------------------------------------------
 
-def quantize_tokens(k, v, C, S, U, g: int) -> dict:
+def quantize_tokens(k, v, C, S, U, g: int, objective: str = "qsac") -> dict:
     """Everything the cache stores for each token of one head, given one epoch's
     calibration (centroids C [m][d], sensitivity S [nG], basis U [d][r]).
 
-    Each token's record depends only on the token and the calibration, so
-    appending in one call or frame by frame gives the same bits.
+    ``objective`` picks the centroid rule ("qsac", or "nearest" for the QVG
+    baseline). A basis with r = 0 columns turns PSAC off: no coefficients are
+    stored. Each token's record depends only on the token and the
+    calibration, so appending in one call or frame by frame gives the same
+    bits.
     """
     k = np.asarray(k, dtype=F32)
     v = np.asarray(v, dtype=F32)
     C = np.asarray(C, dtype=F32)
-    ids = qsac_assign(k, C, S, g)
+    ids = assign(k, C, S, g, objective)
     c = C[ids]
     r = k - c
     kcode, kzp, ksc = int2_quantize(r, g)
@@ -336,7 +396,7 @@ def init_centroids(keys: np.ndarray, m: int) -> np.ndarray:
     return keys[idx].copy()
 
 
-def build_centroids(keys, S, m: int, g: int, iters: int, dtype: str) -> np.ndarray:
+def build_centroids(keys, S, m: int, g: int, iters: int, dtype: str, objective: str = "qsac") -> np.ndarray:
     """Centroid table C [m][d] (float32 values in the stored dtype).
 
     The article clusters the Keys around high-precision centers ("Step 1";
@@ -346,12 +406,13 @@ def build_centroids(keys, S, m: int, g: int, iters: int, dtype: str) -> np.ndarr
     ``init_centroids``, then ``iters`` times assign every Key by
     ``qsac_assign`` and replace each centroid by the float64 mean of its
     Keys rounded once to the stored dtype; a centroid with no Keys keeps its
-    value.
+    value. With objective "nearest" (the QVG baseline) the assignment is the
+    nearest centroid instead and everything else is the same.
     """
     keys = np.asarray(keys, dtype=F32)
     C = init_centroids(keys, m)
     for _ in range(iters):
-        ids = qsac_assign(keys, C, S, g)
+        ids = assign(keys, C, S, g, objective)
         for i in range(m):
             sel = keys[ids == i]
             if sel.shape[0]:
@@ -360,12 +421,12 @@ def build_centroids(keys, S, m: int, g: int, iters: int, dtype: str) -> np.ndarr
     return C
 
 
-def mean_objective(keys, C, S, g) -> float:
-    """Mean over Keys of min_c J (float64 of the float32 values)."""
+def mean_objective(keys, C, S, g, objective: str = "qsac") -> float:
+    """Mean over Keys of the smallest assignment cost (float64 of the float32 values)."""
     keys = np.asarray(keys, dtype=F32)
     tot = 0.0
     for a in range(0, keys.shape[0], 2048):
-        J = qsac_objective(keys[a:a + 2048], C, S, g)
+        J = objective_values(keys[a:a + 2048], C, S, g, objective)
         tot += float(J.min(axis=1).astype(F64).sum())
     return tot / keys.shape[0]
 
@@ -421,9 +482,10 @@ class HeadCache:
     """One head's cache as the oracle sees it: per-token records plus the
     calibration of every epoch and the token at which each epoch starts."""
 
-    def __init__(self, g: int, dtype: str):
+    def __init__(self, g: int, dtype: str, objective: str = "qsac"):
         self.g = g
         self.dtype = dtype
+        self.objective = objective
         self.records = []  # list of (start, record dict)
         self.epochs = []  # list of (start, C, S, U)
         self.length = 0
@@ -437,7 +499,7 @@ class HeadCache:
         if not self.epochs:
             raise RuntimeError("no committed epoch")
         _, C, S, U = self.epochs[-1]
-        rec = quantize_tokens(k, v, C, S, U, self.g)
+        rec = quantize_tokens(k, v, C, S, U, self.g, self.objective)
         rec["epoch"] = np.full(len(rec["ids"]), len(self.epochs) - 1, np.int64)
         self.records.append((self.length, rec))
         self.length += len(rec["ids"])
@@ -512,3 +574,26 @@ def attend(q, cache: HeadCache, k_self=None, v_self=None, mask: str = "none",
     p = np.exp(ell - mrow)
     p /= p.sum(axis=1, keepdims=True)
     return p @ vv
+
+
+# ---------------------------------------------------------------------------
+# Table 1 diagnostic -- top-scoring historical token
+# ---------------------------------------------------------------------------
+
+def top1_cached(q, cache: HeadCache) -> np.ndarray:
+    """Per Query, the cached token with the largest compensated logit
+    q . khat_j + (q U^(e(j))) . coef_j (float64; the first index on a tie)."""
+    return np.argmax(cache_logits(q, cache, 1.0), axis=1)
+
+
+def top1_dense(q, k) -> np.ndarray:
+    """Per Query, the token with the largest full-precision logit q . k_j
+    (float64; the first index on a tie)."""
+    return np.argmax(np.asarray(q, F64) @ np.asarray(k, F64).T, axis=1)
+
+
+def top1_change_rate(q, k_full, cache: HeadCache) -> float:
+    """The article's attention analysis ("Table 1"): how often the top-scoring
+    historical token of a Query differs between the quantized cache and full
+    precision, as a fraction of Queries."""
+    return float(np.mean(top1_cached(q, cache) != top1_dense(q, k_full)))
