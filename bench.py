@@ -12,6 +12,14 @@ One step is one pass of the whole path over one chunk of synthetic input:
 The default workload is the "small video chunk": 12 heads, head_dim 128,
 8 frames x 880 tokens cached, 64 centroids, rank 8, one 880-Query frame.
 
+--mode picks the method: "quantwm" (QSAC + PSAC, the default), "qvg" (the
+baseline of the article's "Step 1": nearest centroid, no compensation, no
+historical Queries, so step 1 is skipped), or the two ablations "qsac"
+(PSAC off) and "nearest-psac". After the timed steps the run also reports
+the top-1 change rate of the article's "Table 1" analysis: the share of
+(head, Query) pairs whose top-scoring cached token differs from the one
+full-precision Keys give.
+
 Prints ONE JSON line. `value` = cache token-heads attended per second of
 whole-step time (H * N_kv / t_step). Per-kernel times come from HIP events
 the library records around each launch on its stream during the timed
@@ -46,6 +54,16 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # arithmetic peak is 1.5 x 39.32 = 58.98 T ops/s.
 VALU_LANE_INSTR_PER_S = 256 * 4 * 16 * 2.4e9
 QSAC_OPS_PEAK = 1.5 * VALU_LANE_INSTR_PER_S
+# The nearest-centroid cost retires its 3 ops per channel (sub, mul, add) as
+# 3 lane-instructions.
+NEAREST_OPS_PEAK = VALU_LANE_INSTR_PER_S
+
+MODES = {  # objective, PSAC on
+    "quantwm": ("qsac", True),
+    "qvg": ("nearest", False),
+    "qsac": ("qsac", False),
+    "nearest-psac": ("nearest", True),
+}
 
 KERNELS = ["quantize", "attend", "merge", "qu", "gram", "eigen", "assign", "update", "other"]
 KERNEL_SOURCES = {
@@ -65,9 +83,9 @@ def bytes_per_token_head(d, g, r):
     return 2 * (d // 4) + 2 * (d // g) * 4 + 1 + 2 * r
 
 
-def models(w: W.Workload):
-    """Algorithmic work per launch of each kernel class."""
-    H, d, g, m, r = w.heads, w.head_dim, w.group, w.n_centroids, w.rank
+def models(w: W.Workload, r: int):
+    """Algorithmic work per launch of each kernel class (PSAC rank r)."""
+    H, d, g, m = w.heads, w.head_dim, w.group, w.n_centroids
     N, Nq, Ns, M = w.n_kv, w.n_q, w.n_self, w.n_hist
     esz = 2 if w.dtype == "bf16" else 4
     B = bytes_per_token_head(d, g, r)
@@ -83,7 +101,7 @@ def models(w: W.Workload):
 # ----------------------------------------------------------------- CPU oracle
 
 def _oracle_head(args):
-    name, head = args
+    name, head, objective, r = args
     from threadpoolctl import threadpool_limits
 
     import oracle.qwm_oracle as O
@@ -96,17 +114,20 @@ def _oracle_head(args):
         ks, vs = hg.self_keys(), hg.self_values()
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        S = O.sensitivity(qh, w.group)
-        U = O.subspace(qh, w.rank)
-        C = O.build_centroids(keys, S, w.n_centroids, w.group, w.kmeans_iters, w.dtype)
-        hc = O.HeadCache(w.group, w.dtype)
+        if objective == "qsac" or r > 0:
+            S = O.sensitivity(qh, w.group)
+        else:
+            S = np.zeros(w.head_dim // w.group, np.float32)
+        U = O.subspace(qh, r)
+        C = O.build_centroids(keys, S, w.n_centroids, w.group, w.kmeans_iters, w.dtype, objective=objective)
+        hc = O.HeadCache(w.group, w.dtype, objective)
         hc.add_epoch(C, S, U)
         hc.append(keys, vals)
         O.attend(q, hc, ks, vs, mask=w.self_mask)
         return time.perf_counter() - t0
 
 
-def cpu_baseline(w: W.Workload, n_heads: int):
+def cpu_baseline(w: W.Workload, n_heads: int, objective: str, r: int):
     """The oracle's full step on `n_heads` heads, one forked worker per head
     (run before the GPU is initialized), scaled to cache tokens/s."""
     import multiprocessing as mp
@@ -114,7 +135,7 @@ def cpu_baseline(w: W.Workload, n_heads: int):
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(n_heads) as pool:
-        times = pool.map(_oracle_head, [(w.name, h) for h in range(n_heads)])
+        times = pool.map(_oracle_head, [(w.name, h, objective, r) for h in range(n_heads)])
     wall = time.perf_counter() - t0
     busy = max(times)
     return {
@@ -122,7 +143,8 @@ def cpu_baseline(w: W.Workload, n_heads: int):
         "unit": "KV tokens/s",
         "cores": n_heads,
         "kind": "oracle",
-        "sample": (f"one full {w.name} step (subspace, {w.kmeans_iters}-iteration centroid build, quantize of "
+        "sample": (f"one full {w.name} step ({objective} rule, rank {r}: subspace, {w.kmeans_iters}-iteration "
+                   f"centroid build, quantize of "
                    f"{w.n_kv} tokens, attention of {w.n_q} Queries) on {n_heads} of {w.heads} heads, one forked "
                    f"process per head, BLAS 1 thread; slowest head {busy:.2f} s, pool wall {wall:.2f} s"),
         "host_cpus": len(os.sched_getaffinity(0)),
@@ -138,6 +160,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_chunk", choices=["tiny", "video_chunk", "wm_layer"])
+    ap.add_argument("--mode", default="quantwm", choices=sorted(MODES))
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's timed sample (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg) over this many MiB first, as a known-size "
@@ -149,7 +172,10 @@ def main():
         sys.exit(2)
 
     w = W.workload(args.workload)
-    cpu = cpu_baseline(w, args.cpu_heads) if args.cpu_heads > 0 else None
+    objective, psac = MODES[args.mode]
+    r = w.rank if psac else 0
+    needs_queries = psac or objective == "qsac"  # QVG uses no historical Queries
+    cpu = cpu_baseline(w, args.cpu_heads, objective, r) if args.cpu_heads > 0 else None
 
     import torch
     from video_world_model_amd import Cache
@@ -177,14 +203,15 @@ def main():
     if w.n_self:
         ks = dev([g.self_keys() for g in gens])
         vs = dev([g.self_values() for g in gens])
-    cache = Cache(w.heads, w.head_dim, w.n_centroids, w.rank, w.n_kv,
+    cache = Cache(w.heads, w.head_dim, w.n_centroids, r, w.n_kv,
                   dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
-                  max_query_tokens=w.n_q, max_build_tokens=w.n_kv)
+                  max_query_tokens=w.n_q, max_build_tokens=w.n_kv, objective=objective)
     out = torch.empty((w.heads, w.n_q, w.head_dim), dtype=torch.float32, device="cuda")
 
     def step():
         cache.truncate(0)
-        cache.build_subspace(qh)
+        if needs_queries:
+            cache.build_subspace(qh)
         cache.build_centroids(keys, w.kmeans_iters)
         cache.quantize_append(keys, vals)
         cache.attend(q, ks, vs, mask=w.self_mask, out=out)
@@ -209,14 +236,19 @@ def main():
         if n:
             kern[k] = dict(ms_per_step=ms / args.steps, launches_per_step=n / args.steps, avg_launch_ms=ms / n)
     cache.profile_enable(False)
+    # the article's "Table 1" diagnostic, outside the timed region
+    top_cache = cache.attend_top1(q)
+    top_full = cache.attend_top1(q, keys)
+    top1_rate = float((top_cache != top_full).float().mean().item())
 
-    mdl = models(w)
+    ops_peak = QSAC_OPS_PEAK if objective == "qsac" else NEAREST_OPS_PEAK
+    mdl = models(w, r)
     dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
     avg_s = kern[dom]["avg_launch_ms"] * 1e-3
     if dom in ("quantize", "assign"):
         achieved = mdl[dom]["ops"] / avg_s / 1e12
-        roof = dict(bound="alu", achieved=achieved, peak=QSAC_OPS_PEAK / 1e12, unit="Top/s",
-                    frac=achieved * 1e12 / QSAC_OPS_PEAK)
+        roof = dict(bound="alu", achieved=achieved, peak=ops_peak / 1e12, unit="Top/s",
+                    frac=achieved * 1e12 / ops_peak)
     elif dom == "attend":
         achieved = mdl[dom]["flops"] / avg_s / 1e12
         roof = dict(bound="mfma", achieved=achieved, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
@@ -225,7 +257,8 @@ def main():
         roof = dict(bound="alu", achieved=None, peak=None, unit=None, frac=None)
     roof["kernel"] = dom
     roof["traffic"] = None
-    pmc_path = os.path.join(ROOT, "profiles", f"{dom}_{w.name}_pmc.json")
+    suffix = "" if args.mode == "quantwm" else f"_{args.mode}"
+    pmc_path = os.path.join(ROOT, "profiles", f"{dom}_{w.name}{suffix}_pmc.json")
     if os.path.exists(pmc_path):
         with open(pmc_path) as f:
             pmc = json.load(f)
@@ -237,7 +270,7 @@ def main():
         t = kern["quantize"]["avg_launch_ms"] * 1e-3
         gbps = mdl["quantize"]["bytes"] / t / 1e9
         extras["quantize"] = dict(GBps=gbps, hbm_frac=gbps / HBM_PEAK_GBPS,
-                                  alu_frac=mdl["quantize"]["ops"] / t / QSAC_OPS_PEAK, ms=t * 1e3)
+                                  alu_frac=mdl["quantize"]["ops"] / t / ops_peak, ms=t * 1e3)
     if "attend" in kern:
         t = sum(kern[k]["ms_per_step"] for k in ("qu", "attend", "merge") if k in kern) * 1e-3
         ta = kern["attend"]["avg_launch_ms"] * 1e-3
@@ -261,14 +294,16 @@ def main():
         "vs_baseline": None,
         "dtype": "f32-valu+f16-mfma",
         "data": "synthetic",
-        "config": {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim, "group": w.group,
-                   "n_centroids": w.n_centroids, "rank": w.rank, "n_kv": w.n_kv, "n_q": w.n_q,
+        "config": {"workload": w.name, "mode": args.mode, "objective": objective, "heads": w.heads,
+                   "head_dim": w.head_dim, "group": w.group,
+                   "n_centroids": w.n_centroids, "rank": r, "n_kv": w.n_kv, "n_q": w.n_q,
                    "n_self": w.n_self, "n_hist": w.n_hist, "kmeans_iters": w.kmeans_iters,
                    "input_dtype": w.dtype, "query_alpha": W.QUERY_ALPHA},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kern,
         "phases": extras,
+        "diagnostics": {"top1_change_rate": top1_rate},
     }
     print(json.dumps(rec), flush=True)
 

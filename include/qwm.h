@@ -13,6 +13,13 @@
  *     error left after quantization is projected on the top-r principal
  *     directions of historical Queries, r coefficients per token are kept,
  *     and (q . U_r) . coef is added back to every attention logit.
+ * Two switches give the baseline the article ("Step 1") compares against,
+ * QVG, and the ablations between: the centroid rule (QSAC objective or the
+ * nearest centroid) and the PSAC rank (0 turns compensation off). The
+ * article's attention analysis ("Table 1") counts how often a Query's
+ * top-scoring historical token changes under quantization;
+ * qwm_attend_top1 computes that token for the cache and for full-precision
+ * Keys.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -58,7 +65,7 @@ typedef enum {
   QWM_OK = 0,
   QWM_ERR_INVALID_ARG = -1,    /* null pointer, negative size, bad enum value */
   QWM_ERR_UNSUPPORTED = -2,    /* head_dim not 64/128, group not 32, n_centroids not 1..256,
-                                  rank not 1..16, max_epochs not 1..64 */
+                                  rank not 0..16, max_epochs not 1..64 */
   QWM_ERR_CAPACITY = -3,       /* length + n > capacity, n beyond a max_* bound, too many epochs */
   QWM_ERR_STATE = -4,          /* append/attend before a committed epoch; build_centroids
                                   before build_subspace */
@@ -74,16 +81,23 @@ typedef enum {
   QWM_SELF_CAUSAL = 2  /* Query i sees self tokens 0..i (requires n_self == n_q) */
 } qwm_self_mask;
 
+/* Centroid rule of quantize-on-insert and of the centroid build. */
+typedef enum {
+  QWM_OBJ_QSAC = 0,    /* QSAC: sum_G S_G (max_G r - min_G r)^2 (roboind.com "Step 1") */
+  QWM_OBJ_NEAREST = 1  /* QVG baseline: nearest centroid, sum_j r_j^2 per group in
+                          channel order, groups added in order (float32) */
+} qwm_objective;
+
 typedef struct {
   int32_t heads;            /* >= 1 */
   int32_t head_dim;         /* 64 or 128 */
   int32_t group;            /* channels per INT2 group: 32 */
   int32_t n_centroids;      /* 1..256 (ids are stored as u8) */
-  int32_t rank;             /* PSAC rank r: 1..16 */
+  int32_t rank;             /* PSAC rank r: 0..16 (0: no compensation, no coefficients) */
   int32_t max_epochs;       /* calibration epochs kept: 1..64 */
   int64_t capacity_tokens;  /* tokens per head the cache can hold, 1 .. 2^26 */
   int32_t dtype;            /* qwm_dtype of K/V/Q inputs and of the centroid table */
-  int32_t reserved;         /* must be 0 */
+  int32_t objective;        /* qwm_objective */
   int64_t max_query_tokens; /* largest n_q of qwm_attend (sizes split-KV scratch) */
   int64_t max_build_tokens; /* largest n_keys of qwm_build_centroids, 1 .. 2^22 */
 } qwm_desc;
@@ -110,28 +124,33 @@ qwm_status qwm_destroy(qwm_cache* cache);
  * factorization), largest-magnitude entry of each column positive. The
  * result goes to a staged epoch that qwm_build_centroids commits. S_G is
  * ready on the cache stream when the call returns; U_r is computed on the
- * library's eigensolve stream (see above). 1 <= n_hist. */
+ * library's eigensolve stream (see above); at rank 0 there is no U_r and
+ * nothing runs there. 1 <= n_hist. */
 qwm_status qwm_build_subspace(qwm_cache* cache, const void* q_hist, int64_t n_hist);
 
 /* QSAC centroid table from n_keys Keys [heads][n_keys][head_dim]
  * (roboind.com "Step 1": Keys are grouped around high-precision centers):
  * seeds c_i = key floor(i * n_keys / n_centroids), then `iters` Lloyd
- * iterations that assign by the QSAC objective of the staged sensitivity and
- * replace each centroid by the float64 mean of its Keys rounded once to the
- * cache dtype (an empty cluster keeps its centroid). Commits the staged epoch:
- * tokens appended from now on use it. An epoch that holds no token yet is
- * replaced rather than kept. 1 <= n_keys <= max_build_tokens, 0 <= iters. */
+ * iterations that assign by the cache's centroid rule (the QSAC objective of
+ * the staged sensitivity, or the nearest centroid) and replace each centroid
+ * by the float64 mean of its Keys rounded once to the cache dtype (an empty
+ * cluster keeps its centroid). Commits the staged epoch: tokens appended from
+ * now on use it. An epoch that holds no token yet is replaced rather than
+ * kept. Needs a staged qwm_build_subspace, except with QWM_OBJ_NEAREST at
+ * rank 0, where the epoch's S_G is then zero.
+ * 1 <= n_keys <= max_build_tokens, 0 <= iters. */
 qwm_status qwm_build_centroids(qwm_cache* cache, const void* keys, int64_t n_keys, int32_t iters);
 
 /* Quantize-on-insert of n_tokens new tokens k, v [heads][n_tokens][head_dim]
  * with the current epoch. Per token and head:
  *   id = argmin_c sum_G S_G (max_G(k - c) - min_G(k - c))^2 in float32, ties
- *        to the smallest id (QSAC, roboind.com "Step 1");
+ *        to the smallest id (QSAC, roboind.com "Step 1"), or with
+ *        QWM_OBJ_NEAREST argmin_c of the squared distance (qwm_objective);
  *   the residual k - c_id and the Value each get per-group (32 channels)
  *   asymmetric INT2: fp16 zero-point = largest fp16 <= group min, fp16 step =
  *   smallest fp16 >= (max - zp) / 3, codes = clamp(rint((x - zp) / step), 0, 3);
  *   coef = U_r^T (k - (c_id + reconstructed residual)), float64, rounded once
- *   to fp16 (PSAC, "Step 2").
+ *   to fp16 (PSAC, "Step 2"); none at rank 0.
  * The records go to positions length .. length + n_tokens - 1 and the length
  * advances. Bit-identical whether tokens arrive in one call or several. */
 qwm_status qwm_quantize_append(qwm_cache* cache, const void* k, const void* v, int64_t n_tokens);
@@ -161,7 +180,8 @@ qwm_status qwm_truncate(qwm_cache* cache, int64_t n_tokens);
 /* ---- calibration import/export and inspection (tests, diagnostics) ---- */
 
 /* Stage a calibration given by the caller (C in the cache dtype, S_G and U_r
- * float, device pointers, layouts as above) and commit it as a new epoch. */
+ * float, device pointers, layouts as above) and commit it as a new epoch.
+ * S_G may be NULL with QWM_OBJ_NEAREST (stored as zeros), U_r at rank 0. */
 qwm_status qwm_import_calibration(qwm_cache* cache, const void* C, const float* S_G, const float* U_r);
 
 /* Copy epoch `epoch`'s calibration (or the staged one when epoch == -1) into
@@ -186,6 +206,18 @@ qwm_status qwm_export(const qwm_cache* cache, int64_t t0, int64_t t1, void* dev_
  * same contraction path qwm_attend uses. */
 qwm_status qwm_attend_logits(qwm_cache* cache, const void* q, int64_t n_q, int32_t head,
                              float softmax_scale, float* logits);
+
+/* Top-scoring token per Query (the article's attention analysis, roboind.com
+ * "Table 1"): top1 [heads][n_q] int32 receives, for each head and Query of q
+ * [heads][n_q][head_dim], the index of the token with the largest logit, the
+ * smallest index among equal logits. Without k_ref (n_ref == 0) the tokens are
+ * the cached ones and the logit is the compensated q . khat_j + (q . U_r) .
+ * coef_j of qwm_attend (unscaled); with k_ref [heads][n_ref][head_dim] in the
+ * cache dtype (1 <= n_ref <= 2^22) they are those full-precision Keys and the
+ * logit is q . k_j. Both go through the contraction path of qwm_attend, whose
+ * float32 logits decide the order. */
+qwm_status qwm_attend_top1(qwm_cache* cache, const void* q, int64_t n_q, const void* k_ref, int64_t n_ref,
+                           int32_t* top1);
 
 /* ---- kernel timing (HIP events around each launch, on the stream it runs on) ---- */
 

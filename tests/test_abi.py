@@ -16,12 +16,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "qwm.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(qwm_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(qwm_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     L = Q.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -40,8 +40,10 @@ def _desc(**kw):
     (dict(group=16), Q.QWM_ERR_UNSUPPORTED),
     (dict(n_centroids=0), Q.QWM_ERR_UNSUPPORTED),
     (dict(n_centroids=257), Q.QWM_ERR_UNSUPPORTED),
-    (dict(rank=0), Q.QWM_ERR_UNSUPPORTED),
+    (dict(rank=-1), Q.QWM_ERR_UNSUPPORTED),
     (dict(rank=17), Q.QWM_ERR_UNSUPPORTED),
+    (dict(objective=2), Q.QWM_ERR_INVALID_ARG),
+    (dict(objective=-1), Q.QWM_ERR_INVALID_ARG),
     (dict(max_epochs=65), Q.QWM_ERR_UNSUPPORTED),
     (dict(heads=0), Q.QWM_ERR_INVALID_ARG),
     (dict(dtype=7), Q.QWM_ERR_INVALID_ARG),
@@ -53,6 +55,17 @@ def test_desc_validation(kw, status):
     n = ctypes.c_size_t(0)
     assert Q.lib().qwm_arena_bytes(ctypes.byref(d), ctypes.byref(n)) == status
     assert Q.last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(rank=0), dict(objective=1), dict(rank=0, objective=1), dict(rank=16)])
+def test_desc_modes_accepted(kw):
+    """Rank 0 (PSAC off) and the nearest-centroid rule (QVG) are valid caches;
+    rank 0 needs fewer arena bytes (no coefficients, no basis)."""
+    d = _desc(**kw)
+    n = ctypes.c_size_t(0)
+    assert Q.lib().qwm_arena_bytes(ctypes.byref(d), ctypes.byref(n)) == Q.QWM_OK
+    if kw.get("rank") == 0:
+        assert n.value < Q.arena_bytes(_desc())
 
 
 def test_arena_bytes_accounts_for_every_region():
@@ -122,6 +135,38 @@ def test_call_order_and_argument_checks():
         Q.QWM_ERR_INVALID_ARG
     assert L.qwm_destroy(h) == Q.QWM_OK
     assert L.qwm_destroy(None) == Q.QWM_ERR_INVALID_ARG
+
+
+def test_mode_state_rules_and_top1_checks():
+    """build_centroids needs a staged subspace except for the nearest-centroid
+    rule at rank 0 (QVG), which then gets past the state check and fails only
+    for want of a device. qwm_attend_top1 checks its arguments first."""
+    L = Q.lib()
+    P = ctypes.c_void_p(4096)
+    top = ctypes.c_void_p(8192)
+    for kw, status in ((dict(), Q.QWM_ERR_STATE), (dict(rank=0), Q.QWM_ERR_STATE),
+                       (dict(objective=1), Q.QWM_ERR_STATE), (dict(rank=0, objective=1), None)):
+        h = _handle(**kw)
+        st = L.qwm_build_centroids(h, P, 100, 3)
+        if status is None:
+            assert st in (Q.QWM_OK, Q.QWM_ERR_HIP), Q.last_error()
+        else:
+            assert st == status
+        assert L.qwm_destroy(h) == Q.QWM_OK
+    h = _handle()
+    assert L.qwm_attend_top1(h, P, 4, None, 0, top) == Q.QWM_ERR_STATE  # empty cache
+    assert L.qwm_attend_top1(h, P, 4, None, 3, top) == Q.QWM_ERR_INVALID_ARG  # n_ref without k_ref
+    assert L.qwm_attend_top1(h, P, 4, P, 0, top) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend_top1(h, P, 4, P, (1 << 22) + 1, top) == Q.QWM_ERR_CAPACITY
+    assert L.qwm_attend_top1(h, P, 65, P, 10, top) == Q.QWM_ERR_CAPACITY
+    assert L.qwm_attend_top1(h, P, 4, P, 10, None) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend_top1(h, P, 0, P, 10, top) == Q.QWM_ERR_INVALID_ARG
+    # import without a basis is allowed only at rank 0
+    assert L.qwm_import_calibration(h, P, P, None) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_destroy(h) == Q.QWM_OK
+    h = _handle(rank=0, objective=1)
+    assert L.qwm_import_calibration(h, P, None, None) in (Q.QWM_OK, Q.QWM_ERR_HIP)
+    assert L.qwm_destroy(h) == Q.QWM_OK
 
 
 def test_no_oracle_in_product_path():

@@ -137,12 +137,17 @@ __device__ __forceinline__ TileInfo tile_info(const AttnPlan& p, int tile) {
 // other stage after it, so global latency hides behind the MFMA chains and
 // one barrier per tile suffices. Threads 0..KITEMS-1 build khat rows, threads
 // 256.. build vhat^T.
-template <int D, int DT, bool LOGITS>
+// MODE: kModeAttend (softmax and P.V), kModeLogits (write one head's scaled
+// logits), kModeTop1 (per Query the index of the largest unscaled logit).
+constexpr int kModeAttend = 0, kModeLogits = 1, kModeTop1 = 2;
+
+template <int D, int DT, int MODE>
 __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, const AttnPlan p) {
+  constexpr bool LOGITS = (MODE == kModeLogits), TOP1 = (MODE == kModeTop1), NOV = (MODE != kModeAttend);
   using Sh = AttnShape<D>;
   constexpr int KS = Sh::KS, KROW = Sh::KROW, VROW = Sh::VROW, NG = Sh::NG;
   constexpr bool QLO = (DT == 1);  // float32 Queries also carry a lo part
-  constexpr int KST = Sh::KST, VST = LOGITS ? 0 : Sh::VST;
+  constexpr int KST = Sh::KST, VST = NOV ? 0 : Sh::VST;
   constexpr int KITEMS = Sh::KITEMS, VITEMS = Sh::VITEMS;
   static_assert(KITEMS <= kAttnThreads && VITEMS <= kAttnThreads, "dequant items must fit one pass");
   // Raw words one thread holds for the next tile: khat values (16 cache-dtype
@@ -163,10 +168,10 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
   const bool wave_live = qw0 < a.nq;  // waves whose 32 Queries are all padding skip the math
   // wave-uniform producer roles (items are whole waves)
   const bool is_k = wave < KITEMS / 64;
-  const bool is_v = !LOGITS && wave < VITEMS / 64;
+  const bool is_v = !NOV && wave < VITEMS / 64;
   // softmax in the log2 domain with a positive factor; a negative scale is
   // carried by negated Queries (exact in fp16)
-  const float qsign = (!LOGITS && a.scale_log2 < 0.0f) ? -1.0f : 1.0f;
+  const float qsign = (!NOV && a.scale_log2 < 0.0f) ? -1.0f : 1.0f;
   const float cl2 = a.scale_log2 * qsign;
 
   const int T = p.tile_prefix[p.n_seg];
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
         *reinterpret_cast<uint4*>(row + 2 * D + 8 * kq) = cfw;
       }
     }
-    if constexpr (!LOGITS) {
+    if constexpr (!NOV) {
       if (is_v) {
         _Float16* Vh = Ks + KST;
         _Float16* Vl = Vh + VST;
@@ -401,11 +406,14 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
     for (int s2 = 0; s2 < 8; ++s2) qu[qb][s2] = (_Float16)0.0f;
   int cur_epoch = -2;
 
-  floatx4 O[2][LOGITS ? 1 : D / 16];
+  floatx4 O[2][NOV ? 1 : D / 16];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int cb = 0; cb < (LOGITS ? 1 : D / 16); ++cb) O[qb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < (NOV ? 1 : D / 16); ++cb) O[qb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // top-1 mode: this lane's best logit and its token index per Query block
+  float bval[2] = {-__builtin_inff(), -__builtin_inff()};
+  int bidx[2] = {0x7fffffff, 0x7fffffff};
   // per lane: this lane's share of the row sum of the fp16 P (the values the
   // PV product uses), float32
   float lrow[2] = {0.0f, 0.0f};
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int64_t qi = qw0 + 16 * qb + l16;
-          if (ep >= 0 && qi < a.nq) {
+          if (ep >= 0 && qi < a.nq && a.r > 0) {
             const float* src =
                 a.qU + (((int64_t)h * a.n_epoch_slots + ep) * a.nq + qi) * kRankPad + 8 * (g & 1);
 #pragma unroll
@@ -520,6 +528,21 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
               }
           }
         }
+      } else if constexpr (TOP1) {
+        // this lane's tokens of the tile in ascending order: a strict compare
+        // keeps the first of equal logits
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int j = 16 * tb + 4 * g + v;
+              if (j < ti.tcount && S[qb][tb][v] > bval[qb]) {
+                bval[qb] = S[qb][tb][v];
+                bidx[qb] = ti.tstart + j;
+              }
+            }
       } else {
         // ---- online softmax (log2 domain). The running max is only raised
         // when a row's new max exceeds it by more than 8 (p <= 2^8 stays exact
@@ -610,7 +633,34 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
     __syncthreads();
   }
 
-  if constexpr (!LOGITS) {
+  if constexpr (TOP1) {
+    if (!wave_live) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // the four lane groups holding this Query: larger logit, then smaller index
+      float bv = bval[qb];
+      int bi = bidx[qb];
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      const int64_t qi = qw0 + 16 * qb + l16;
+      if (qi >= a.nq || g != 0) continue;
+      if (a.splits == 1) {
+        a.top1[(int64_t)h * a.nq + qi] = bi;
+      } else {
+        const int64_t row = ((int64_t)split * a.H + h) * a.nq + qi;
+        a.part_ml[row * 2] = bv;
+        a.part_ml[row * 2 + 1] = __int_as_float(bi);
+      }
+    }
+  }
+  if constexpr (!NOV) {
     if (!wave_live) return;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -642,6 +692,25 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
       }
     }
   }
+}
+
+// Top-1 over the split partials (value, index) of each (head, Query): the
+// larger logit wins, the smaller token index on a tie.
+__global__ __launch_bounds__(256) void top1_merge_kernel(const AttnArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)a.H * a.nq;
+  if (row >= rows) return;
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff;
+  for (int s = 0; s < a.splits; ++s) {
+    const float v = a.part_ml[(s * rows + row) * 2];
+    const int i = __float_as_int(a.part_ml[(s * rows + row) * 2 + 1]);
+    if (v > bv || (v == bv && i < bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  a.top1[row] = bi;
 }
 
 // Log-sum-exp merge of the split-KV partials (log2 domain): one thread per
@@ -706,26 +775,36 @@ hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, 
   return hipGetLastError();
 }
 
-template <bool LOGITS>
+template <int MODE>
 static hipError_t launch_attend_impl(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  dim3 grid((unsigned)((a.nq + kTileQ - 1) / kTileQ), (unsigned)a.splits, LOGITS ? 1u : (unsigned)a.H);
+  dim3 grid((unsigned)((a.nq + kTileQ - 1) / kTileQ), (unsigned)a.splits,
+            MODE == kModeLogits ? 1u : (unsigned)a.H);
   dim3 block(kAttnThreads);
   if (D == 128 && dtype == 0)
-    hipLaunchKernelGGL((attend_kernel<128, 0, LOGITS>), grid, block, 0, s, a, p);
+    hipLaunchKernelGGL((attend_kernel<128, 0, MODE>), grid, block, 0, s, a, p);
   else if (D == 128)
-    hipLaunchKernelGGL((attend_kernel<128, 1, LOGITS>), grid, block, 0, s, a, p);
+    hipLaunchKernelGGL((attend_kernel<128, 1, MODE>), grid, block, 0, s, a, p);
   else if (dtype == 0)
-    hipLaunchKernelGGL((attend_kernel<64, 0, LOGITS>), grid, block, 0, s, a, p);
+    hipLaunchKernelGGL((attend_kernel<64, 0, MODE>), grid, block, 0, s, a, p);
   else
-    hipLaunchKernelGGL((attend_kernel<64, 1, LOGITS>), grid, block, 0, s, a, p);
+    hipLaunchKernelGGL((attend_kernel<64, 1, MODE>), grid, block, 0, s, a, p);
   return hipGetLastError();
 }
 
 hipError_t launch_attend(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  return launch_attend_impl<false>(D, dtype, a, p, s);
+  return launch_attend_impl<kModeAttend>(D, dtype, a, p, s);
 }
 hipError_t launch_attend_logits(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  return launch_attend_impl<true>(D, dtype, a, p, s);
+  return launch_attend_impl<kModeLogits>(D, dtype, a, p, s);
+}
+hipError_t launch_attend_top1(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
+  return launch_attend_impl<kModeTop1>(D, dtype, a, p, s);
+}
+
+hipError_t launch_top1_merge(const AttnArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.H * a.nq;
+  hipLaunchKernelGGL(top1_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(int D, const AttnArgs& a, hipStream_t s) {

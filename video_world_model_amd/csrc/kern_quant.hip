@@ -3,7 +3,8 @@
 //
 // Method (QuantWM, arXiv 2609.26425; roboind.com article "Step 1" and
 // "Step 2", fugumt.com abstract): each Key is assigned the centroid that
-// minimizes J = sum_G S_G (max_G r - min_G r)^2, r = k - c, the residual is
+// minimizes J = sum_G S_G (max_G r - min_G r)^2, r = k - c (or, for the QVG
+// baseline of "Step 1", the squared distance |r|^2), the residual is
 // stored as per-group asymmetric INT2 with fp16 zero-point/step, the Key's
 // remaining error is projected on the PSAC basis (r fp16 coefficients), and
 // the Value is stored as plain per-group INT2.
@@ -47,6 +48,38 @@ __device__ __forceinline__ float qsac_cost(const float (&kf)[D], const float* __
     J = (G == 0) ? u : J + u;
   }
   return J;
+}
+
+// QVG's nearest-centroid cost (float32, fixed order): per group the running
+// sum p_G = t_0 + t_1 + ... of t_j = r_j * r_j over the channels in ascending
+// order, then D = ((p_0 + p_1) + p_2) + ...
+template <int D>
+__device__ __forceinline__ float nearest_cost(const float (&kf)[D], const float* __restrict__ crow) {
+  constexpr int NG = D / kGroup;
+  float J = 0.0f;
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    const float r0 = kf[G * kGroup] - crow[G * kGroup];
+    float p = r0 * r0;
+#pragma unroll
+    for (int j = 1; j < kGroup; ++j) {
+      const float r = kf[G * kGroup + j] - crow[G * kGroup + j];
+      const float t = r * r;
+      p = p + t;
+    }
+    J = (G == 0) ? p : J + p;
+  }
+  return J;
+}
+
+// Assignment cost of the chosen rule: kObjQsac or kObjNearest.
+template <int OBJ, int D>
+__device__ __forceinline__ float assign_cost(const float (&kf)[D], const float* __restrict__ crow,
+                                             const float (&SG)[D / kGroup]) {
+  if constexpr (OBJ == kObjNearest)
+    return nearest_cost<D>(kf, crow);
+  else
+    return qsac_cost<D>(kf, crow, SG);
 }
 
 // Per-group INT2 parameters (signed zeros folded to +0):
@@ -169,7 +202,7 @@ __device__ __forceinline__ void int2_row(const float (&x)[D], uint32_t (&words)[
 //           adjacent), and all records are written with contiguous stores.
 constexpr int kQTok = 64;
 
-template <int D, int DT, bool ASSIGN_ONLY>
+template <int D, int DT, bool ASSIGN_ONLY, int OBJ>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   constexpr int NG = D / kGroup;
   __shared__ float bj[4][kQTok];
@@ -183,7 +216,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const int64_t t0 = (int64_t)blockIdx.x * kQTok;
   const int nt = (int)((a.n - t0) < kQTok ? (a.n - t0) : kQTok);
 
-  // ---- phase 1: QSAC objective over this wave's candidate quarter. It runs
+  // ---- phase 1: assignment cost over this wave's candidate quarter. It runs
   // before any barrier so that the wave-uniform candidate rows are fetched
   // with scalar loads (a barrier would make them possibly clobbered).
   {
@@ -198,7 +231,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     float bestJ = __builtin_inff();
     int best = c0;
     for (int c = c0; c < c1; ++c) {
-      const float J = qsac_cost<D>(kf, Ch + (int64_t)c * D, SG);
+      const float J = assign_cost<OBJ, D>(kf, Ch + (int64_t)c * D, SG);
       if (J < bestJ) {  // strict: the smallest id keeps an exact tie
         bestJ = J;
         best = c;
@@ -459,7 +492,8 @@ __global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys
 //
 // sqrt(J) is a seminorm of r = k - c: each group range R_G is one (it is
 // subadditive and absolutely homogeneous) and sqrt(sum_G S_G R_G^2) is a
-// weighted 2-norm of them. Hence, for a token x last assigned to centroid b,
+// weighted 2-norm of them; the square root of the nearest-centroid cost is
+// the Euclidean norm. Hence, for a token x last assigned to centroid b,
 // N(x - c) >= N(c - b) - N(x - b), and every candidate with
 // N(c - b) > 2 N(x - b) has J(x, c) > J(x, b) strictly: it can neither win
 // nor tie. Tokens are grouped by their previous centroid, 64 to a wave; a
@@ -532,7 +566,7 @@ __global__ __launch_bounds__(1024) void bucket_kernel(const uint8_t* ids, int64_
 // scalar loads, so nothing before them may look like a memory clobber: the
 // centroid distances N(C_c - C_b) are recomputed by every wave (one lane per
 // candidate) instead of being shared through LDS behind a barrier.
-template <int D, int DT>
+template <int D, int DT, int OBJ>
 __global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, int64_t n, int m, const float* C32,
                                                             const float* S, const int32_t* perm, const int32_t* off,
                                                             const int32_t* woff, uint8_t* ids_out) {
@@ -572,14 +606,14 @@ __global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, in
     if (64 * rd < m) {
       float x[D];
       load_row_span<D, 1>(Ch, (int64_t)(c < m ? c : 0) * D, x);
-      ccd[rd] = sqrtf(qsac_cost<D>(x, Cb, SG));
+      ccd[rd] = sqrtf(assign_cost<OBJ, D>(x, Cb, SG));
     }
   }
 
   const int tok = perm[(int64_t)h * n + start + (lane < cnt ? lane : cnt - 1)];
   float kf[D];
   load_row_span<D, DT>(keys, ((int64_t)h * n + tok) * D, kf);
-  const float Jb = qsac_cost<D>(kf, Cb, SG);
+  const float Jb = assign_cost<OBJ, D>(kf, Cb, SG);
   float d = (lane < cnt) ? sqrtf(Jb) : 0.0f;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) d = fmaxf(d, __shfl_xor(d, o));
@@ -597,7 +631,7 @@ __global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, in
       const int c = 64 * rd + __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(keep));
       keep &= keep - 1;
       if ((rank++ & 3) != wave) continue;
-      const float J = qsac_cost<D>(kf, Ch + (int64_t)c * D, SG);
+      const float J = assign_cost<OBJ, D>(kf, Ch + (int64_t)c * D, SG);
       if (J < bestJ || (J == bestJ && c < best)) {
         bestJ = J;
         best = c;
@@ -621,6 +655,11 @@ __global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, in
   }
 }
 
+__global__ void fill_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 template <int DT>
 __global__ void shadow_kernel(const void* C, const float* U, int64_t nC, int64_t nU, float* C32, double* U64) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -635,22 +674,30 @@ hipError_t launch_quantize(int D, int dtype, const QuantArgs& a, hipStream_t s) 
   dim3 grid((unsigned)((a.n + kQTok - 1) / kQTok), (unsigned)a.H);
   dim3 block(256);
   const bool assign = (a.v == nullptr);
-#define QWM_QLAUNCH(DD, TT)                                                   \
-  if (assign)                                                                 \
-    hipLaunchKernelGGL((quantize_kernel<DD, TT, true>), grid, block, 0, s, a); \
-  else                                                                        \
-    hipLaunchKernelGGL((quantize_kernel<DD, TT, false>), grid, block, 0, s, a);
+#define QWM_QLAUNCH(DD, TT, OO)                                                   \
+  if (assign)                                                                     \
+    hipLaunchKernelGGL((quantize_kernel<DD, TT, true, OO>), grid, block, 0, s, a); \
+  else                                                                            \
+    hipLaunchKernelGGL((quantize_kernel<DD, TT, false, OO>), grid, block, 0, s, a);
+#define QWM_QOBJ(DD, TT)                  \
+  if (a.obj == kObjNearest) {             \
+    QWM_QLAUNCH(DD, TT, kObjNearest)      \
+  } else {                                \
+    QWM_QLAUNCH(DD, TT, kObjQsac)         \
+  }
+  if (a.obj != kObjQsac && a.obj != kObjNearest) return hipErrorInvalidValue;
   if (D == 128 && dtype == 0) {
-    QWM_QLAUNCH(128, 0)
+    QWM_QOBJ(128, 0)
   } else if (D == 128 && dtype == 1) {
-    QWM_QLAUNCH(128, 1)
+    QWM_QOBJ(128, 1)
   } else if (D == 64 && dtype == 0) {
-    QWM_QLAUNCH(64, 0)
+    QWM_QOBJ(64, 0)
   } else if (D == 64 && dtype == 1) {
-    QWM_QLAUNCH(64, 1)
+    QWM_QOBJ(64, 1)
   } else {
     return hipErrorInvalidValue;
   }
+#undef QWM_QOBJ
 #undef QWM_QLAUNCH
   return hipGetLastError();
 }
@@ -673,20 +720,29 @@ hipError_t launch_kmeans_bucket(const uint8_t* ids, int64_t n, int H, int m, int
   return hipGetLastError();
 }
 
-hipError_t launch_kmeans_assign_pruned(int D, int dtype, const void* keys, int64_t n, int H, int m, const float* C32,
-                                       const float* S, const int32_t* perm, const int32_t* off, const int32_t* woff,
-                                       uint8_t* ids_out, hipStream_t s) {
+hipError_t launch_kmeans_assign_pruned(int D, int dtype, int obj, const void* keys, int64_t n, int H, int m,
+                                       const float* C32, const float* S, const int32_t* perm, const int32_t* off,
+                                       const int32_t* woff, uint8_t* ids_out, hipStream_t s) {
   dim3 grid((unsigned)((n + 63) / 64 + m), (unsigned)H), block(256);
-#define QWM_PLAUNCH(DD, TT) \
-  hipLaunchKernelGGL((assign_pruned_kernel<DD, TT>), grid, block, 0, s, keys, n, m, C32, S, perm, off, woff, ids_out)
-  if (D == 128 && dtype == 0)
-    QWM_PLAUNCH(128, 0);
-  else if (D == 128)
-    QWM_PLAUNCH(128, 1);
-  else if (dtype == 0)
-    QWM_PLAUNCH(64, 0);
-  else
-    QWM_PLAUNCH(64, 1);
+  if (obj != kObjQsac && obj != kObjNearest) return hipErrorInvalidValue;
+#define QWM_PLAUNCH(DD, TT, OO)                                                                                  \
+  hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO>), grid, block, 0, s, keys, n, m, C32, S, perm, off, woff, \
+                     ids_out)
+#define QWM_POBJ(DD, TT)                \
+  if (obj == kObjNearest)               \
+    QWM_PLAUNCH(DD, TT, kObjNearest);   \
+  else                                  \
+    QWM_PLAUNCH(DD, TT, kObjQsac);
+  if (D == 128 && dtype == 0) {
+    QWM_POBJ(128, 0)
+  } else if (D == 128) {
+    QWM_POBJ(128, 1)
+  } else if (dtype == 0) {
+    QWM_POBJ(64, 0)
+  } else {
+    QWM_POBJ(64, 1)
+  }
+#undef QWM_POBJ
 #undef QWM_PLAUNCH
   return hipGetLastError();
 }
@@ -702,6 +758,12 @@ hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_
     hipLaunchKernelGGL((update_kernel<64, 0>), grid, block, 0, s, keys, ids, n, m, C, C32);
   else
     hipLaunchKernelGGL((update_kernel<64, 1>), grid, block, 0, s, keys, ids, n, m, C, C32);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

@@ -41,14 +41,15 @@ qwm_status check_desc(const qwm_desc* d) {
   if (!d) return fail(QWM_ERR_INVALID_ARG, "desc is NULL");
   if (d->heads < 1) return fail(QWM_ERR_INVALID_ARG, "heads must be >= 1");
   if (d->dtype != QWM_BF16 && d->dtype != QWM_F32) return fail(QWM_ERR_INVALID_ARG, "dtype must be QWM_BF16 or QWM_F32");
-  if (d->reserved != 0) return fail(QWM_ERR_INVALID_ARG, "reserved must be 0");
+  if (d->objective != QWM_OBJ_QSAC && d->objective != QWM_OBJ_NEAREST)
+    return fail(QWM_ERR_INVALID_ARG, "objective must be QWM_OBJ_QSAC or QWM_OBJ_NEAREST");
   if (d->capacity_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "capacity_tokens must be >= 1");
   if (d->max_query_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "max_query_tokens must be >= 1");
   if (d->max_build_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "max_build_tokens must be >= 1");
   if (d->head_dim != 64 && d->head_dim != 128) return fail(QWM_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (d->group != qwm::kGroup) return fail(QWM_ERR_UNSUPPORTED, "group must be 32");
   if (d->n_centroids < 1 || d->n_centroids > 256) return fail(QWM_ERR_UNSUPPORTED, "n_centroids must be 1..256");
-  if (d->rank < 1 || d->rank > qwm::kRankPad) return fail(QWM_ERR_UNSUPPORTED, "rank must be 1..16");
+  if (d->rank < 0 || d->rank > qwm::kRankPad) return fail(QWM_ERR_UNSUPPORTED, "rank must be 0..16");
   if (d->max_epochs < 1 || d->max_epochs > qwm::kMaxEpochs) return fail(QWM_ERR_UNSUPPORTED, "max_epochs must be 1..64");
   if (d->capacity_tokens > ((int64_t)1 << 26))
     return fail(QWM_ERR_UNSUPPORTED, "capacity_tokens beyond 2^26 per head");
@@ -78,7 +79,9 @@ Layout make_layout(const qwm_desc* d) {
   L.kparam = take((size_t)(H * L.capP * nG * 4));
   L.vparam = take((size_t)(H * L.capP * nG * 4));
   L.ids = take((size_t)(H * L.capP));
-  L.coef = take((size_t)(H * L.capP * r * 2));
+  // the attention tile loads read 16 coefficient halves per token whatever r
+  // is (those past r are discarded), hence the tail
+  L.coef = take((size_t)(H * L.capP * r * 2 + 64));
   L.epochC = take((size_t)((E + 1) * H * m * D * esz));
   L.epochS = take((size_t)((E + 1) * H * nG * 4));
   L.epochU = take((size_t)((E + 1) * H * D * r * 4));
@@ -128,6 +131,7 @@ struct qwm_cache {
   int64_t length = 0;
   std::vector<int64_t> epoch_start;  // committed epoch i lives in slot i
   bool staged_subspace = false;
+  int obj = 0;  // qwm::kObjQsac or qwm::kObjNearest
   // The eigensolve of build_subspace runs on `side` (created on first use,
   // default priority) so the k-means of build_centroids, which needs only the
   // sensitivity, overlaps it; `stream` waits for `join_ev` before the staged
@@ -222,7 +226,7 @@ qwm_status commit_staged(qwm_cache* c) {
     return fail_hip(e, "commit C");
   if ((e = hipMemcpyAsync(c->slotS(slot), c->slotS(st), bS, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
     return fail_hip(e, "commit S");
-  if ((e = hipMemcpyAsync(c->slotU(slot), c->slotU(st), bU, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
+  if (bU && (e = hipMemcpyAsync(c->slotU(slot), c->slotU(st), bU, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
     return fail_hip(e, "commit U");
   e = c->run(QWM_K_OTHER, [&] {
     return qwm::launch_shadow(c->D, c->dtype, c->slotC(slot), c->slotU(slot), c->H, c->m, c->r, c->C32(), c->U64(),
@@ -282,6 +286,26 @@ qwm::AttnArgs base_args(qwm_cache* c) {
   return a;
 }
 
+// Split the KV tiles so that the workgroups fill the device in as few
+// rounds as possible: cost = rounds x (tiles per workgroup + 2 for its
+// prologue and epilogue) + 2 for the merge pass when split; one 145 KB-LDS
+// workgroup per CU for head_dim 128.
+int choose_splits(const qwm_cache* c, int64_t n_q, int T) {
+  const int64_t qtiles = (n_q + qwm::kTileQ - 1) / qwm::kTileQ;
+  const int64_t slots = (int64_t)c->ncu * (c->D == 128 ? 1 : 2);
+  int64_t splits = 1, best = -1;
+  for (int64_t sp = 1; sp <= 16 && sp <= T; ++sp) {
+    if (sp > 1 && sp * c->H * n_q > c->L.part_rows) break;
+    const int64_t rounds = (qtiles * c->H * sp + slots - 1) / slots;
+    const int64_t cost = rounds * ((T + sp - 1) / sp + 2) + (sp > 1 ? 2 : 0);
+    if (best < 0 || cost < best) {
+      best = cost;
+      splits = sp;
+    }
+  }
+  return (int)splits;
+}
+
 }  // namespace
 
 extern "C" {
@@ -321,6 +345,7 @@ qwm_status qwm_create(const qwm_desc* desc, void* dev_arena, size_t arena_bytes,
   c->nG = desc->head_dim / qwm::kGroup;
   c->m = desc->n_centroids;
   c->r = desc->rank;
+  c->obj = desc->objective == QWM_OBJ_NEAREST ? qwm::kObjNearest : qwm::kObjQsac;
   c->dtype = desc->dtype;
   c->esz = desc->dtype == QWM_BF16 ? 2 : 4;
   c->device = dev;
@@ -388,6 +413,10 @@ qwm_status qwm_build_subspace(qwm_cache* c, const void* q_hist, int64_t n_hist) 
     return qwm::launch_sens(c->D, c->gram(), nchunk, n_hist, c->H, c->slotS(st_slot), c->stream);
   });
   if (e != hipSuccess) return fail_hip(e, "sensitivity");
+  if (c->r == 0) {  // PSAC off: no basis to compute
+    c->staged_subspace = true;
+    return QWM_OK;
+  }
   if ((e = hipEventRecord(c->fork_ev, c->stream)) != hipSuccess) return fail_hip(e, "fork eigensolve");
   if ((e = hipStreamWaitEvent(c->side, c->fork_ev, 0)) != hipSuccess) return fail_hip(e, "fork eigensolve");
   e = c->run_on(c->side, QWM_K_EIGEN, [&] {
@@ -407,12 +436,21 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
   if (n_keys < 1) return fail(QWM_ERR_INVALID_ARG, "n_keys must be >= 1");
   if (iters < 0) return fail(QWM_ERR_INVALID_ARG, "iters must be >= 0");
   if (n_keys > c->desc.max_build_tokens) return fail(QWM_ERR_CAPACITY, "n_keys exceeds max_build_tokens");
-  if (!c->staged_subspace) return fail(QWM_ERR_STATE, "build_centroids needs build_subspace first");
+  // The nearest-centroid rule with PSAC off needs no historical Queries: the
+  // staged sensitivity is then all zeros.
+  const bool no_subspace_needed = (c->obj == qwm::kObjNearest && c->r == 0);
+  if (!c->staged_subspace && !no_subspace_needed)
+    return fail(QWM_ERR_STATE, "build_centroids needs build_subspace first");
   if (!epoch_room(c)) return fail(QWM_ERR_CAPACITY, "max_epochs reached");
   if ((st = need_device(c)) != QWM_OK) return st;
   DeviceGuard g(c->device);
   const int stg = c->staged();
-  hipError_t e = c->run(QWM_K_OTHER, [&] {
+  hipError_t e;
+  if (!c->staged_subspace) {
+    e = c->run(QWM_K_OTHER, [&] { return qwm::launch_fill(c->slotS(stg), (int64_t)c->H * c->nG, 0.0f, c->stream); });
+    if (e != hipSuccess) return fail_hip(e, "zero sensitivity");
+  }
+  e = c->run(QWM_K_OTHER, [&] {
     return qwm::launch_kmeans_seed(c->D, c->dtype, keys, n_keys, c->H, c->m, c->slotC(stg), c->kmC32(), c->stream);
   });
   if (e != hipSuccess) return fail_hip(e, "kmeans seed");
@@ -430,6 +468,7 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
       a.H = c->H;
       a.m = c->m;
       a.r = c->r;
+      a.obj = c->obj;
       e = c->run(QWM_K_ASSIGN, [&] { return qwm::launch_quantize(c->D, c->dtype, a, c->stream); });
       if (e != hipSuccess) return fail_hip(e, "kmeans assign");
     } else {  // the same ids, skipping candidates the triangle inequality rules out
@@ -439,7 +478,7 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
       });
       if (e != hipSuccess) return fail_hip(e, "kmeans bucket");
       e = c->run(QWM_K_ASSIGN, [&] {
-        return qwm::launch_kmeans_assign_pruned(c->D, c->dtype, keys, n_keys, c->H, c->m, c->kmC32(), c->slotS(stg),
+        return qwm::launch_kmeans_assign_pruned(c->D, c->dtype, c->obj, keys, n_keys, c->H, c->m, c->kmC32(), c->slotS(stg),
                                                 c->km_perm(), c->km_off(), c->km_woff(), c->build_ids(), c->stream);
       });
       if (e != hipSuccess) return fail_hip(e, "kmeans assign");
@@ -457,8 +496,10 @@ qwm_status qwm_import_calibration(qwm_cache* c, const void* C, const float* S_G,
   qwm_status st;
   if ((st = check_cache(c)) != QWM_OK) return st;
   if ((st = check_ptr(C, "C")) != QWM_OK) return st;
-  if ((st = check_ptr(S_G, "S_G")) != QWM_OK) return st;
-  if ((st = check_ptr(U_r, "U_r")) != QWM_OK) return st;
+  if (S_G || c->obj == qwm::kObjQsac)
+    if ((st = check_ptr(S_G, "S_G")) != QWM_OK) return st;
+  if (U_r || c->r > 0)
+    if ((st = check_ptr(U_r, "U_r")) != QWM_OK) return st;
   if (!epoch_room(c)) return fail(QWM_ERR_CAPACITY, "max_epochs reached");
   if ((st = need_device(c)) != QWM_OK) return st;
   DeviceGuard g(c->device);
@@ -468,11 +509,16 @@ qwm_status qwm_import_calibration(qwm_cache* c, const void* C, const float* S_G,
   if ((e = hipMemcpyAsync(c->slotC(stg), C, (size_t)c->H * c->m * c->D * c->esz, hipMemcpyDeviceToDevice,
                           c->stream)) != hipSuccess)
     return fail_hip(e, "import C");
-  if ((e = hipMemcpyAsync(c->slotS(stg), S_G, (size_t)c->H * c->nG * 4, hipMemcpyDeviceToDevice, c->stream)) !=
-      hipSuccess)
-    return fail_hip(e, "import S");
-  if ((e = hipMemcpyAsync(c->slotU(stg), U_r, (size_t)c->H * c->D * c->r * 4, hipMemcpyDeviceToDevice,
-                          c->stream)) != hipSuccess)
+  if (S_G) {
+    if ((e = hipMemcpyAsync(c->slotS(stg), S_G, (size_t)c->H * c->nG * 4, hipMemcpyDeviceToDevice, c->stream)) !=
+        hipSuccess)
+      return fail_hip(e, "import S");
+  } else {
+    e = c->run(QWM_K_OTHER, [&] { return qwm::launch_fill(c->slotS(stg), (int64_t)c->H * c->nG, 0.0f, c->stream); });
+    if (e != hipSuccess) return fail_hip(e, "zero sensitivity");
+  }
+  if (c->r > 0 && (e = hipMemcpyAsync(c->slotU(stg), U_r, (size_t)c->H * c->D * c->r * 4, hipMemcpyDeviceToDevice,
+                                      c->stream)) != hipSuccess)
     return fail_hip(e, "import U");
   return commit_staged(c);
 }
@@ -493,7 +539,7 @@ qwm_status qwm_export_calibration(const qwm_cache* cc, int32_t epoch, void* C, f
   if (S_G && (e = hipMemcpyAsync(S_G, c->slotS(slot), (size_t)c->H * c->nG * 4, hipMemcpyDeviceToDevice,
                                  c->stream)) != hipSuccess)
     return fail_hip(e, "export S");
-  if (U_r && (e = hipMemcpyAsync(U_r, c->slotU(slot), (size_t)c->H * c->D * c->r * 4, hipMemcpyDeviceToDevice,
+  if (U_r && c->r > 0 && (e = hipMemcpyAsync(U_r, c->slotU(slot), (size_t)c->H * c->D * c->r * 4, hipMemcpyDeviceToDevice,
                                  c->stream)) != hipSuccess)
     return fail_hip(e, "export U");
   return QWM_OK;
@@ -523,6 +569,7 @@ qwm_status qwm_quantize_append(qwm_cache* c, const void* k, const void* v, int64
   a.H = c->H;
   a.m = c->m;
   a.r = c->r;
+  a.obj = c->obj;
   hipError_t e = c->run(QWM_K_QUANTIZE, [&] { return qwm::launch_quantize(c->D, c->dtype, a, c->stream); });
   if (e != hipSuccess) return fail_hip(e, "quantize");
   c->length += n_tokens;
@@ -570,28 +617,15 @@ qwm_status qwm_attend(qwm_cache* c, const void* q, int64_t n_q, const void* k_se
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.n_epoch_slots = E;
   a.out = out;
-  // Split the KV tiles so that the workgroups fill the device in as few
-  // rounds as possible: cost = rounds x (tiles per workgroup + 2 for its
-  // prologue and epilogue) + 2 for the merge pass when split; one 145 KB-LDS
-  // workgroup per CU for head_dim 128.
-  const int64_t qtiles = (n_q + qwm::kTileQ - 1) / qwm::kTileQ;
-  const int64_t slots = (int64_t)c->ncu * (c->D == 128 ? 1 : 2);
-  int64_t splits = 1, best = -1;
-  for (int64_t sp = 1; sp <= 16 && sp <= T; ++sp) {
-    if (sp > 1 && sp * c->H * n_q > c->L.part_rows) break;
-    const int64_t rounds = (qtiles * c->H * sp + slots - 1) / slots;
-    const int64_t cost = rounds * ((T + sp - 1) / sp + 2) + (sp > 1 ? 2 : 0);
-    if (best < 0 || cost < best) {
-      best = cost;
-      splits = sp;
-    }
+  a.splits = choose_splits(c, n_q, T);
+  hipError_t e = hipSuccess;
+  if (c->r > 0) {  // the kernels read no qU at rank 0
+    e = c->run(QWM_K_QU, [&] {
+      return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
+                            c->stream);
+    });
+    if (e != hipSuccess) return fail_hip(e, "qU");
   }
-  a.splits = (int)splits;
-  hipError_t e = c->run(QWM_K_QU, [&] {
-    return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
-                          c->stream);
-  });
-  if (e != hipSuccess) return fail_hip(e, "qU");
   e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_attend(c->D, c->dtype, a, p, c->stream); });
   if (e != hipSuccess) return fail_hip(e, "attend");
   if (a.splits > 1) {
@@ -628,13 +662,76 @@ qwm_status qwm_attend_logits(qwm_cache* c, const void* q, int64_t n_q, int32_t h
   a.logit_head = head;
   a.logit_len = c->length;
   a.splits = T < 64 ? T : 64;
-  hipError_t e = c->run(QWM_K_QU, [&] {
-    return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
-                          c->stream);
-  });
-  if (e != hipSuccess) return fail_hip(e, "qU");
+  hipError_t e = hipSuccess;
+  if (c->r > 0) {  // the kernels read no qU at rank 0
+    e = c->run(QWM_K_QU, [&] {
+      return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
+                            c->stream);
+    });
+    if (e != hipSuccess) return fail_hip(e, "qU");
+  }
   e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_attend_logits(c->D, c->dtype, a, p, c->stream); });
   if (e != hipSuccess) return fail_hip(e, "attend_logits");
+  return QWM_OK;
+}
+
+qwm_status qwm_attend_top1(qwm_cache* c, const void* q, int64_t n_q, const void* k_ref, int64_t n_ref,
+                           int32_t* top1) {
+  qwm_status st;
+  if ((st = check_cache(c)) != QWM_OK) return st;
+  if ((st = check_ptr(q, "q")) != QWM_OK) return st;
+  if ((st = check_ptr(top1, "top1")) != QWM_OK) return st;
+  if (n_q < 1) return fail(QWM_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (n_q > c->desc.max_query_tokens) return fail(QWM_ERR_CAPACITY, "n_q exceeds max_query_tokens");
+  const bool ref = (k_ref != nullptr);
+  if (ref) {
+    if ((st = check_ptr(k_ref, "k_ref")) != QWM_OK) return st;
+    if (n_ref < 1) return fail(QWM_ERR_INVALID_ARG, "n_ref must be >= 1 with k_ref");
+    if (n_ref > ((int64_t)1 << 22)) return fail(QWM_ERR_CAPACITY, "n_ref beyond 2^22");
+  } else {
+    if (n_ref != 0) return fail(QWM_ERR_INVALID_ARG, "n_ref must be 0 without k_ref");
+    if (c->epoch_start.empty() || c->length == 0) return fail(QWM_ERR_STATE, "empty cache");
+  }
+  if ((st = need_device(c)) != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  qwm::AttnPlan p;
+  if (ref) {  // one segment: the full-precision Keys
+    std::memset(&p, 0, sizeof(p));
+    p.n_seg = 1;
+    p.seg_start[0] = 0;
+    p.seg_len[0] = (int32_t)n_ref;
+    p.seg_epoch[0] = -1;
+    p.tile_prefix[1] = (int32_t)((n_ref + qwm::kTileKV - 1) / qwm::kTileKV);
+  } else {
+    make_plan(c, 0, false, p);
+  }
+  const int T = p.tile_prefix[p.n_seg];
+  const int E = (int)c->epoch_start.size();
+  qwm::AttnArgs a = base_args(c);
+  a.q = q;
+  a.qU = c->qU();
+  a.kself = ref ? k_ref : nullptr;
+  a.nq = n_q;
+  a.nself = ref ? n_ref : 0;
+  a.scale = 1.0f;
+  a.scale_log2 = 1.4426950408889634f;
+  a.n_epoch_slots = E;
+  a.top1 = top1;
+  a.splits = choose_splits(c, n_q, T);
+  hipError_t e = hipSuccess;
+  if (!ref && c->r > 0) {
+    e = c->run(QWM_K_QU, [&] {
+      return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
+                            c->stream);
+    });
+    if (e != hipSuccess) return fail_hip(e, "qU");
+  }
+  e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_attend_top1(c->D, c->dtype, a, p, c->stream); });
+  if (e != hipSuccess) return fail_hip(e, "attend_top1");
+  if (a.splits > 1) {
+    e = c->run(QWM_K_MERGE, [&] { return qwm::launch_top1_merge(a, c->stream); });
+    if (e != hipSuccess) return fail_hip(e, "top1 merge");
+  }
   return QWM_OK;
 }
 

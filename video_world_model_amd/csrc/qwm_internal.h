@@ -15,6 +15,8 @@ constexpr int kAttnThreads = 512;
 constexpr int kMaxEpochs = 64;
 constexpr int kMaxSegments = kMaxEpochs + 1;  // epochs + the self segment
 constexpr int kGramMaxChunks = 8;   // historical-Query chunks per head in the Gram
+constexpr int kObjQsac = 0;         // centroid rule: QSAC objective
+constexpr int kObjNearest = 1;      // centroid rule: nearest centroid (QVG)
 
 // Per-head structure-of-arrays cache. Every per-head array holds capP token
 // slots (capacity rounded up to a tile multiple) so tile loads never leave the
@@ -48,6 +50,7 @@ struct QuantArgs {
   int64_t pos0;            // first destination slot
   uint8_t* ids_out;        // assignment-only output [H][n] (k-means)
   int H, m, r;
+  int obj;                 // kObjQsac or kObjNearest
 };
 hipError_t launch_quantize(int D, int dtype, const QuantArgs& a, hipStream_t s);
 
@@ -61,9 +64,11 @@ hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_
 // skipping candidates that provably lose.
 hipError_t launch_kmeans_bucket(const uint8_t* ids, int64_t n, int H, int m, int32_t* perm, int32_t* off,
                                 int32_t* woff, hipStream_t s);
-hipError_t launch_kmeans_assign_pruned(int D, int dtype, const void* keys, int64_t n, int H, int m, const float* C32,
-                                       const float* S, const int32_t* perm, const int32_t* off, const int32_t* woff,
-                                       uint8_t* ids_out, hipStream_t s);
+hipError_t launch_kmeans_assign_pruned(int D, int dtype, int obj, const void* keys, int64_t n, int H, int m,
+                                       const float* C32, const float* S, const int32_t* perm, const int32_t* off,
+                                       const int32_t* woff, uint8_t* ids_out, hipStream_t s);
+// p[0 .. n) = v
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 // Float (and float64 U) shadows of a committed epoch, used by quantize.
 hipError_t launch_shadow(int D, int dtype, const void* C, const float* U, int H, int m, int r,
                          float* C32, double* U64, hipStream_t s);
@@ -105,6 +110,7 @@ struct AttnArgs {
   float* part_o;          // [splits][H][nq][D]
   float* part_ml;         // [splits][H][nq][2]
   float* logits;          // logits mode: [nq][len] of head `logit_head`
+  int32_t* top1;          // top-1 mode: [H][nq] token index of the largest logit
   int logit_head;
   int64_t logit_len;
 };
@@ -113,6 +119,11 @@ hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, 
 hipError_t launch_attend(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_attend_logits(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_merge(int D, const AttnArgs& a, hipStream_t s);
+// Top-1 mode: per (head, Query) the token with the largest unscaled logit
+// (first on a tie); with splits > 1 the partials go to part_ml and
+// launch_top1_merge combines them.
+hipError_t launch_attend_top1(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+hipError_t launch_top1_merge(const AttnArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- export
 struct ExportArgs {

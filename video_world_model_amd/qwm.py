@@ -29,6 +29,7 @@ STATUS_NAMES = {
     -4: "QWM_ERR_STATE", -5: "QWM_ERR_HIP", -6: "QWM_ERR_ARENA_TOO_SMALL",
 }
 QWM_BF16, QWM_F32 = 0, 1
+OBJECTIVES = {"qsac": 0, "nearest": 1}
 MASKS = {"none": 0, "full": 1, "causal": 2}
 KERNELS = {"quantize": 0, "attend": 1, "merge": 2, "qu": 3, "gram": 4, "eigen": 5, "assign": 6,
            "update": 7, "other": 8}
@@ -50,7 +51,7 @@ class Desc(ctypes.Structure):
         ("max_epochs", ctypes.c_int32),
         ("capacity_tokens", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("objective", ctypes.c_int32),
         ("max_query_tokens", ctypes.c_int64),
         ("max_build_tokens", ctypes.c_int64),
     ]
@@ -77,6 +78,7 @@ _SIGS = {
     "qwm_export_bytes": [_VP, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "qwm_export": [_VP, _I64, _I64, _VP],
     "qwm_attend_logits": [_VP, _VP, _I64, _I32, ctypes.c_float, _VP],
+    "qwm_attend_top1": [_VP, _VP, _I64, _VP, _I64, _VP],
     "qwm_profile_enable": [_VP, _I32],
     "qwm_profile_read": [_VP, _I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)],
 }
@@ -111,8 +113,8 @@ def check(status: int) -> None:
 
 
 def make_desc(heads, head_dim, n_centroids, rank, capacity_tokens, dtype=QWM_BF16, max_epochs=1,
-              max_query_tokens=1024, max_build_tokens=1024, group=32) -> Desc:
-    return Desc(heads, head_dim, group, n_centroids, rank, max_epochs, capacity_tokens, dtype, 0,
+              max_query_tokens=1024, max_build_tokens=1024, group=32, objective=0) -> Desc:
+    return Desc(heads, head_dim, group, n_centroids, rank, max_epochs, capacity_tokens, dtype, objective,
                 max_query_tokens, max_build_tokens)
 
 
@@ -131,12 +133,13 @@ class Cache:
 
     Tensors passed in must be contiguous, on the cache's device, in the
     cache dtype (``torch.bfloat16`` or ``torch.float32``), shaped
-    [heads][n][head_dim]; outputs are float32.
+    [heads][n][head_dim]; outputs are float32. ``objective`` is the centroid
+    rule ("qsac", or "nearest" for the QVG baseline); rank 0 turns PSAC off.
     """
 
     def __init__(self, heads: int, head_dim: int, n_centroids: int, rank: int, capacity_tokens: int,
                  dtype=None, max_epochs: int = 1, max_query_tokens: int = 1024,
-                 max_build_tokens: int = 1024, device=None):
+                 max_build_tokens: int = 1024, device=None, objective: str = "qsac"):
         import torch
         self.torch = torch
         if dtype is None:
@@ -147,9 +150,12 @@ class Cache:
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         self.heads, self.head_dim, self.n_centroids, self.rank = heads, head_dim, n_centroids, rank
         self.group = 32
+        if objective not in OBJECTIVES:
+            raise ValueError(f"objective must be one of {sorted(OBJECTIVES)}")
+        self.objective = objective
         self.desc = make_desc(heads, head_dim, n_centroids, rank, capacity_tokens,
                               QWM_BF16 if dtype == torch.bfloat16 else QWM_F32, max_epochs,
-                              max_query_tokens, max_build_tokens)
+                              max_query_tokens, max_build_tokens, objective=OBJECTIVES[objective])
         nbytes = arena_bytes(self.desc)
         with torch.cuda.device(self.device):
             self.arena = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
@@ -228,6 +234,20 @@ class Cache:
         check(lib().qwm_attend_logits(self._h, _ptr(q), q.shape[1], head, ctypes.c_float(scale), _ptr(out)))
         return out
 
+    def attend_top1(self, q, k_ref=None):
+        """Per head and Query, the index of the token with the largest logit:
+        over the cache (compensated logits) or, with k_ref, over those
+        full-precision Keys. Returns int32 [heads][n_q]."""
+        torch = self.torch
+        self._chk(q, "q")
+        nref = 0
+        if k_ref is not None:
+            self._chk(k_ref, "k_ref")
+            nref = k_ref.shape[1]
+        out = torch.empty((self.heads, q.shape[1]), dtype=torch.int32, device=self.device)
+        check(lib().qwm_attend_top1(self._h, _ptr(q), q.shape[1], _ptr(k_ref), nref, _ptr(out)))
+        return out
+
     def length(self) -> int:
         n = _I64(0)
         check(lib().qwm_length(self._h, ctypes.byref(n)))
@@ -246,11 +266,15 @@ class Cache:
         torch = self.torch
         if tuple(C.shape) != (self.heads, self.n_centroids, self.head_dim) or C.dtype != self.dtype:
             raise ValueError("C must be [heads][n_centroids][head_dim] in the cache dtype")
-        if tuple(S.shape) != (self.heads, self.head_dim // 32) or S.dtype != torch.float32:
+        if S is not None and (tuple(S.shape) != (self.heads, self.head_dim // 32) or S.dtype != torch.float32):
             raise ValueError("S must be [heads][head_dim/32] float32")
-        if tuple(U.shape) != (self.heads, self.head_dim, self.rank) or U.dtype != torch.float32:
+        if U is not None and (tuple(U.shape) != (self.heads, self.head_dim, self.rank) or U.dtype != torch.float32):
             raise ValueError("U must be [heads][head_dim][rank] float32")
+        if self.rank == 0:
+            U = None  # nothing to import
         for t in (C, S, U):
+            if t is None:
+                continue
             if t.device != self.device or not t.is_contiguous():
                 raise ValueError("calibration tensors must be contiguous on the cache device")
         check(lib().qwm_import_calibration(self._h, _ptr(C), _ptr(S), _ptr(U)))
