@@ -161,6 +161,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_chunk", choices=["tiny", "video_chunk", "wm_layer"])
     ap.add_argument("--mode", default="quantwm", choices=sorted(MODES))
+    ap.add_argument("--graph", type=int, default=0,
+                    help="1: capture one step in a HIP graph (through torch.cuda.graph) and time its replays; "
+                         "0: time eager calls")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's timed sample (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg) over this many MiB first, as a known-size "
@@ -203,10 +206,15 @@ def main():
     if w.n_self:
         ks = dev([g.self_keys() for g in gens])
         vs = dev([g.self_values() for g in gens])
-    cache = Cache(w.heads, w.head_dim, w.n_centroids, r, w.n_kv,
-                  dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
-                  max_query_tokens=w.n_q, max_build_tokens=w.n_kv, objective=objective)
-    out = torch.empty((w.heads, w.n_q, w.head_dim), dtype=torch.float32, device="cuda")
+    # the library works on the stream current at create: a stream of our own,
+    # which is also the one a graph is captured on
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        cache = Cache(w.heads, w.head_dim, w.n_centroids, r, w.n_kv,
+                      dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                      max_query_tokens=w.n_q, max_build_tokens=w.n_kv, objective=objective)
+        out = torch.empty((w.heads, w.n_q, w.head_dim), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
 
     def step():
         cache.truncate(0)
@@ -216,20 +224,40 @@ def main():
         cache.quantize_append(keys, vals)
         cache.attend(q, ks, vs, mask=w.self_mask, out=out)
 
-    for _ in range(args.warmup):
-        step()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
-    cache.profile_enable(True)
-    stream = torch.cuda.current_stream()
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+
+    # timed region: K steps, nothing else on the stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
-        step()
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
+    # per-kernel times: the same number of eager steps with the library's
+    # HIP events around every launch (outside the timed region)
+    with torch.cuda.stream(stream):
+        cache.profile_enable(True)
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
     kern = {}
     for k in KERNELS:
         ms, n = cache.profile_read(k)
@@ -237,8 +265,10 @@ def main():
             kern[k] = dict(ms_per_step=ms / args.steps, launches_per_step=n / args.steps, avg_launch_ms=ms / n)
     cache.profile_enable(False)
     # the article's "Table 1" diagnostic, outside the timed region
-    top_cache = cache.attend_top1(q)
-    top_full = cache.attend_top1(q, keys)
+    with torch.cuda.stream(stream):
+        top_cache = cache.attend_top1(q)
+        top_full = cache.attend_top1(q, keys)
+    torch.cuda.synchronize()
     top1_rate = float((top_cache != top_full).float().mean().item())
 
     ops_peak = QSAC_OPS_PEAK if objective == "qsac" else NEAREST_OPS_PEAK
@@ -294,7 +324,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32-valu+f16-mfma",
         "data": "synthetic",
-        "config": {"workload": w.name, "mode": args.mode, "objective": objective, "heads": w.heads,
+        "config": {"workload": w.name, "mode": args.mode, "hip_graph": bool(args.graph), "objective": objective, "heads": w.heads,
                    "head_dim": w.head_dim, "group": w.group,
                    "n_centroids": w.n_centroids, "rank": r, "n_kv": w.n_kv, "n_q": w.n_q,
                    "n_self": w.n_self, "n_hist": w.n_hist, "kmeans_iters": w.kmeans_iters,

@@ -655,6 +655,26 @@ __global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, in
   }
 }
 
+// Commit of a staged calibration: copy C, S, U from the staging slot to the
+// epoch slot and write the float / float64 shadows quantize reads, in one pass.
+template <int DT>
+__global__ void commit_kernel(const void* Cs, const float* Ss, const float* Us, void* Cd, float* Sd, float* Ud,
+                              int64_t nC, int64_t nS, int64_t nU, float* C32, double* U64) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nC) {
+    if constexpr (DT == 0)
+      reinterpret_cast<uint16_t*>(Cd)[i] = reinterpret_cast<const uint16_t*>(Cs)[i];
+    else
+      reinterpret_cast<float*>(Cd)[i] = reinterpret_cast<const float*>(Cs)[i];
+    C32[i] = load_in<DT>(Cs, i);
+  }
+  if (i < nS) Sd[i] = Ss[i];
+  if (i < nU) {
+    Ud[i] = Us[i];
+    U64[i] = (double)Us[i];
+  }
+}
+
 __global__ void fill_kernel(float* p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -764,6 +784,19 @@ hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(int D, int dtype, const void* Cs, const float* Ss, const float* Us, void* Cd, float* Sd,
+                         float* Ud, int H, int m, int r, float* C32, double* U64, hipStream_t s) {
+  const int64_t nC = (int64_t)H * m * D, nS = (int64_t)H * (D / kGroup), nU = (int64_t)H * D * r;
+  int64_t n = nC > nU ? nC : nU;
+  if (nS > n) n = nS;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(commit_kernel<0>, grid, block, 0, s, Cs, Ss, Us, Cd, Sd, Ud, nC, nS, nU, C32, U64);
+  else
+    hipLaunchKernelGGL(commit_kernel<1>, grid, block, 0, s, Cs, Ss, Us, Cd, Sd, Ud, nC, nS, nU, C32, U64);
   return hipGetLastError();
 }
 

@@ -219,20 +219,11 @@ qwm_status commit_staged(qwm_cache* c) {
   int slot = (int)c->epoch_start.size();
   if (!c->epoch_start.empty() && c->epoch_start.back() == c->length) slot -= 1;
   const int st = c->staged();
-  const size_t bC = (size_t)c->H * c->m * c->D * c->esz, bS = (size_t)c->H * c->nG * 4,
-               bU = (size_t)c->H * c->D * c->r * 4;
-  hipError_t e;
-  if ((e = hipMemcpyAsync(c->slotC(slot), c->slotC(st), bC, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
-    return fail_hip(e, "commit C");
-  if ((e = hipMemcpyAsync(c->slotS(slot), c->slotS(st), bS, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
-    return fail_hip(e, "commit S");
-  if (bU && (e = hipMemcpyAsync(c->slotU(slot), c->slotU(st), bU, hipMemcpyDeviceToDevice, c->stream)) != hipSuccess)
-    return fail_hip(e, "commit U");
-  e = c->run(QWM_K_OTHER, [&] {
-    return qwm::launch_shadow(c->D, c->dtype, c->slotC(slot), c->slotU(slot), c->H, c->m, c->r, c->C32(), c->U64(),
-                              c->stream);
+  hipError_t e = c->run(QWM_K_OTHER, [&] {
+    return qwm::launch_commit(c->D, c->dtype, c->slotC(st), c->slotS(st), c->slotU(st), c->slotC(slot), c->slotS(slot),
+                              c->slotU(slot), c->H, c->m, c->r, c->C32(), c->U64(), c->stream);
   });
-  if (e != hipSuccess) return fail_hip(e, "shadow");
+  if (e != hipSuccess) return fail_hip(e, "commit");
   if (slot == (int)c->epoch_start.size())
     c->epoch_start.push_back(c->length);
   else

@@ -69,6 +69,9 @@ hipError_t launch_kmeans_assign_pruned(int D, int dtype, int obj, const void* ke
                                        const int32_t* woff, uint8_t* ids_out, hipStream_t s);
 // p[0 .. n) = v
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+// Copy a staged calibration (C, S, U) into an epoch slot and write its shadows.
+hipError_t launch_commit(int D, int dtype, const void* Cs, const float* Ss, const float* Us, void* Cd, float* Sd,
+                         float* Ud, int H, int m, int r, float* C32, double* U64, hipStream_t s);
 // Float (and float64 U) shadows of a committed epoch, used by quantize.
 hipError_t launch_shadow(int D, int dtype, const void* C, const float* U, int H, int m, int r,
                          float* C32, double* U64, hipStream_t s);
