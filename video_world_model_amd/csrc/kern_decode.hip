@@ -1,0 +1,506 @@
+// Decode-shaped attention over the 2-bit QuantWM cache (gfx950): a few
+// Queries per head (16 per workgroup) against a long cache, the regime
+// where reading the packed cache from HBM should bound the time.
+//
+// Method (QuantWM; fugumt.com abstract and roboind.com "Step 1"/"Step 2"):
+// for cached token t of epoch e(t), Key residual group G with zero-point zp_G
+// and step s_G, centroid id(t) and PSAC coefficients coef_t,
+//   l_qt = q . C_id(t) + sum_G s_G (q_G . code_G) + sum_G zp_G (sum of q over G)
+//          + (q U_r^(e)) . coef_t,
+// which is q . khat_t + (q U_r) . coef_t with khat = c + zp + code * s
+// regrouped so that no Key is dequantized:
+//  * q . C_m is one table per (head, epoch, Query) made by qc_kernel (bf16
+//    products are exact, float32 sums), looked up by id;
+//  * q_G . code_G runs on v_mfma_f32_16x16x32_f16 with the 2-bit codes as
+//    the operand (small integers are exact in fp16; q is exact in fp16 for
+//    bf16 inputs), one MFMA per group, and the group's step is applied to the
+//    float32 result;
+//  * zp . qsum and the PSAC term are one more pair of MFMAs ([qU_hi | qU_lo]
+//    x [coef | coef], [qsum_hi | qsum_lo] x [zp | zp]);
+//  * Values are dequantized once per token into LDS as fp16 hi + lo pairs
+//    (vhat^T, two passes of 64 channels) and o += P vhat by MFMA with P in
+//    fp16.
+// Requires bf16 inputs, head_dim 128 and an even PSAC rank.
+// Mapping: one workgroup = one wave = 16 Queries of one head and one
+// split of the KV tiles; every wave streams its own 64-token tiles, so many
+// tiles are in flight per CU. The packed words of the next tile are loaded
+// while the current one is computed.
+#include "qwm_dev.h"
+#include "qwm_internal.h"
+
+namespace qwm {
+
+namespace {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx4 mfma_f16(const half8& a, const half8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma_bf16(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ half2v pk_f16(float x, float y) { return __builtin_convertvector(float2v{x, y}, half2v); }
+
+// DPP lane moves inside rows of 16 lanes (float bits).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Max / sum over the 16 lanes of a row; every lane of the row gets the result.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_row<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp_row<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp_row<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_row<kDppRowMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_row<kDppQuadSwap1>(x);
+  x += dpp_row<kDppQuadSwap2>(x);
+  x += dpp_row<kDppRowHalfMirror>(x);
+  x += dpp_row<kDppRowMirror>(x);
+  return x;
+}
+
+// Eight 2-bit codes (bits 2e .. 2e+1 of w, e = 0..7) -> eight fp16 values
+// 0..3: y = w | w << 14 puts code 2p+1 beside code 2p in the high half, the
+// pair is or-ed into 1024 + c (0x6400 | c, exact) and 1024 is subtracted.
+__device__ __forceinline__ half8 codes_to_f16(uint32_t w) {
+  const uint32_t y = w | (w << 14);
+  const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  half8 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t x = ((y >> (4 * p)) & 0x00030003u) | 0x64006400u;
+    const half2v v = __builtin_bit_cast(half2v, x) - k1024;
+    r[2 * p] = v[0];
+    r[2 * p + 1] = v[1];
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- q . C table
+// qc[h][e][c][j] = q_j . C_c^(e) for Queries j < nqp (zero past nq). One wave
+// per 16 centroids x 16 Queries, K = 128 in four bf16 MFMAs.
+__global__ __launch_bounds__(64) void qc_kernel(const uint16_t* q, int64_t nq, int nqp, const uint16_t* Cbase,
+                                                int64_t epoch_C_stride, int H, int m, float* qc) {
+  const int lane = threadIdx.x, i = lane & 15, kg = lane >> 4;
+  const int qb = blockIdx.x, cb = blockIdx.y;
+  const int h = blockIdx.z % H, e = blockIdx.z / H;
+  const int c = 16 * cb + i;
+  const uint16_t* Crow = Cbase + (size_t)e * epoch_C_stride + ((size_t)h * m + (c < m ? c : m - 1)) * 128;
+  const int64_t qi = 16 * qb + i;
+  const bool qv = qi < nq;
+  const uint16_t* qrow = q + ((size_t)h * nq + (qv ? qi : 0)) * 128;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint4 aw = *reinterpret_cast<const uint4*>(Crow + 32 * ks + 8 * kg);
+    uint4 bw = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * kg);
+    if (!qv) bw = make_uint4(0u, 0u, 0u, 0u);
+    acc = mfma_bf16(__builtin_bit_cast(bf16x8, aw), __builtin_bit_cast(bf16x8, bw), acc);
+  }
+  // D[row = centroid 4kg + v][col = Query i]
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int cr = 16 * cb + 4 * kg + v;
+    if (cr < m) qc[(((size_t)h * (gridDim.z / H) + e) * m + cr) * nqp + 16 * qb + i] = acc[v];
+  }
+}
+
+struct TileInfo {
+  int ep;      // epoch slot
+  int tstart;  // first cache position of the tile
+  int tcount;  // tokens in the tile (1..64)
+};
+
+__device__ __forceinline__ TileInfo tile_info(const AttnPlan& p, int tile) {
+  int sg = 0;
+  while (p.tile_prefix[sg + 1] <= tile) ++sg;
+  TileInfo ti;
+  ti.ep = p.seg_epoch[sg];
+  ti.tstart = p.seg_start[sg] + (tile - p.tile_prefix[sg]) * kTileKV;
+  const int tend = p.seg_start[sg] + p.seg_len[sg];
+  ti.tcount = (tend - ti.tstart) < kTileKV ? (tend - ti.tstart) : kTileKV;
+  return ti;
+}
+
+// ---------------------------------------------------------------- decode kernel
+// Raw words of one tile. Lane = token for the K words (staged in LDS); lane
+// (kg, j) for the V words of tokens 16tb + j: in channel pass P (channels
+// 64P .. 64P+63) the lane dequantizes channels 16(kg&1) .. +15 of group
+// 2P + (kg>>1).
+struct DecRaw {
+  uint4 k0, k1, kp, c0, c1;
+  uint32_t id;
+  uint32_t vc[4][2];  // [tb][pass] 16 codes
+  uint32_t vp[4][2];  // [tb][pass] zero-point | step << 16
+};
+
+template <int NQ>
+__global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const AttnPlan p) {
+  static_assert(NQ == 16, "one 16-Query block per wave");
+  constexpr int D = 128, NG = 4;
+  // vhat^T of one 64-channel pass, fp16 hi and lo planes: [channel][token
+  // slot], rows of 72 halves (16-byte aligned; 16 consecutive rows hit
+  // distinct banks), every 16-channel block skewed by 64 bytes so the four
+  // blocks written together hit different banks.
+  constexpr int VROW = 72;
+  constexpr int VPL = 64 * VROW + 4 * 32;  // halves of one plane
+  constexpr int PROW = 80;                 // P [Query][token slot] fp16
+  __shared__ __attribute__((aligned(16))) _Float16 vt[2 * VPL];
+  __shared__ __attribute__((aligned(16))) _Float16 pt[NQ * PROW];
+  __shared__ __attribute__((aligned(16))) uint32_t kst[kTileKV * 8];  // K codes [token][kg][group] u16
+  __shared__ __attribute__((aligned(16))) uint32_t kpr[kTileKV * 4];  // K params [token][group]
+  __shared__ __attribute__((aligned(16))) uint32_t cst[kTileKV * 8];  // PSAC coefficients [token][16]
+  auto vrow_off = [](int cl) { return cl * VROW + 32 * (cl >> 4); };  // local channel 0..63
+
+  const int lane = threadIdx.x, j = lane & 15, kg = lane >> 4;
+  const int h = blockIdx.z, split = blockIdx.y;
+  const int64_t q0 = (int64_t)blockIdx.x * NQ;
+  // the softmax runs in the log2 domain with a positive factor; a negative
+  // scale is carried by negated Queries (exact) and a negated q . C table
+  const float qsign = (a.scale_log2 < 0.0f) ? -1.0f : 1.0f;
+  const float cl2 = a.scale_log2 * qsign;
+
+  const int T = p.tile_prefix[p.n_seg];
+  const int tlo = (int)(((int64_t)T * split) / a.splits);
+  const int thi = (int)(((int64_t)T * (split + 1)) / a.splits);
+
+  // per-head bases; per-token offsets fit 32 bits (capacity <= 2^26)
+  const uint8_t* kcode_h = a.cache.kcode + (size_t)h * a.cache.capP * (D / 4);
+  const uint8_t* vcode_h = a.cache.vcode + (size_t)h * a.cache.capP * (D / 4);
+  const uint32_t* kparam_h = a.cache.kparam + (size_t)h * a.cache.capP * NG;
+  const uint32_t* vparam_h = a.cache.vparam + (size_t)h * a.cache.capP * NG;
+  const uint8_t* ids_h = a.cache.ids + (size_t)h * a.cache.capP;
+  const uint16_t* coef_h = a.cache.coef + (size_t)h * a.cache.capP * a.r;
+  const float* qc_h = a.qc + (size_t)h * a.E * a.m * a.nqp;
+
+  // ---- Query operands (fp16, exact for bf16 inputs): qa[G] holds Query
+  // q0 + j, channels 32G + 8kg .. +7; qsum[G] = sum of the Query over group G
+  half8 qa[NG];
+  float qsum[NG];
+  {
+    const int64_t qi = q0 + j;
+    const bool qv = qi < a.nq;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)h * a.nq + (qv ? qi : 0)) * D;
+#pragma unroll
+    for (int G = 0; G < NG; ++G) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * G + 8 * kg);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      float s = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = qv ? qsign * __uint_as_float(ww[k] << 16) : 0.0f;
+        const float x1 = qv ? qsign * __uint_as_float(ww[k] & 0xFFFF0000u) : 0.0f;
+        qa[G][2 * k] = (_Float16)x0;
+        qa[G][2 * k + 1] = (_Float16)x1;
+        s += x0;
+        s += x1;
+      }
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      qsum[G] = s;
+    }
+  }
+  // [qsum_hi | qsum_lo] operand of the zero-point MFMA
+  half8 ax2;
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    const _Float16 hi = (_Float16)qsum[G];
+    const _Float16 lo = (_Float16)(qsum[G] - (float)hi);
+    ax2[G] = (kg == 0) ? hi : (kg == 1) ? lo : (_Float16)0.0f;
+    ax2[G + 4] = (_Float16)0.0f;
+  }
+  half8 ax1;  // [qU_hi | qU_lo] of the current epoch
+  int cur_ep = -2;
+
+  floatx4 O[D / 16];  // o[Query 4kg + v][channel 16cb + j]
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int cb = 0; cb < D / 16; ++cb) O[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    mrow[v] = -__builtin_inff();
+    lrow[v] = 0.0f;
+  }
+  const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  uint32_t cmask[8];  // wave-uniform: word s2 holds coefficients 2s2, 2s2+1
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) cmask[s2] = (2 * s2 < a.r) ? 0xFFFFFFFFu : 0u;
+
+  // Token indices are clamped into the tile, so every load is unconditional.
+  auto load_raw = [&](DecRaw& r, const TileInfo& ti) {
+    const uint32_t t = (uint32_t)ti.tstart + (uint32_t)(lane < ti.tcount ? lane : ti.tcount - 1);
+    r.id = ids_h[t];
+    const uint4* kc = reinterpret_cast<const uint4*>(kcode_h + t * (D / 4));
+    r.k0 = kc[0];
+    r.k1 = kc[1];
+    r.kp = *reinterpret_cast<const uint4*>(kparam_h + t * NG);
+    // r is even: 4-byte aligned rows; halves past r are dropped when staged
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(coef_h + t * (uint32_t)a.r);
+    r.c0 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    r.c1 = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int tt = 16 * tb + j;
+      const uint32_t tv = (uint32_t)ti.tstart + (uint32_t)(tt < ti.tcount ? tt : ti.tcount - 1);
+#pragma unroll
+      for (int P = 0; P < 2; ++P) {
+        const int g = 2 * P + (kg >> 1);
+        r.vc[tb][P] = *reinterpret_cast<const uint32_t*>(vcode_h + tv * (D / 4) + 8 * g + 4 * (kg & 1));
+        r.vp[tb][P] = vparam_h[tv * NG + g];
+      }
+    }
+  };
+  // q . C of the lane's 4 Queries (4kg .. +3) and token 16tb + j
+  auto load_qc = [&](floatx4 (&dst)[4], const TileInfo& ti, uint32_t id_lane) {
+    const float* base = qc_h + (size_t)ti.ep * a.m * a.nqp + q0 + 4 * kg;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const uint32_t id = (uint32_t)__shfl((int)id_lane, 16 * tb + j);
+      const float4 x = *reinterpret_cast<const float4*>(base + id * (uint32_t)a.nqp);
+      dst[tb] = floatx4{x.x, x.y, x.z, x.w};
+    }
+  };
+  // Values of one channel pass: 16 channels of 4 tokens -> hi and lo planes,
+  // token slot 4j + tb (hi = fp16(zp + code * step), lo = fp16(rest))
+  auto dequant_v = [&](const uint32_t (&vc)[4], const uint32_t (&vp)[4]) {
+    float zp[4], st[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      zp[tb] = half_bits_to_float(vp[tb] & 0xFFFFu);
+      st[tb] = half_bits_to_float(vp[tb] >> 16);
+    }
+    const int clb = 32 * (kg >> 1) + 16 * (kg & 1);  // first local channel
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // channels clb + k + 4b (b = 0..3) sit in byte b after the shift
+      uint32_t sp[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) sp[tb] = (vc[tb] >> (2 * k)) & 0x03030303u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float x[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const float c = (float)((sp[tb] >> (8 * b)) & 0xFFu);  // v_cvt_f32_ubyte<b>
+          x[tb] = __builtin_fmaf(c, st[tb], zp[tb]);
+        }
+        const half2v h0 = pk_f16(x[0], x[1]), h1 = pk_f16(x[2], x[3]);
+        const half2v l0 = pk_f16(__builtin_fmaf((float)h0[0], -1.0f, x[0]), __builtin_fmaf((float)h0[1], -1.0f, x[1]));
+        const half2v l1 = pk_f16(__builtin_fmaf((float)h1[0], -1.0f, x[2]), __builtin_fmaf((float)h1[1], -1.0f, x[3]));
+        const int off = vrow_off(clb + k + 4 * b) + 4 * j;
+        *reinterpret_cast<half4*>(vt + off) = half4{h0[0], h0[1], h1[0], h1[1]};
+        *reinterpret_cast<half4*>(vt + VPL + off) = half4{l0[0], l0[1], l1[0], l1[1]};
+      }
+    }
+  };
+  // o += P vhat for the 64 channels of pass P (hi and lo planes)
+  auto pv_pass = [&](int P) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const half8 pa = *reinterpret_cast<const half8*>(pt + j * PROW + 32 * ks + 8 * kg);
+#pragma unroll
+      for (int cbl = 0; cbl < 4; ++cbl) {
+        const int off = vrow_off(16 * cbl + j) + 32 * ks + 8 * kg;
+        const half8 vh = *reinterpret_cast<const half8*>(vt + off);
+        const half8 vl = *reinterpret_cast<const half8*>(vt + VPL + off);
+        O[4 * P + cbl] = mfma_f16(pa, vh, O[4 * P + cbl]);
+        O[4 * P + cbl] = mfma_f16(pa, vl, O[4 * P + cbl]);
+      }
+    }
+  };
+
+  // One tile: `cur` holds its raw words, `nxt` those of the next tile (in
+  // flight); `cur` is refilled with the tile after next once consumed.
+  auto process = [&](int tile, DecRaw& cur, DecRaw& nxt, floatx4 (&qcc)[4], floatx4 (&qcn)[4]) {
+    const TileInfo ti = tile_info(p, tile);
+    // ---- stage the K words: codes permuted to [token][kg][group] so a lane
+    // reads the 4 groups of its channel octet in one 8-byte read
+    {
+      const uint32_t ow[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
+      uint32_t nw[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          // octet d of groups 2s and 2s+1 (u16 index 4G + d of the row)
+          const uint32_t lo = ow[4 * s + d / 2], hi = ow[4 * s + 2 + d / 2];
+          nw[2 * d + s] = __builtin_amdgcn_perm(hi, lo, (d & 1) ? 0x07060302u : 0x05040100u);
+        }
+      uint4* ks4 = reinterpret_cast<uint4*>(kst + lane * 8);
+      ks4[0] = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+      ks4[1] = make_uint4(nw[4], nw[5], nw[6], nw[7]);
+      *reinterpret_cast<uint4*>(kpr + lane * 4) = cur.kp;
+      uint4* cs4 = reinterpret_cast<uint4*>(cst + lane * 8);
+      cs4[0] = make_uint4(cur.c0.x & cmask[0], cur.c0.y & cmask[1], cur.c0.z & cmask[2], cur.c0.w & cmask[3]);
+      cs4[1] = make_uint4(cur.c1.x & cmask[4], cur.c1.y & cmask[5], cur.c1.z & cmask[6], cur.c1.w & cmask[7]);
+    }
+    uint32_t vc1[4], vp1[4];  // pass 1 words, kept while `cur` is refilled
+    {
+      uint32_t vc0[4], vp0[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        vc0[tb] = cur.vc[tb][0];
+        vp0[tb] = cur.vp[tb][0];
+        vc1[tb] = cur.vc[tb][1];
+        vp1[tb] = cur.vp[tb][1];
+      }
+      dequant_v(vc0, vp0);
+    }
+    if (tile + 2 < thi) load_raw(cur, tile_info(p, tile + 2));
+    if (tile + 1 < thi) load_qc(qcn, tile_info(p, tile + 1), nxt.id);
+    __syncthreads();
+
+    // ---- PSAC Query operand of this epoch: lanes kg < 2 hold qU_hi, kg >= 2 qU_lo
+    if (ti.ep != cur_ep) {
+      cur_ep = ti.ep;
+      const int64_t qi = q0 + j;
+      if (qi < a.nq && a.r > 0) {
+        const float* src = a.qU + (((int64_t)h * a.E + cur_ep) * a.nq + qi) * kRankPad + 8 * (kg & 1);
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const float x = qsign * src[s2];
+          const _Float16 hi = (_Float16)x;
+          ax1[s2] = (kg < 2) ? hi : (_Float16)(x - (float)hi);
+        }
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) ax1[s2] = (_Float16)0.0f;
+      }
+    }
+
+    // ---- logits: D[Query 4kg + v][token 16tb + j]
+    floatx4 S[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int tt = 16 * tb + j;
+      const uint2 cw = *reinterpret_cast<const uint2*>(kst + tt * 8 + 2 * kg);
+      const uint4 kp = *reinterpret_cast<const uint4*>(kpr + tt * 4);
+      const uint4 cf = *reinterpret_cast<const uint4*>(cst + tt * 8 + 4 * (kg & 1));
+      const uint32_t kpw[4] = {kp.x, kp.y, kp.z, kp.w};
+      half8 bzp;
+#pragma unroll
+      for (int G = 0; G < NG; ++G) {
+        bzp[G] = (kg < 2) ? __builtin_bit_cast(_Float16, (uint16_t)(kpw[G] & 0xFFFFu)) : (_Float16)0.0f;
+        bzp[G + 4] = (_Float16)0.0f;
+      }
+      floatx4 acc = mfma_f16(ax1, __builtin_bit_cast(half8, cf), floatx4{0.f, 0.f, 0.f, 0.f});
+      acc = mfma_f16(ax2, bzp, acc);
+      const uint32_t cws[4] = {cw.x & 0xFFFFu, cw.x >> 16, cw.y & 0xFFFFu, cw.y >> 16};
+#pragma unroll
+      for (int G = 0; G < NG; ++G) {
+        const floatx4 dg = mfma_f16(qa[G], codes_to_f16(cws[G]), floatx4{0.f, 0.f, 0.f, 0.f});
+        const float st = half_bits_to_float(kpw[G] >> 16);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(st, dg[v], acc[v]);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += qsign * qcc[tb][v];
+      if (tt >= ti.tcount) acc = floatx4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      S[tb] = acc;
+    }
+
+    // ---- online softmax (log2 domain); the running max is raised only when
+    // a row's max exceeds it by more than 8, so the rescale of O is rare
+    bool raise_any = false;
+    float mnew[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float mx = fmaxf(fmaxf(S[0][v], S[1][v]), fmaxf(S[2][v], S[3][v]));
+      mx = row16_max(mx) * cl2;
+      const bool raise = mx > mrow[v] + 8.0f;
+      mnew[v] = raise ? mx : mrow[v];
+      raise_any |= raise;
+    }
+    if (__builtin_amdgcn_ballot_w64(raise_any)) {  // wave-uniform
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float alpha = (mrow[v] == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(mrow[v] - mnew[v]);
+        mrow[v] = mnew[v];
+        lrow[v] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) O[cb][v] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float nm = (mrow[v] == -__builtin_inff()) ? 0.0f : -mrow[v];
+      float pv[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) pv[tb] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[tb][v], cl2, nm));
+      const half2v p0 = pk_f16(pv[0], pv[1]), p1 = pk_f16(pv[2], pv[3]);
+      float l = lrow[v];
+      l = __builtin_amdgcn_fdot2(p0, one2, l, false);
+      l = __builtin_amdgcn_fdot2(p1, one2, l, false);
+      lrow[v] = l;
+      *reinterpret_cast<half4*>(pt + (4 * kg + v) * PROW + 4 * j) = half4{p0[0], p0[1], p1[0], p1[1]};
+    }
+    __syncthreads();
+    pv_pass(0);
+    __syncthreads();
+    dequant_v(vc1, vp1);
+    __syncthreads();
+    pv_pass(1);
+    __syncthreads();
+  };
+
+  DecRaw ra, rb;
+  floatx4 qa4[4], qb4[4];
+  if (tlo < thi) {
+    const TileInfo t0 = tile_info(p, tlo);
+    load_raw(ra, t0);
+    if (tlo + 1 < thi) load_raw(rb, tile_info(p, tlo + 1));
+    load_qc(qa4, t0, ra.id);
+  }
+  for (int tile = tlo; tile < thi; tile += 2) {
+    process(tile, ra, rb, qa4, qb4);
+    if (tile + 1 < thi) process(tile + 1, rb, ra, qb4, qa4);
+  }
+
+  // ---- epilogue: row sums over the 16 token lanes; normalized output or a
+  // split partial (o, running max, row sum) for the merge
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float l = row16_sum(lrow[v]);
+    const int64_t qi = q0 + 4 * kg + v;
+    if (qi >= a.nq) continue;
+    if (a.splits == 1) {
+      const float inv = 1.0f / l;
+      float* dst = a.out + ((int64_t)h * a.nq + qi) * D + j;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) dst[16 * cb] = O[cb][v] * inv;
+    } else {
+      const int64_t row = ((int64_t)split * a.H + h) * a.nq + qi;
+      float* dst = a.part_o + row * D + j;
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) dst[16 * cb] = O[cb][v];
+      if (j == 0) {
+        a.part_ml[row * 2] = mrow[v];
+        a.part_ml[row * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qc(const void* q, int64_t nq, int nqp, const void* Cbase, int64_t epoch_C_stride, int H, int m,
+                     int E, float* qc, hipStream_t s) {
+  dim3 grid((unsigned)(nqp / 16), (unsigned)((m + 15) / 16), (unsigned)(H * E)), block(64);
+  hipLaunchKernelGGL(qc_kernel, grid, block, 0, s, reinterpret_cast<const uint16_t*>(q), nq, nqp,
+                     reinterpret_cast<const uint16_t*>(Cbase), epoch_C_stride, H, m, qc);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const AttnPlan& p, hipStream_t s) {
+  dim3 grid((unsigned)((a.nq + kDecodeQ - 1) / kDecodeQ), (unsigned)a.splits, (unsigned)a.H), block(64);
+  hipLaunchKernelGGL(decode_kernel<kDecodeQ>, grid, block, 0, s, a, p);
+  return hipGetLastError();
+}
+
+}  // namespace qwm

@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Layout {
   size_t kcode, vcode, kparam, vparam, ids, coef;
-  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, build_ids, km_perm, km_off, km_woff, qU, part_o, part_ml;
+  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, build_ids, km_perm, km_off, km_woff, qU, qc, part_o, part_ml;
   size_t total;
   int64_t capP, part_rows;
 };
@@ -67,7 +67,11 @@ Layout make_layout(const qwm_desc* d) {
   const int64_t big = 1 << 18;
   int64_t pr = 8 * H * maxq > big ? 8 * H * maxq : big;
   if (pr > 16 * H * maxq) pr = 16 * H * maxq;
+  // decode-shaped calls split the cache more finely (up to 64 ways)
+  const int64_t dq = maxq < qwm::kDecodeMaxQ ? maxq : qwm::kDecodeMaxQ;
+  if (pr < 64 * H * dq) pr = 64 * H * dq;
   L.part_rows = pr;
+  const int64_t nqp_max = (dq + qwm::kDecodeQ - 1) / qwm::kDecodeQ * qwm::kDecodeQ;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -94,6 +98,7 @@ Layout make_layout(const qwm_desc* d) {
   L.km_off = take((size_t)(H * 257 * 4));
   L.km_woff = take((size_t)(H * 257 * 4));
   L.qU = take((size_t)(H * E * maxq * qwm::kRankPad * 4));
+  L.qc = take((size_t)(H * E * m * nqp_max * 4));
   L.part_o = take((size_t)(pr * D * 4));
   L.part_ml = take((size_t)(pr * 2 * 4));
   L.total = off;
@@ -163,6 +168,7 @@ struct qwm_cache {
   int32_t* km_off() const { return reinterpret_cast<int32_t*>(arena + L.km_off); }
   int32_t* km_woff() const { return reinterpret_cast<int32_t*>(arena + L.km_woff); }
   float* qU() const { return reinterpret_cast<float*>(arena + L.qU); }
+  float* qc() const { return reinterpret_cast<float*>(arena + L.qc); }
   float* part_o() const { return reinterpret_cast<float*>(arena + L.part_o); }
   float* part_ml() const { return reinterpret_cast<float*>(arena + L.part_ml); }
 
@@ -295,6 +301,61 @@ int choose_splits(const qwm_cache* c, int64_t n_q, int T) {
     }
   }
   return (int)splits;
+}
+
+// The decode path of qwm_attend: q . U_r and q . C tables, then the decode
+// kernel over splits of the tiles and the log-sum-exp merge.
+qwm_status attend_decode(qwm_cache* c, const void* q, int64_t n_q, float softmax_scale, float* out,
+                         const qwm::AttnPlan& p) {
+  const int T = p.tile_prefix[p.n_seg];
+  const int E = (int)c->epoch_start.size();
+  const int64_t qtiles = (n_q + qwm::kDecodeQ - 1) / qwm::kDecodeQ;
+  const int nqp = (int)(qtiles * qwm::kDecodeQ);
+  // about 8 single-wave workgroups per CU, at least 4 tiles per split
+  int64_t splits = (8 * (int64_t)c->ncu + qtiles * c->H - 1) / (qtiles * c->H);
+  const int64_t cap = T / 4 > 1 ? T / 4 : 1;
+  if (splits > cap) splits = cap;
+  if (splits > 64) splits = 64;
+  while (splits > 1 && splits * c->H * n_q > c->L.part_rows) --splits;
+  qwm::DecodeArgs d{};
+  d.q = q;
+  d.qc = c->qc();
+  d.qU = c->qU();
+  d.cache = c->view;
+  d.nq = n_q;
+  d.nqp = nqp;
+  d.H = c->H;
+  d.m = c->m;
+  d.r = c->r;
+  d.E = E;
+  d.scale_log2 = softmax_scale * 1.4426950408889634f;
+  d.splits = (int)splits;
+  d.out = out;
+  d.part_o = c->part_o();
+  d.part_ml = c->part_ml();
+  hipError_t e = hipSuccess;
+  if (c->r > 0) {
+    e = c->run(QWM_K_QU, [&] {
+      return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
+                            c->stream);
+    });
+    if (e != hipSuccess) return fail_hip(e, "qU");
+  }
+  e = c->run(QWM_K_QU, [&] {
+    return qwm::launch_qc(q, n_q, nqp, c->slotC(0), (int64_t)c->H * c->m * c->D, c->H, c->m, E, c->qc(), c->stream);
+  });
+  if (e != hipSuccess) return fail_hip(e, "qC");
+  e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_decode(d, p, c->stream); });
+  if (e != hipSuccess) return fail_hip(e, "decode");
+  if (splits > 1) {
+    qwm::AttnArgs a = base_args(c);
+    a.nq = n_q;
+    a.splits = (int)splits;
+    a.out = out;
+    e = c->run(QWM_K_MERGE, [&] { return qwm::launch_merge(c->D, a, c->stream); });
+    if (e != hipSuccess) return fail_hip(e, "merge");
+  }
+  return QWM_OK;
 }
 
 }  // namespace
@@ -608,6 +669,10 @@ qwm_status qwm_attend(qwm_cache* c, const void* q, int64_t n_q, const void* k_se
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.n_epoch_slots = E;
   a.out = out;
+  // Few Queries over bf16 Keys: the decode kernel (2-bit codes as the MFMA
+  // operand, one wave per workgroup, many splits)
+  if (c->dtype == QWM_BF16 && c->D == 128 && mask == QWM_SELF_NONE && n_q <= qwm::kDecodeMaxQ && (c->r % 2) == 0)
+    return attend_decode(c, q, n_q, softmax_scale, out, p);
   a.splits = choose_splits(c, n_q, T);
   hipError_t e = hipSuccess;
   if (c->r > 0) {  // the kernels read no qU at rank 0

@@ -128,6 +128,29 @@ hipError_t launch_merge(int D, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attend_top1(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_top1_merge(const AttnArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- decode
+// Few Queries per head (bf16, head_dim 128, no self segment): the Key side
+// runs on the 2-bit codes with a q . C table; one wave per workgroup.
+struct DecodeArgs {
+  const void* q;      // [H][nq][128] bf16
+  const float* qc;    // [H][E][m][nqp] float: q . C_c of every epoch
+  const float* qU;    // [H][E][nq][16] float
+  CacheView cache;
+  int64_t nq;
+  int nqp;            // row length of qc (multiple of 16, >= nq)
+  int H, m, r, E;
+  float scale_log2;   // softmax_scale * log2(e)
+  int splits;
+  float* out;         // [H][nq][128] (splits == 1)
+  float* part_o;      // [splits][H][nq][128]
+  float* part_ml;     // [splits][H][nq][2]
+};
+hipError_t launch_qc(const void* q, int64_t nq, int nqp, const void* Cbase, int64_t epoch_C_stride, int H, int m,
+                     int E, float* qc, hipStream_t s);
+constexpr int kDecodeQ = 16;        // Queries per decode workgroup
+constexpr int kDecodeMaxQ = 64;     // largest n_q served by the decode kernel
+hipError_t launch_decode(const DecodeArgs& a, const AttnPlan& p, hipStream_t s);
+
 // ---------------------------------------------------------------- export
 struct ExportArgs {
   CacheView cache;
