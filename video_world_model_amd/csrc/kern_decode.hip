@@ -140,6 +140,15 @@ struct DecRaw {
   uint32_t vp[4][2];  // [tb][pass] zero-point | step << 16
 };
 
+// The workgroup is one wave: LDS accesses of a wave execute in program order,
+// so a fence for the compiler is the only synchronization the tile stages
+// need (no wait for the loads in flight).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int NQ>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const AttnPlan p) {
   static_assert(NQ == 16, "one 16-Query block per wave");
@@ -352,9 +361,11 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
       }
       dequant_v(vc0, vp0);
     }
-    if (tile + 2 < thi) load_raw(cur, tile_info(p, tile + 2));
-    if (tile + 1 < thi) load_qc(qcn, tile_info(p, tile + 1), nxt.id);
-    __syncthreads();
+    // Prefetch without branches (indices clamped to the last tile): a load on
+    // one path only would make the next wait cover every load in flight.
+    load_raw(cur, tile_info(p, tile + 2 < thi ? tile + 2 : thi - 1));
+    load_qc(qcn, tile_info(p, tile + 1 < thi ? tile + 1 : thi - 1), nxt.id);
+    wave_sync();
 
     // ---- PSAC Query operand of this epoch: lanes kg < 2 hold qU_hi, kg >= 2 qU_lo
     if (ti.ep != cur_ep) {
@@ -440,26 +451,28 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
       lrow[v] = l;
       *reinterpret_cast<half4*>(pt + (4 * kg + v) * PROW + 4 * j) = half4{p0[0], p0[1], p1[0], p1[1]};
     }
-    __syncthreads();
+    wave_sync();
     pv_pass(0);
-    __syncthreads();
+    wave_sync();
     dequant_v(vc1, vp1);
-    __syncthreads();
+    wave_sync();
     pv_pass(1);
-    __syncthreads();
+    wave_sync();
   };
 
   DecRaw ra, rb;
   floatx4 qa4[4], qb4[4];
+  int tile = tlo;
   if (tlo < thi) {
     const TileInfo t0 = tile_info(p, tlo);
     load_raw(ra, t0);
-    if (tlo + 1 < thi) load_raw(rb, tile_info(p, tlo + 1));
+    load_raw(rb, tile_info(p, tlo + 1 < thi ? tlo + 1 : thi - 1));
     load_qc(qa4, t0, ra.id);
-  }
-  for (int tile = tlo; tile < thi; tile += 2) {
-    process(tile, ra, rb, qa4, qb4);
-    if (tile + 1 < thi) process(tile + 1, rb, ra, qb4, qa4);
+    for (; tile + 1 < thi; tile += 2) {
+      process(tile, ra, rb, qa4, qb4);
+      process(tile + 1, rb, ra, qb4, qa4);
+    }
+    if (tile < thi) process(tile, ra, rb, qa4, qb4);
   }
 
   // ---- epilogue: row sums over the 16 token lanes; normalized output or a
