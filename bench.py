@@ -154,12 +154,109 @@ def cpu_baseline(w: W.Workload, n_heads: int, objective: str, r: int):
 
 # ----------------------------------------------------------------- GPU
 
+def bench_long_horizon(args, w):
+    """Attention over the long-horizon cache (built once per epoch from the
+    epoch's historical Queries and first frame, untimed): a step is one
+    qwm_attend of n_q Queries per head, no self segment."""
+    import torch
+    from video_world_model_amd import Cache
+    nq = args.nq or w.n_q
+    torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib * (1 << 18), dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    gens = [W.HeadGen(w, h) for h in range(w.heads)]
+
+    def dev(arrs):
+        x = np.ascontiguousarray(np.stack(arrs))
+        return torch.from_numpy(W.bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        cache = Cache(w.heads, w.head_dim, w.n_centroids, w.rank, w.n_kv, dtype=torch.bfloat16,
+                      max_epochs=w.n_epochs, max_query_tokens=max(nq, 16), max_build_tokens=w.frame_tokens)
+        for e in range(w.n_epochs):
+            s0, s1 = w.epoch_start(e), w.epoch_end(e)
+            a0, a1 = w.centroid_keys_range(e)
+            cache.build_subspace(dev([g.hist_queries(e) for g in gens]))
+            cache.build_centroids(dev([g.keys(a0, a1) for g in gens]), w.kmeans_iters)
+            cache.quantize_append(dev([g.keys(s0, s1) for g in gens]), dev([g.values(s0, s1) for g in gens]))
+            torch.cuda.synchronize()
+        q = dev([g.queries(W.Q_CURRENT, nq) for g in gens])
+        out = torch.empty((w.heads, nq, w.head_dim), dtype=torch.float32, device="cuda")
+        for _ in range(args.warmup):
+            cache.attend(q, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            cache.attend(q, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    with torch.cuda.stream(stream):
+        cache.profile_enable(True)
+        for _ in range(args.steps):
+            cache.attend(q, out=out)
+    torch.cuda.synchronize()
+    kern = {}
+    for k in KERNELS:
+        ms, n = cache.profile_read(k)
+        if n:
+            kern[k] = dict(ms_per_step=ms / args.steps, launches_per_step=n / args.steps, avg_launch_ms=ms / n)
+    cache.profile_enable(False)
+    B = bytes_per_token_head(w.head_dim, w.group, w.rank)
+    attend_bytes = w.heads * (w.n_kv * B + nq * w.head_dim * 2 + nq * w.head_dim * 4)
+    attend_flops = w.heads * nq * w.n_kv * (4 * w.head_dim + 2 * w.rank)
+    ta = kern["attend"]["avg_launch_ms"] * 1e-3
+    decode = nq <= 64
+    if decode:
+        achieved = attend_bytes / ta / 1e9
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS)
+    else:
+        achieved = attend_flops / ta / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / MFMA_F16_PEAK_TFLOPS)
+    roof["kernel"] = "decode" if decode else "attend"
+    roof["traffic"] = None
+    rec = {
+        "metric": METRIC,
+        "value": w.heads * w.n_kv / (ms_step * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32-valu+f16-mfma",
+        "data": "synthetic",
+        "config": {"workload": w.name, "step": "attend", "heads": w.heads, "head_dim": w.head_dim,
+                   "n_centroids": w.n_centroids, "rank": w.rank, "n_kv": w.n_kv, "n_q": nq, "epochs": w.n_epochs,
+                   "input_dtype": w.dtype},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "kernels": kern,
+        "phases": {"attend": dict(GBps=attend_bytes / ta / 1e9, hbm_frac=attend_bytes / ta / 1e9 / HBM_PEAK_GBPS,
+                                  ms=ta * 1e3, pair_per_s=w.heads * nq * w.n_kv / (ms_step * 1e-3))},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video_chunk", choices=["tiny", "video_chunk", "wm_layer"])
+    ap.add_argument("--workload", default="video_chunk", choices=["tiny", "video_chunk", "wm_layer", "long_horizon"],
+                    help="long_horizon: the 131,072-token, 11-epoch cache is built once (untimed) and a step is "
+                         "one attention of --nq Queries per head over it (decode-shaped when --nq <= 64)")
+    ap.add_argument("--nq", type=int, default=0, help="Queries per head for long_horizon (default: the workload's)")
     ap.add_argument("--mode", default="quantwm", choices=sorted(MODES))
     ap.add_argument("--graph", type=int, default=0,
                     help="1: capture one step in a HIP graph (through torch.cuda.graph) and time its replays; "
@@ -175,6 +272,8 @@ def main():
         sys.exit(2)
 
     w = W.workload(args.workload)
+    if w.name == "long_horizon":
+        return bench_long_horizon(args, w)
     objective, psac = MODES[args.mode]
     r = w.rank if psac else 0
     needs_queries = psac or objective == "qsac"  # QVG uses no historical Queries
