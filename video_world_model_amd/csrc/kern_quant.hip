@@ -365,14 +365,12 @@ __global__ void seed_kernel(const void* keys, int64_t n, int m, void* C, float* 
 // k-means update: one block of 16 waves per (centroid, head). Wave w owns the
 // contiguous token range [w*span, (w+1)*span) (span = n/16 rounded up to a
 // multiple of 64); each lane reads a contiguous run of at most 16 ids per
-// round (one 16-byte load when the run is full), so a wave prefix sum over the
-// per-lane match counts lists the centroid's members in token order in LDS.
-// Member Key rows are fetched 8 at a time (each row by the whole wave) and
-// added into float64 lane accumulators; the 16 wave sums are then added in
-// wave order.
-// The mean is rounded once to the cache dtype; a centroid without members
-// keeps its value. The order of every addition is fixed, so repeated runs
-// give the same bits.
+// round, so a wave prefix sum over the per-lane match counts lists the
+// centroid's members in token order in LDS. Member Key rows are fetched 8 at a
+// time (each row by the whole wave) and added into float64 lane accumulators;
+// the 16 wave sums are then added in wave order. The mean is rounded once to
+// the cache dtype; a centroid without members keeps its value. The order of
+// every addition is fixed, so repeated runs give the same bits.
 constexpr int kUpdWaves = 16;
 constexpr int kUpdLane = 16;  // ids per lane per round
 
@@ -405,17 +403,9 @@ __global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys
   for (int64_t base = w0; base < w1; base += round_len) {
     const int64_t t0 = base + (int64_t)per_lane * lane;
     uint32_t match = 0;
-    if (per_lane == kUpdLane && (n & 15) == 0 && t0 + kUpdLane <= w1) {  // a full, 16-byte aligned run
-      const uint4 q = *reinterpret_cast<const uint4*>(idh + t0);
-      const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-      for (int b = 0; b < kUpdLane; ++b)
-        if (((qw[b >> 2] >> (8 * (b & 3))) & 0xFFu) == (uint32_t)c) match |= 1u << b;
-    } else {
-#pragma unroll
-      for (int b = 0; b < kUpdLane; ++b)
-        if (b < per_lane && t0 + b < w1 && idh[t0 + b] == (uint8_t)c) match |= 1u << b;
-    }
+    for (int b = 0; b < kUpdLane; ++b)
+      if (b < per_lane && t0 + b < w1 && idh[t0 + b] == (uint8_t)c) match |= 1u << b;
     const int mc = __popc(match);
     int incl = mc;
 #pragma unroll
