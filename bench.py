@@ -154,6 +154,165 @@ def cpu_baseline(w: W.Workload, n_heads: int, objective: str, r: int):
 
 # ----------------------------------------------------------------- GPU
 
+def _build_epochs(cache, w, gens, dev, n_tokens):
+    """Cache of the first n_tokens stream tokens, epoch by epoch, calibrated on
+    the GPU from each epoch's historical Queries and first frame."""
+    import torch
+    for e in range(w.n_epochs):
+        s0, s1 = w.epoch_start(e), min(w.epoch_end(e), n_tokens)
+        if s1 <= s0:
+            break
+        a0, a1 = w.centroid_keys_range(e)
+        cache.build_subspace(dev([g.hist_queries(e) for g in gens]))
+        cache.build_centroids(dev([g.keys(a0, a1) for g in gens]), w.kmeans_iters)
+        cache.quantize_append(dev([g.keys(s0, s1) for g in gens]), dev([g.values(s0, s1) for g in gens]))
+        torch.cuda.synchronize()
+
+
+def _bf16_dev(x_list):
+    import torch
+    x = np.ascontiguousarray(np.stack(x_list))
+    return torch.from_numpy(W.bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _kernel_times(cache, steps):
+    kern = {}
+    for k in KERNELS:
+        ms, n = cache.profile_read(k)
+        if n:
+            kern[k] = dict(ms_per_step=ms / steps, launches_per_step=n / steps, avg_launch_ms=ms / n)
+    return kern
+
+
+def bench_streaming(args, w):
+    """The streaming-insert step on the 100,000-token cache (built once,
+    untimed): quantize-append one 1,560-token frame, then attention of a
+    1,560-Query chunk over all 101,560 tokens. The calibration refresh (every
+    8 frames: subspace from the last 8 frames' 12,480 Queries, 10-iteration
+    centroid build on the refresh frame) is timed on its own and reported per
+    refresh and per frame."""
+    import torch
+    from video_world_model_amd import Cache
+    torch.cuda.set_device(0)
+    gens = [W.HeadGen(w, h) for h in range(w.heads)]
+    base = w.n_kv - w.n_append
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        cache = Cache(w.heads, w.head_dim, w.n_centroids, w.rank, w.n_kv, dtype=torch.bfloat16,
+                      max_epochs=w.n_epochs, max_query_tokens=w.n_q, max_build_tokens=w.frame_tokens)
+        _build_epochs(cache, w, gens, _bf16_dev, base)
+        kf = _bf16_dev([g.keys(base, w.n_kv) for g in gens])
+        vf = _bf16_dev([g.values(base, w.n_kv) for g in gens])
+        q = _bf16_dev([g.current_queries() for g in gens])
+        e_last = w.n_epochs - 1
+        qh = _bf16_dev([g.hist_queries(e_last) for g in gens])
+        a0, a1 = w.centroid_keys_range(e_last)
+        kref = _bf16_dev([g.keys(a0, a1) for g in gens])
+        out = torch.empty((w.heads, w.n_q, w.head_dim), dtype=torch.float32, device="cuda")
+
+    def step():
+        cache.truncate(base)
+        cache.quantize_append(kf, vf)
+        cache.attend(q, out=out)
+
+    refresh_at = w.epoch_start(e_last)  # the last refresh point: an epoch boundary
+
+    def refresh():
+        # rewind to the boundary (the epoch there keeps no token and is replaced)
+        cache.truncate(refresh_at)
+        cache.build_subspace(qh)
+        cache.build_centroids(kref, w.kmeans_iters)
+
+    def timed(fn, steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(steps):
+                fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            refresh()
+        cache.truncate(refresh_at)
+    torch.cuda.synchronize()
+    ms_refresh = timed(refresh, max(1, args.steps // 4))
+    # back to the 100,000-token cache: the last epoch rebuilt the same way
+    with torch.cuda.stream(stream):
+        cache.truncate(refresh_at)
+        cache.quantize_append(_bf16_dev([g.keys(refresh_at, base) for g in gens]),
+                              _bf16_dev([g.values(refresh_at, base) for g in gens]))
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+    with torch.cuda.stream(stream):
+        cache.profile_enable(True)
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    kern = _kernel_times(cache, args.steps)
+    cache.profile_enable(False)
+    with torch.cuda.stream(stream):
+        cache.profile_enable(True)
+        for _ in range(max(1, args.steps // 4)):
+            refresh()
+    torch.cuda.synchronize()
+    kref_t = _kernel_times(cache, max(1, args.steps // 4))
+    cache.profile_enable(False)
+
+    B = bytes_per_token_head(w.head_dim, w.group, w.rank)
+    tq = kern["quantize"]["avg_launch_ms"] * 1e-3
+    ta = sum(kern[k]["ms_per_step"] for k in ("qu", "attend", "merge") if k in kern) * 1e-3
+    ta_k = kern["attend"]["avg_launch_ms"] * 1e-3
+    q_bytes = w.heads * w.n_append * (2 * w.head_dim * 2 + B)
+    q_ops = w.heads * w.n_append * 3 * w.n_centroids * w.head_dim
+    a_flops = w.heads * w.n_q * w.n_kv * (4 * w.head_dim + 2 * w.rank)
+    a_bytes = w.heads * (w.n_kv * B + w.n_q * w.head_dim * 2 + w.n_q * w.head_dim * 4)
+    dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
+    if dom == "attend":
+        achieved = a_flops / ta_k / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / MFMA_F16_PEAK_TFLOPS, kernel="attend", traffic=None)
+    else:
+        achieved = q_ops / tq / 1e12
+        roof = dict(bound="alu", achieved=achieved, peak=QSAC_OPS_PEAK / 1e12, unit="Top/s",
+                    frac=achieved * 1e12 / QSAC_OPS_PEAK, kernel=dom, traffic=None)
+    rec = {
+        "metric": METRIC,
+        "value": w.heads * w.n_kv / (ms_step * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32-valu+f16-mfma",
+        "data": "synthetic",
+        "config": {"workload": w.name, "step": "append 1 frame + attend", "heads": w.heads,
+                   "head_dim": w.head_dim, "n_centroids": w.n_centroids, "rank": w.rank, "n_kv": w.n_kv,
+                   "n_append": w.n_append, "n_q": w.n_q, "epochs": w.n_epochs, "input_dtype": w.dtype},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "kernels": kern,
+        "phases": {
+            "quantize": dict(ms=tq * 1e3, GBps=q_bytes / tq / 1e9, hbm_frac=q_bytes / tq / 1e9 / HBM_PEAK_GBPS,
+                             alu_frac=q_ops / tq / QSAC_OPS_PEAK),
+            "attend": dict(ms=ta * 1e3, kv_tokens_per_s=w.heads * w.n_kv / ta,
+                           mfma_frac=a_flops / ta_k / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                           hbm_frac=a_bytes / ta_k / 1e9 / HBM_PEAK_GBPS),
+            "refresh": dict(ms=ms_refresh, ms_per_frame=ms_refresh / (w.epoch_tokens // w.frame_tokens),
+                            kernels=kref_t),
+        },
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_long_horizon(args, w):
     """Attention over the long-horizon cache (built once per epoch from the
     epoch's historical Queries and first frame, untimed): a step is one
@@ -253,9 +412,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video_chunk", choices=["tiny", "video_chunk", "wm_layer", "long_horizon"],
-                    help="long_horizon: the 131,072-token, 11-epoch cache is built once (untimed) and a step is "
-                         "one attention of --nq Queries per head over it (decode-shaped when --nq <= 64)")
+    ap.add_argument("--workload", default="video_chunk",
+                    choices=["tiny", "video_chunk", "wm_layer", "streaming", "long_horizon"],
+                    help="streaming: the 100,000-token cache is built once (untimed); a step appends one "
+                         "1,560-token frame and attends with 1,560 Queries; the every-8-frames refresh is timed "
+                         "apart. long_horizon: the 131,072-token, 11-epoch cache is built once (untimed) and a "
+                         "step is one attention of --nq Queries per head over it (decode-shaped when --nq <= 64)")
     ap.add_argument("--nq", type=int, default=0, help="Queries per head for long_horizon (default: the workload's)")
     ap.add_argument("--mode", default="quantwm", choices=sorted(MODES))
     ap.add_argument("--graph", type=int, default=0,
@@ -274,6 +436,8 @@ def main():
     w = W.workload(args.workload)
     if w.name == "long_horizon":
         return bench_long_horizon(args, w)
+    if w.name == "streaming":
+        return bench_streaming(args, w)
     objective, psac = MODES[args.mode]
     r = w.rank if psac else 0
     needs_queries = psac or objective == "qsac"  # QVG uses no historical Queries

@@ -206,7 +206,7 @@ def test_determinism():
 
 
 @pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1024, 10), ("video_chunk", 4, 1760, 4),
-                                                     ("wm_layer", 2, 6000, 5)])
+                                                     ("wm_layer", 2, 1560, 4), ("wm_layer", 2, 9000, 4)])
 def test_build_calibration(name, heads, n_keys, iters):
     """GPU-built calibration: S_G bit-exact (exact float64 sums of bf16/fp32
     squares), U_r spans the oracle's subspace (projector within 1e-4), and the

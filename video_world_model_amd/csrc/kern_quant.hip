@@ -362,25 +362,27 @@ __global__ void seed_kernel(const void* keys, int64_t n, int m, void* C, float* 
   C32[di] = load_in<DT>(keys, si);
 }
 
-// k-means update: one block of 16 waves per (centroid, head). Wave w owns the
-// contiguous token range [w*span, (w+1)*span) (span = n/16 rounded up to a
-// multiple of 64); each lane reads a contiguous run of at most 16 ids per
-// round, so a wave prefix sum over the per-lane match counts lists the
-// centroid's members in token order in LDS. Member Key rows are fetched 8 at a
-// time (each row by the whole wave) and added into float64 lane accumulators;
-// the 16 wave sums are then added in wave order. The mean is rounded once to
+// k-means update: one block of NW waves per (centroid, head) (16 for long
+// builds, 2 for short ones, where many centroids each have few members and
+// the block count, not the scan, sets the time). Wave w owns the contiguous
+// token range [w*span, (w+1)*span) (span = n/NW rounded up to a multiple of
+// 64); each lane reads a contiguous run of at most 16 ids per round, so a wave
+// prefix sum over the per-lane match counts lists the centroid's members in
+// token order in LDS. Member Key rows are fetched 8 at a time (each row by the
+// whole wave) and added into float64 lane accumulators; the NW wave sums are
+// then added in wave order. The mean is rounded once to
 // the cache dtype; a centroid without members keeps its value. The order of
 // every addition is fixed, so repeated runs give the same bits.
-constexpr int kUpdWaves = 16;
 constexpr int kUpdLane = 16;  // ids per lane per round
 
-template <int D, int DT>
-__global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys, const uint8_t* ids, int64_t n,
-                                                                int m, void* C, float* C32) {
+template <int D, int DT, int NW>
+__global__ __launch_bounds__(NW * 64) void update_kernel(const void* keys, const uint8_t* ids, int64_t n, int m,
+                                                         void* C, float* C32) {
   constexpr int PER = D / 64;  // channels per lane
-  __shared__ uint16_t list[kUpdWaves][64 * kUpdLane];
-  __shared__ double red[kUpdWaves][D];
-  __shared__ int cnt[kUpdWaves];
+  static_assert(NW * 64 >= D, "one thread per channel in the final sum");
+  __shared__ uint16_t list[NW][64 * kUpdLane];
+  __shared__ double red[NW][D];
+  __shared__ int cnt[NW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = blockIdx.x, h = blockIdx.y;
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys
   const uint16_t* kh16 = reinterpret_cast<const uint16_t*>(keys) + (size_t)h * n * D;
   const float* kh32 = reinterpret_cast<const float*>(keys) + (size_t)h * n * D;
 
-  const int64_t span = ((n + kUpdWaves - 1) / kUpdWaves + 63) / 64 * 64;
+  const int64_t span = ((n + NW - 1) / NW + 63) / 64 * 64;
   const int per_lane = (int)(span / 64 < kUpdLane ? span / 64 : kUpdLane);
   const int64_t round_len = 64 * (int64_t)per_lane;
   const int64_t w0 = (int64_t)wave * span;
@@ -470,7 +472,7 @@ __global__ __launch_bounds__(kUpdWaves * 64) void update_kernel(const void* keys
   int total = 0;
   double sum = 0.0;
 #pragma unroll
-  for (int w = 0; w < kUpdWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     total += cnt[w];
     sum += red[w][j];
   }
@@ -769,15 +771,23 @@ hipError_t launch_kmeans_assign_pruned(int D, int dtype, int obj, const void* ke
 
 hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_t* ids, int64_t n, int H, int m,
                                 void* C, float* C32, hipStream_t s) {
-  dim3 grid((unsigned)m, (unsigned)H), block(kUpdWaves * 64);
-  if (D == 128 && dtype == 0)
-    hipLaunchKernelGGL((update_kernel<128, 0>), grid, block, 0, s, keys, ids, n, m, C, C32);
-  else if (D == 128)
-    hipLaunchKernelGGL((update_kernel<128, 1>), grid, block, 0, s, keys, ids, n, m, C, C32);
-  else if (dtype == 0)
-    hipLaunchKernelGGL((update_kernel<64, 0>), grid, block, 0, s, keys, ids, n, m, C, C32);
-  else
-    hipLaunchKernelGGL((update_kernel<64, 1>), grid, block, 0, s, keys, ids, n, m, C, C32);
+  dim3 grid((unsigned)m, (unsigned)H);
+  const bool small = n <= 4096;  // 2 waves per block
+#define QWM_ULAUNCH(DD, TT)                                                                               \
+  if (small)                                                                                              \
+    hipLaunchKernelGGL((update_kernel<DD, TT, 2>), grid, dim3(128), 0, s, keys, ids, n, m, C, C32);       \
+  else                                                                                                    \
+    hipLaunchKernelGGL((update_kernel<DD, TT, 16>), grid, dim3(1024), 0, s, keys, ids, n, m, C, C32);
+  if (D == 128 && dtype == 0) {
+    QWM_ULAUNCH(128, 0)
+  } else if (D == 128) {
+    QWM_ULAUNCH(128, 1)
+  } else if (dtype == 0) {
+    QWM_ULAUNCH(64, 0)
+  } else {
+    QWM_ULAUNCH(64, 1)
+  }
+#undef QWM_ULAUNCH
   return hipGetLastError();
 }
 

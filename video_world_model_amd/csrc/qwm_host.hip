@@ -507,9 +507,10 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
   });
   if (e != hipSuccess) return fail_hip(e, "kmeans seed");
   for (int it = 0; it < iters; ++it) {
-    // Pruning pays for its grouping pass only with many centroids: below 128
-    // about half the candidates survive and the full pass is as fast.
-    if (it == 0 || c->m < 128) {  // every candidate for every Key
+    // Pruning pays for its grouping pass only with many centroids (below 128
+    // about half the candidates survive) that each hold enough Keys to fill
+    // waves of 64 (a wave serves the Keys of one previous centroid).
+    if (it == 0 || c->m < 128 || n_keys < 32 * (int64_t)c->m) {  // every candidate for every Key
       qwm::QuantArgs a{};
       a.k = keys;
       a.v = nullptr;
