@@ -259,7 +259,44 @@ def nearest_assign32(k: np.ndarray, C: np.ndarray, g: int, chunk: int = 2048) ->
     return out
 
 
-OBJECTIVES = ("qsac", "nearest")
+def postq_objective(k: np.ndarray, C: np.ndarray, S: np.ndarray, g: int) -> np.ndarray:
+    """Sensitivity-weighted error left after the actual INT2 quantization
+    (float32 [N][m]): the "exact post-rounding error" alternative to the
+    range form of the QSAC objective.
+
+    "Step 1" of the article says the nearest centroid is not necessarily the
+    best one once the residual is quantized; instead of the range proxy this
+    variant quantizes the residual r = k - c with the cache's own per-group
+    INT2 (``int2_quantize``, ``int2_dequant``) and scores
+    J = sum_G S_G * E_G, E_G = sum over j in G of (r_j - rhat_j)^2,
+    in float32: per group the running sum E = t_0 + t_1 + ... of
+    t_j = e_j * e_j, e_j = r_j - rhat_j, channels in ascending order; then
+    u_G = S_G * E_G and J = ((u_0 + u_1) + u_2) + ... left to right.
+    """
+    k = np.asarray(k, dtype=F32)
+    C = np.asarray(C, dtype=F32)
+    S = np.asarray(S, dtype=F32)
+    N, d = k.shape
+    m = C.shape[0]
+    nG = d // g
+    J = np.empty((N, m), F32)
+    for c in range(m):
+        r = k - C[c][None, :]
+        codes, zp, sc = int2_quantize(r, g)
+        e = r - int2_dequant(codes, zp, sc, g)
+        Jc = None
+        for G in range(nG):
+            E = None
+            for j in range(G * g, (G + 1) * g):
+                t = e[:, j] * e[:, j]
+                E = t if E is None else E + t
+            u = S[G] * E
+            Jc = u if Jc is None else Jc + u
+        J[:, c] = Jc
+    return J
+
+
+OBJECTIVES = ("qsac", "nearest", "postq")
 
 
 def objective_values(k, C, S, g: int, objective: str) -> np.ndarray:
@@ -268,15 +305,24 @@ def objective_values(k, C, S, g: int, objective: str) -> np.ndarray:
         return qsac_objective(k, C, S, g)
     if objective == "nearest":
         return nearest_objective(k, C, g)
+    if objective == "postq":
+        return postq_objective(k, C, S, g)
     raise ValueError(objective)
 
 
 def assign(k, C, S, g: int, objective: str = "qsac") -> np.ndarray:
-    """Centroid id per Key under the chosen rule (QSAC, or QVG's nearest centroid)."""
+    """Centroid id per Key under the chosen rule (QSAC, QVG's nearest centroid,
+    or the post-rounding error); ties to the smallest id."""
     if objective == "qsac":
         return qsac_assign(k, C, S, g)
     if objective == "nearest":
         return nearest_assign32(k, C, g)
+    if objective == "postq":
+        k = np.asarray(k, dtype=F32)
+        out = np.empty(k.shape[0], np.int64)
+        for a in range(0, k.shape[0], 2048):
+            out[a:a + 2048] = np.argmin(postq_objective(k[a:a + 2048], C, S, g), axis=1)
+        return out
     raise ValueError(objective)
 
 

@@ -281,3 +281,88 @@ def test_table1_direction_on_workload_data():
         hc.append(k, v)
         rates[name] = O.top1_change_rate(q, k, hc)
     assert rates["quantwm"] < rates["qvg"]
+
+
+# ---------------------------------------------------------------- post-rounding error objective
+
+def test_postq_is_the_weighted_error_of_the_stored_record():
+    """postq_objective(k, c) is the sensitivity-weighted squared error the
+    INT2 record of k would have with centroid c: recomputed in float64 from
+    the quantizer's codes and parameters it agrees to float32 rounding, and
+    the record that quantize_tokens stores with this rule has exactly the
+    smallest such error."""
+    rng = np.random.default_rng(31)
+    d, g, m, N = 64, 32, 6, 40
+    k = rng.standard_normal((N, d)).astype(np.float32) * np.float32(2)
+    C = rng.standard_normal((m, d)).astype(np.float32) * np.float32(2)
+    S = np.array([1.5, 0.25], np.float32)
+    J = O.postq_objective(k, C, S, g)
+    for c in range(m):
+        r = (k - C[c]).astype(np.float32)
+        codes, zp, sc = O.int2_quantize(r, g)
+        e = r.astype(np.float64) - O.int2_dequant64(codes, zp, sc, g)
+        j64 = ((e ** 2).reshape(N, d // g, g).sum(2) * S.astype(np.float64)).sum(1)
+        assert np.all(np.abs(J[:, c] - j64) <= 1e-5 * j64 + 1e-30)
+    rec = O.quantize_tokens(k, np.zeros_like(k), C, S, np.zeros((d, 0), np.float32), g, "postq")
+    ids = rec["ids"].astype(np.int64)
+    assert np.array_equal(ids, np.argmin(J, 1))
+    rhat = O.int2_dequant64(rec["kcode"], rec["kzp"], rec["kscale"], g)
+    e = (k - C[ids]).astype(np.float64) - rhat
+    err = ((e ** 2).reshape(N, d // g, g).sum(2) * S.astype(np.float64)).sum(1)
+    assert np.allclose(err, J.min(1), rtol=1e-5)
+    # its own optimum: never above the error of the QSAC or nearest choice
+    for obj in ("qsac", "nearest"):
+        other = O.assign(k, C, S, g, obj)
+        assert np.all(J[np.arange(N), ids] <= J[np.arange(N), other])
+
+
+def test_postq_zero_on_grid_keys_and_half_step_bound():
+    """Keys built exactly on the INT2 grid around one centroid have zero
+    post-rounding error for it (and that centroid is chosen); every error is
+    within the half-step bound sum_G S_G g (step_G / 2)^2."""
+    rng = np.random.default_rng(32)
+    N, d, g, m = 50, 64, 32, 5
+    C = (rng.integers(-40, 40, (m, d)) * 8).astype(np.float32)
+    ids = rng.integers(0, m, N)
+    zp = (rng.integers(-64, 64, (N, d // g)) / 32).astype(np.float16)
+    sc = (rng.integers(1, 32, (N, d // g)) / 64).astype(np.float16)
+    codes = rng.integers(0, 4, (N, d)).astype(np.uint8)
+    codes.reshape(N, d // g, g)[:, :, 0] = 0
+    codes.reshape(N, d // g, g)[:, :, 1] = 3
+    k = C[ids] + O.int2_dequant(codes, zp, sc, g)
+    S = np.array([1.0, 2.0], np.float32)
+    J = O.postq_objective(k, C, S, g)
+    assert np.all(J[np.arange(N), ids] == 0)
+    assert np.array_equal(O.assign(k, C, S, g, "postq"), ids)
+    # half-step bound against each candidate's own quantization step
+    for c in range(m):
+        _, _, stp = O.int2_quantize((k - C[c]).astype(np.float32), g)
+        bound = (S.astype(np.float64) * g * (stp.astype(np.float64) / 2) ** 2).sum(1)
+        assert np.all(J[:, c] <= bound * (1 + 1e-5) + 1e-12)
+
+
+def test_postq_brute_force_argmin_on_tiny_inputs():
+    """On tiny random inputs the float32 argmin equals the argmin of the
+    float64 error (recomputed from the quantizer's records) wherever the two
+    best are not within 1e-6 relative."""
+    rng = np.random.default_rng(33)
+    checked = 0
+    for trial in range(8):
+        d, g = 8, 4
+        m = int(rng.integers(2, 7))
+        N = 40
+        k = rng.standard_normal((N, d)).astype(np.float32) * np.float32(2)
+        C = rng.standard_normal((m, d)).astype(np.float32) * np.float32(2)
+        S = (rng.random(d // g) * 3 + 0.1).astype(np.float32)
+        ids = O.assign(k, C, S, g, "postq")
+        J64 = np.empty((N, m))
+        for c in range(m):
+            r = (k - C[c]).astype(np.float32)
+            codes, zp, sc = O.int2_quantize(r, g)
+            e = r.astype(np.float64) - O.int2_dequant64(codes, zp, sc, g)
+            J64[:, c] = ((e ** 2).reshape(N, d // g, g).sum(2) * S.astype(np.float64)).sum(1)
+        s = np.sort(J64, 1)
+        clear = (s[:, 1] - s[:, 0]) > 1e-6 * s[:, 1]
+        assert np.array_equal(ids[clear], np.argmin(J64, 1)[clear])
+        checked += int(clear.sum())
+    assert checked > 250
