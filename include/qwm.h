@@ -84,8 +84,11 @@ typedef enum {
 /* Centroid rule of quantize-on-insert and of the centroid build. */
 typedef enum {
   QWM_OBJ_QSAC = 0,    /* QSAC: sum_G S_G (max_G r - min_G r)^2 (roboind.com "Step 1") */
-  QWM_OBJ_NEAREST = 1  /* QVG baseline: nearest centroid, sum_j r_j^2 per group in
+  QWM_OBJ_NEAREST = 1, /* QVG baseline: nearest centroid, sum_j r_j^2 per group in
                           channel order, groups added in order (float32) */
+  QWM_OBJ_POSTQ = 2    /* the error the INT2 quantization actually leaves:
+                          sum_G S_G sum_j (r_j - rhat_j)^2, rhat from the cache's own
+                          per-group quantizer (float32, channel order, groups in order) */
 } qwm_objective;
 
 typedef struct {
@@ -145,7 +148,8 @@ qwm_status qwm_build_centroids(qwm_cache* cache, const void* keys, int64_t n_key
  * with the current epoch. Per token and head:
  *   id = argmin_c sum_G S_G (max_G(k - c) - min_G(k - c))^2 in float32, ties
  *        to the smallest id (QSAC, roboind.com "Step 1"), or with
- *        QWM_OBJ_NEAREST argmin_c of the squared distance (qwm_objective);
+ *        QWM_OBJ_NEAREST / QWM_OBJ_POSTQ argmin_c of the squared distance /
+ *        the weighted post-quantization error (qwm_objective);
  *   the residual k - c_id and the Value each get per-group (32 channels)
  *   asymmetric INT2: fp16 zero-point = largest fp16 <= group min, fp16 step =
  *   smallest fp16 >= (max - zp) / 3, codes = clamp(rint((x - zp) / step), 0, 3);

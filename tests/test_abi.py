@@ -42,7 +42,7 @@ def _desc(**kw):
     (dict(n_centroids=257), Q.QWM_ERR_UNSUPPORTED),
     (dict(rank=-1), Q.QWM_ERR_UNSUPPORTED),
     (dict(rank=17), Q.QWM_ERR_UNSUPPORTED),
-    (dict(objective=2), Q.QWM_ERR_INVALID_ARG),
+    (dict(objective=3), Q.QWM_ERR_INVALID_ARG),
     (dict(objective=-1), Q.QWM_ERR_INVALID_ARG),
     (dict(max_epochs=65), Q.QWM_ERR_UNSUPPORTED),
     (dict(heads=0), Q.QWM_ERR_INVALID_ARG),
@@ -57,7 +57,8 @@ def test_desc_validation(kw, status):
     assert Q.last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(rank=0), dict(objective=1), dict(rank=0, objective=1), dict(rank=16)])
+@pytest.mark.parametrize("kw", [dict(rank=0), dict(objective=1), dict(rank=0, objective=1), dict(rank=16),
+                                dict(objective=2)])
 def test_desc_modes_accepted(kw):
     """Rank 0 (PSAC off) and the nearest-centroid rule (QVG) are valid caches;
     rank 0 needs fewer arena bytes (no coefficients, no basis)."""

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-MODES = [("nearest", 0), ("nearest", None), ("qsac", 0)]  # None: the workload's rank
+MODES = [("nearest", 0), ("nearest", None), ("qsac", 0), ("postq", None)]  # None: the workload's rank
 
 
 def _cache(w, rank, objective, capacity=None, max_q=None, max_build=None):
@@ -118,6 +118,29 @@ def test_nearest_rank0_without_sensitivity():
     assert np.array_equal(a.export().cpu().numpy(), b.export().cpu().numpy())
     _, S, _ = b.export_calibration(0)
     assert torch.count_nonzero(S).item() == 0
+
+
+@pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1024, 4), ("video_chunk", 2, 1200, 3)])
+def test_postq_build(name, heads, n_keys, iters):
+    """GPU k-means with the post-rounding error rule reaches the oracle
+    build's mean error within 1%."""
+    w = small(W.workload(name), heads=heads)
+    log(f"[postq build] {name} H={heads} n_keys={n_keys} iters={iters}")
+    gens = [W.HeadGen(w, h) for h in range(heads)]
+    keys = [g.keys(0, n_keys) for g in gens]
+    qh = [g.hist_queries() for g in gens]
+    cache = _cache(w, w.rank, "postq", max_build=n_keys)
+    cache.build_subspace(to_dev(qh, w.dtype))
+    cache.build_centroids(to_dev(keys, w.dtype), iters)
+    C, S, _ = (t.cpu() for t in cache.export_calibration(0))
+    C = C.float().numpy()
+    S = S.numpy()
+    for h in range(heads):
+        Co = O.build_centroids(keys[h], S[h], w.n_centroids, w.group, iters, w.dtype, objective="postq")
+        jg = O.mean_objective(keys[h], C[h], S[h], w.group, "postq")
+        jo = O.mean_objective(keys[h], Co, S[h], w.group, "postq")
+        log(f"  head {h}: mean error gpu {jg:.6g} oracle {jo:.6g} identical {np.array_equal(C[h], Co)}")
+        assert abs(jg - jo) <= 0.01 * jo
 
 
 @pytest.mark.parametrize("name,heads,n_keys,iters,with_subspace", [

@@ -4,7 +4,8 @@
 // Method (QuantWM, arXiv 2609.26425; roboind.com article "Step 1" and
 // "Step 2", fugumt.com abstract): each Key is assigned the centroid that
 // minimizes J = sum_G S_G (max_G r - min_G r)^2, r = k - c (or, for the QVG
-// baseline of "Step 1", the squared distance |r|^2), the residual is
+// baseline of "Step 1", the squared distance |r|^2; or the weighted error the
+// INT2 quantization of r actually leaves), the residual is
 // stored as per-group asymmetric INT2 with fp16 zero-point/step, the Key's
 // remaining error is projected on the PSAC basis (r fp16 coefficients), and
 // the Value is stored as plain per-group INT2.
@@ -72,16 +73,6 @@ __device__ __forceinline__ float nearest_cost(const float (&kf)[D], const float*
   return J;
 }
 
-// Assignment cost of the chosen rule: kObjQsac or kObjNearest.
-template <int OBJ, int D>
-__device__ __forceinline__ float assign_cost(const float (&kf)[D], const float* __restrict__ crow,
-                                             const float (&SG)[D / kGroup]) {
-  if constexpr (OBJ == kObjNearest)
-    return nearest_cost<D>(kf, crow);
-  else
-    return qsac_cost<D>(kf, crow, SG);
-}
-
 // Per-group INT2 parameters (signed zeros folded to +0):
 // zp = largest fp16 <= min, step = smallest fp16 >= (max - zp) / 3.
 __device__ __forceinline__ void int2_params(float mn, float mx, uint32_t& zpb, uint32_t& scb, float& zpf,
@@ -102,6 +93,55 @@ __device__ __forceinline__ uint32_t int2_code(float x, float zpf, float scf) {
   y = rintf(y);               // nearest, ties to even
   y = fminf(fmaxf(y, 0.0f), 3.0f);
   return (uint32_t)y;
+}
+
+// Weighted error left by the INT2 quantization of r = k - c (float32, fixed
+// order): per group the quantizer of the cache (zero-point, step, codes),
+// e_j = r_j - (zp + code_j * step), E = t_0 + t_1 + ... of t_j = e_j * e_j,
+// u = S_G * E, J = ((u0 + u1) + u2) + ...
+template <int D>
+__device__ __forceinline__ float postq_cost(const float (&kf)[D], const float* __restrict__ crow,
+                                            const float (&SG)[D / kGroup]) {
+  constexpr int NG = D / kGroup;
+  float J = 0.0f;
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    float r[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) r[j] = kf[G * kGroup + j] - crow[G * kGroup + j];
+    float mx = r[0], mn = r[0];
+#pragma unroll
+    for (int j = 1; j < kGroup; ++j) {
+      mx = fmaxf(mx, r[j]);
+      mn = fminf(mn, r[j]);
+    }
+    uint32_t zpb, scb;
+    float zpf, scf;
+    int2_params(mn, mx, zpb, scb, zpf, scf);
+    float E = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const float rhat = zpf + (float)int2_code(r[j], zpf, scf) * scf;  // the product is exact
+      const float e = r[j] - rhat;
+      const float t = e * e;
+      E = (j == 0) ? t : E + t;
+    }
+    const float u = SG[G] * E;
+    J = (G == 0) ? u : J + u;
+  }
+  return J;
+}
+
+// Assignment cost of the chosen rule: kObjQsac, kObjNearest or kObjPostq.
+template <int OBJ, int D>
+__device__ __forceinline__ float assign_cost(const float (&kf)[D], const float* __restrict__ crow,
+                                             const float (&SG)[D / kGroup]) {
+  if constexpr (OBJ == kObjNearest)
+    return nearest_cost<D>(kf, crow);
+  else if constexpr (OBJ == kObjPostq)
+    return postq_cost<D>(kf, crow, SG);
+  else
+    return qsac_cost<D>(kf, crow, SG);
 }
 
 template <int D, int DT>
@@ -704,10 +744,12 @@ hipError_t launch_quantize(int D, int dtype, const QuantArgs& a, hipStream_t s) 
 #define QWM_QOBJ(DD, TT)                  \
   if (a.obj == kObjNearest) {             \
     QWM_QLAUNCH(DD, TT, kObjNearest)      \
+  } else if (a.obj == kObjPostq) {        \
+    QWM_QLAUNCH(DD, TT, kObjPostq)        \
   } else {                                \
     QWM_QLAUNCH(DD, TT, kObjQsac)         \
   }
-  if (a.obj != kObjQsac && a.obj != kObjNearest) return hipErrorInvalidValue;
+  if (a.obj != kObjQsac && a.obj != kObjNearest && a.obj != kObjPostq) return hipErrorInvalidValue;
   if (D == 128 && dtype == 0) {
     QWM_QOBJ(128, 0)
   } else if (D == 128 && dtype == 1) {

@@ -41,8 +41,8 @@ qwm_status check_desc(const qwm_desc* d) {
   if (!d) return fail(QWM_ERR_INVALID_ARG, "desc is NULL");
   if (d->heads < 1) return fail(QWM_ERR_INVALID_ARG, "heads must be >= 1");
   if (d->dtype != QWM_BF16 && d->dtype != QWM_F32) return fail(QWM_ERR_INVALID_ARG, "dtype must be QWM_BF16 or QWM_F32");
-  if (d->objective != QWM_OBJ_QSAC && d->objective != QWM_OBJ_NEAREST)
-    return fail(QWM_ERR_INVALID_ARG, "objective must be QWM_OBJ_QSAC or QWM_OBJ_NEAREST");
+  if (d->objective != QWM_OBJ_QSAC && d->objective != QWM_OBJ_NEAREST && d->objective != QWM_OBJ_POSTQ)
+    return fail(QWM_ERR_INVALID_ARG, "objective must be QWM_OBJ_QSAC, QWM_OBJ_NEAREST or QWM_OBJ_POSTQ");
   if (d->capacity_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "capacity_tokens must be >= 1");
   if (d->max_query_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "max_query_tokens must be >= 1");
   if (d->max_build_tokens < 1) return fail(QWM_ERR_INVALID_ARG, "max_build_tokens must be >= 1");
@@ -397,7 +397,9 @@ qwm_status qwm_create(const qwm_desc* desc, void* dev_arena, size_t arena_bytes,
   c->nG = desc->head_dim / qwm::kGroup;
   c->m = desc->n_centroids;
   c->r = desc->rank;
-  c->obj = desc->objective == QWM_OBJ_NEAREST ? qwm::kObjNearest : qwm::kObjQsac;
+  c->obj = desc->objective == QWM_OBJ_NEAREST ? qwm::kObjNearest
+           : desc->objective == QWM_OBJ_POSTQ ? qwm::kObjPostq
+                                              : qwm::kObjQsac;
   c->dtype = desc->dtype;
   c->esz = desc->dtype == QWM_BF16 ? 2 : 4;
   c->device = dev;
@@ -510,7 +512,8 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
     // Pruning pays for its grouping pass only with many centroids (below 128
     // about half the candidates survive) that each hold enough Keys to fill
     // waves of 64 (a wave serves the Keys of one previous centroid).
-    if (it == 0 || c->m < 128 || n_keys < 32 * (int64_t)c->m) {  // every candidate for every Key
+    // (The post-rounding error is no seminorm: it always takes the full pass.)
+    if (it == 0 || c->m < 128 || n_keys < 32 * (int64_t)c->m || c->obj == qwm::kObjPostq) {
       qwm::QuantArgs a{};
       a.k = keys;
       a.v = nullptr;

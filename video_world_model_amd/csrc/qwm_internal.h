@@ -17,6 +17,7 @@ constexpr int kMaxSegments = kMaxEpochs + 1;  // epochs + the self segment
 constexpr int kGramMaxChunks = 8;   // historical-Query chunks per head in the Gram
 constexpr int kObjQsac = 0;         // centroid rule: QSAC objective
 constexpr int kObjNearest = 1;      // centroid rule: nearest centroid (QVG)
+constexpr int kObjPostq = 2;        // centroid rule: weighted error after INT2 quantization
 
 // Per-head structure-of-arrays cache. Every per-head array holds capP token
 // slots (capacity rounded up to a tile multiple) so tile loads never leave the
@@ -50,7 +51,7 @@ struct QuantArgs {
   int64_t pos0;            // first destination slot
   uint8_t* ids_out;        // assignment-only output [H][n] (k-means)
   int H, m, r;
-  int obj;                 // kObjQsac or kObjNearest
+  int obj;                 // kObjQsac, kObjNearest or kObjPostq
 };
 hipError_t launch_quantize(int D, int dtype, const QuantArgs& a, hipStream_t s);
 

@@ -29,7 +29,7 @@ STATUS_NAMES = {
     -4: "QWM_ERR_STATE", -5: "QWM_ERR_HIP", -6: "QWM_ERR_ARENA_TOO_SMALL",
 }
 QWM_BF16, QWM_F32 = 0, 1
-OBJECTIVES = {"qsac": 0, "nearest": 1}
+OBJECTIVES = {"qsac": 0, "nearest": 1, "postq": 2}
 MASKS = {"none": 0, "full": 1, "causal": 2}
 KERNELS = {"quantize": 0, "attend": 1, "merge": 2, "qu": 3, "gram": 4, "eigen": 5, "assign": 6,
            "update": 7, "other": 8}
@@ -134,7 +134,8 @@ class Cache:
     Tensors passed in must be contiguous, on the cache's device, in the
     cache dtype (``torch.bfloat16`` or ``torch.float32``), shaped
     [heads][n][head_dim]; outputs are float32. ``objective`` is the centroid
-    rule ("qsac", or "nearest" for the QVG baseline); rank 0 turns PSAC off.
+    rule ("qsac"; "nearest" for the QVG baseline; "postq" for the weighted
+    error after INT2 quantization); rank 0 turns PSAC off.
     """
 
     def __init__(self, heads: int, head_dim: int, n_centroids: int, rank: int, capacity_tokens: int,
