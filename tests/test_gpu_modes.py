@@ -146,6 +146,7 @@ def test_postq_build(name, heads, n_keys, iters):
 @pytest.mark.parametrize("name,heads,n_keys,iters,with_subspace", [
     ("tiny", 1, 1024, 10, False),
     ("video_chunk", 3, 1760, 4, True),
+    ("video_chunk", 2, 4000, 4, False),  # 64 centroids, enough Keys: the pruned assignment
     ("wm_layer", 2, 6000, 5, False),  # 256 centroids: the pruned assignment
 ])
 def test_nearest_build(name, heads, n_keys, iters, with_subspace):
@@ -168,6 +169,8 @@ def test_nearest_build(name, heads, n_keys, iters, with_subspace):
         jo = O.mean_objective(keys[h], Co, zero, w.group, "nearest")
         log(f"  head {h}: mean distance gpu {jg:.6g} oracle {jo:.6g} identical {np.array_equal(C[h], Co)}")
         assert abs(jg - jo) <= 0.01 * jo
+        if w.dtype == "bf16":
+            assert np.array_equal(C[h], Co)  # exact float64 sums, bit-exact ids
 
 
 def _check_top1(got, logits64, tol_rel):

@@ -205,12 +205,16 @@ def test_determinism():
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
 
+# video_chunk at 4000 Keys (64 centroids) and wm_layer at 9000 (256) take the
+# pruned assignment after the first iteration; the others the full pass.
 @pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1024, 10), ("video_chunk", 4, 1760, 4),
-                                                     ("wm_layer", 2, 1560, 4), ("wm_layer", 2, 9000, 4)])
+                                                     ("video_chunk", 2, 4000, 4), ("wm_layer", 2, 1560, 4),
+                                                     ("wm_layer", 2, 9000, 4)])
 def test_build_calibration(name, heads, n_keys, iters):
     """GPU-built calibration: S_G bit-exact (exact float64 sums of bf16/fp32
     squares), U_r spans the oracle's subspace (projector within 1e-4), and the
-    GPU k-means reaches the oracle's mean QSAC objective within 1%."""
+    GPU k-means reaches the oracle's mean QSAC objective within 1% (bf16
+    Keys: the oracle's centroids bit for bit)."""
     w = small(W.workload(name), heads=heads)
     log(f"[build] {name} H={heads} n_keys={n_keys} iters={iters}")
     gens = [W.HeadGen(w, h) for h in range(heads)]
@@ -240,3 +244,7 @@ def test_build_calibration(name, heads, n_keys, iters):
         jo = O.mean_objective(keys[h], Co, So, w.group)
         log(f"  head {h}: mean J gpu {jg:.6g} oracle {jo:.6g} bit-identical centroids {np.array_equal(C[h], Co)}")
         assert abs(jg - jo) <= 0.01 * jo
+        if w.dtype == "bf16":
+            # float64 sums of bf16 Keys are exact in any order, and the ids are
+            # bit-exact: the centroids are the oracle's bits
+            assert np.array_equal(C[h], Co)

@@ -742,19 +742,38 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
 }
 
 // q . U_r for every epoch slot: qU[h][e][i][k] (k < 16, zero for k >= r).
+// Block = 16 Queries x 16 ranks of one (head, epoch slot): the 16 Query rows
+// and U (D x r, zero-padded to 16 columns) are staged in LDS with all loads
+// in flight together, then thread (i, k) forms its dot product by fma in
+// channel order.
 template <int D, int DT>
 __global__ __launch_bounds__(256) void qu_kernel(const void* q, int64_t nq, int r, const float* Ubase,
                                                  int64_t ustride, int E, float* qU) {
-  const int h = blockIdx.y, e = blockIdx.z;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t qi = idx / kRankPad;
-  const int k = (int)(idx % kRankPad);
+  constexpr int QB = 256 / kRankPad;  // Queries per block
+  __shared__ float us[D][kRankPad];
+  __shared__ float qs[QB][D + 1];
+  const int h = blockIdx.y, e = blockIdx.z, tid = threadIdx.x;
+  const int64_t q0 = (int64_t)blockIdx.x * QB;
+  const float* U = Ubase + (int64_t)e * ustride + (int64_t)h * D * r;
+#pragma unroll
+  for (int i = tid; i < D * kRankPad; i += 256) {
+    const int j = i / kRankPad, k = i % kRankPad;
+    us[j][k] = (k < r) ? U[j * r + k] : 0.0f;
+  }
+#pragma unroll
+  for (int i = tid; i < QB * D; i += 256) {
+    const int qq = i / D, j = i % D;
+    const int64_t qi = q0 + qq < nq ? q0 + qq : nq - 1;
+    qs[qq][j] = load_in<DT>(q, ((int64_t)h * nq + qi) * D + j);
+  }
+  __syncthreads();
+  const int qq = tid / kRankPad, k = tid % kRankPad;
+  const int64_t qi = q0 + qq;
   if (qi >= nq) return;
   float acc = 0.0f;
   if (k < r) {
-    const float* U = Ubase + (int64_t)e * ustride + (int64_t)h * D * r;
-    const int64_t qb = ((int64_t)h * nq + qi) * D;
-    for (int j = 0; j < D; ++j) acc = fmaf(load_in<DT>(q, qb + j), U[j * r + k], acc);
+#pragma unroll 16
+    for (int j = 0; j < D; ++j) acc = fmaf(qs[qq][j], us[j][k], acc);
   }
   qU[(((int64_t)h * E + e) * nq + qi) * kRankPad + k] = acc;
 }
@@ -763,7 +782,7 @@ __global__ __launch_bounds__(256) void qu_kernel(const void* q, int64_t nq, int 
 
 hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, const float* Ubase,
                      int64_t ustride, int E, float* qU, hipStream_t s) {
-  dim3 grid((unsigned)((nq * kRankPad + 255) / 256), (unsigned)H, (unsigned)E), block(256);
+  dim3 grid((unsigned)((nq + 256 / kRankPad - 1) / (256 / kRankPad)), (unsigned)H, (unsigned)E), block(256);
   if (D == 128 && dtype == 0)
     hipLaunchKernelGGL((qu_kernel<128, 0>), grid, block, 0, s, q, nq, r, Ubase, ustride, E, qU);
   else if (D == 128)

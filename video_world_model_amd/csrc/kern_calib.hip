@@ -87,16 +87,74 @@ __global__ __launch_bounds__(256) void gram_kernel(const void* q, int64_t n, int
   }
 }
 
+// Diagonal of one head's chunk Gram (head, chunk per block): thread j < D
+// forms sum_t q_tj^2 by fma in token order, the operations that give the
+// Gram's diagonal entries. Tokens are staged in LDS 64 at a time as float;
+// the raw words of the next 64 are loaded into registers before the current
+// ones are summed.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void diag_kernel(const void* q, int64_t n, int nchunk, double* diag) {
+  constexpr int ESZ = DT == 0 ? 2 : 4;
+  constexpr int WPR = D * ESZ / 16;          // 16-byte words per token row
+  constexpr int WPT = kGramRows * WPR / 256;  // words per thread per 64 tokens
+  __shared__ float qs[kGramRows][D];
+  const int h = blockIdx.x, mc = blockIdx.y, tid = threadIdx.x;
+  const int64_t ta = n * mc / nchunk, tb = n * (mc + 1) / nchunk;
+  const uint4* qh = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(q) + (size_t)h * n * D * ESZ);
+  uint4 w[WPT];
+  auto load = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int e = i * 256 + tid;
+      const int64_t t = t0 + e / WPR < tb ? t0 + e / WPR : tb - 1;  // rows past the chunk: a valid copy, unused
+      w[i] = qh[t * WPR + e % WPR];
+    }
+  };
+  double acc = 0.0;
+  if (ta < tb) load(ta);
+  for (int64_t t0 = ta; t0 < tb; t0 += kGramRows) {
+    const int rows = (int)((tb - t0) < kGramRows ? (tb - t0) : kGramRows);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int e = i * 256 + tid;
+      float* dst = &qs[e / WPR][(e % WPR) * (16 / ESZ)];
+      if constexpr (DT == 0) {
+        const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          dst[2 * k] = __uint_as_float(ww[k] << 16);
+          dst[2 * k + 1] = __uint_as_float(ww[k] & 0xFFFF0000u);
+        }
+      } else {
+        dst[0] = __uint_as_float(w[i].x);
+        dst[1] = __uint_as_float(w[i].y);
+        dst[2] = __uint_as_float(w[i].z);
+        dst[3] = __uint_as_float(w[i].w);
+      }
+    }
+    __syncthreads();
+    if (t0 + kGramRows < tb) load(t0 + kGramRows);
+    if (tid < D) {
+      for (int tt = 0; tt < rows; ++tt) {
+        const double x = (double)qs[tt][tid];
+        acc = fma(x, x, acc);
+      }
+    }
+  }
+  if (tid < D) diag[((int64_t)h * nchunk + mc) * D + tid] = acc;
+}
+
 // Sensitivity S_G = (sum over the group's channels of Gram_jj) / M, one
 // block per head: thread j adds the chunk partials of Gram_jj in chunk order,
 // then thread G adds its group's 32 diagonal entries in channel order.
 template <int N>
-__global__ __launch_bounds__(N) void sens_kernel(const double* gram, int nchunk, int64_t n_hist, float* S) {
+__global__ __launch_bounds__(N) void sens_kernel(const double* diagp, int nchunk, int64_t n_hist, float* S) {
   __shared__ double diag[N];
   const int h = blockIdx.x, j = threadIdx.x;
-  const double* G = gram + (int64_t)h * nchunk * N * N + (int64_t)j * N + j;
+  const double* G = diagp + (int64_t)h * nchunk * N + j;
   double x = 0.0;
-  for (int ch = 0; ch < nchunk; ++ch) x += G[(int64_t)ch * N * N];
+  for (int ch = 0; ch < nchunk; ++ch) x += G[(int64_t)ch * N];
   diag[j] = x;
   __syncthreads();
   if (j < N / kGroup) {
@@ -485,12 +543,26 @@ hipError_t launch_gram(int D, int dtype, const void* q, int64_t n, int H, double
   return hipGetLastError();
 }
 
-hipError_t launch_sens(int D, const double* gram, int nchunk, int64_t n_hist, int H, float* S, hipStream_t s) {
+hipError_t launch_diag(int D, int dtype, const void* q, int64_t n, int H, double* diag, hipStream_t s) {
+  const int nchunk = gram_chunks(n);
+  dim3 grid((unsigned)H, (unsigned)nchunk), block(256);
+  if (D == 128 && dtype == 0)
+    hipLaunchKernelGGL((diag_kernel<128, 0>), grid, block, 0, s, q, n, nchunk, diag);
+  else if (D == 128)
+    hipLaunchKernelGGL((diag_kernel<128, 1>), grid, block, 0, s, q, n, nchunk, diag);
+  else if (dtype == 0)
+    hipLaunchKernelGGL((diag_kernel<64, 0>), grid, block, 0, s, q, n, nchunk, diag);
+  else
+    hipLaunchKernelGGL((diag_kernel<64, 1>), grid, block, 0, s, q, n, nchunk, diag);
+  return hipGetLastError();
+}
+
+hipError_t launch_sens(int D, const double* diag, int nchunk, int64_t n_hist, int H, float* S, hipStream_t s) {
   dim3 grid((unsigned)H), block((unsigned)D);
   if (D == 128)
-    hipLaunchKernelGGL((sens_kernel<128>), grid, block, 0, s, gram, nchunk, n_hist, S);
+    hipLaunchKernelGGL((sens_kernel<128>), grid, block, 0, s, diag, nchunk, n_hist, S);
   else
-    hipLaunchKernelGGL((sens_kernel<64>), grid, block, 0, s, gram, nchunk, n_hist, S);
+    hipLaunchKernelGGL((sens_kernel<64>), grid, block, 0, s, diag, nchunk, n_hist, S);
   return hipGetLastError();
 }
 

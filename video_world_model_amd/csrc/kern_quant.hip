@@ -132,6 +132,38 @@ __device__ __forceinline__ float postq_cost(const float (&kf)[D], const float* _
   return J;
 }
 
+// Term of group G in the assignment cost of the chosen rule: the cost is
+// ((u_0 + u_1) + u_2) + ... of these terms, all >= 0, so every partial sum is
+// a lower bound of the full cost (float32 addition of non-negative numbers
+// never decreases).
+template <int OBJ, int D>
+__device__ __forceinline__ float group_term(const float (&kf)[D], const float* __restrict__ crow, int G,
+                                            const float (&SG)[D / kGroup]) {
+  static_assert(OBJ != kObjPostq, "the post-rounding error is evaluated whole");
+  const float r0 = kf[G * kGroup] - crow[G * kGroup];
+  if constexpr (OBJ == kObjNearest) {
+    float p = r0 * r0;
+#pragma unroll
+    for (int j = 1; j < kGroup; ++j) {
+      const float r = kf[G * kGroup + j] - crow[G * kGroup + j];
+      const float t = r * r;
+      p = p + t;
+    }
+    return p;
+  } else {
+    float mx = r0, mn = r0;
+#pragma unroll
+    for (int j = 1; j < kGroup; ++j) {
+      const float r = kf[G * kGroup + j] - crow[G * kGroup + j];
+      mx = fmaxf(mx, r);
+      mn = fminf(mn, r);
+    }
+    const float R = mx - mn;
+    const float t = R * R;
+    return SG[G] * t;
+  }
+}
+
 // Assignment cost of the chosen rule: kObjQsac, kObjNearest or kObjPostq.
 template <int OBJ, int D>
 __device__ __forceinline__ float assign_cost(const float (&kf)[D], const float* __restrict__ crow,
@@ -402,52 +434,64 @@ __global__ void seed_kernel(const void* keys, int64_t n, int m, void* C, float* 
   C32[di] = load_in<DT>(keys, si);
 }
 
-// k-means update: one block of NW waves per (centroid, head) (16 for long
+// k-means update: one block of NW waves per (centroid, head) (8 for long
 // builds, 2 for short ones, where many centroids each have few members and
-// the block count, not the scan, sets the time). Wave w owns the contiguous
-// token range [w*span, (w+1)*span) (span = n/NW rounded up to a multiple of
-// 64); each lane reads a contiguous run of at most 16 ids per round, so a wave
-// prefix sum over the per-lane match counts lists the centroid's members in
-// token order in LDS. Member Key rows are fetched 8 at a time (each row by the
-// whole wave) and added into float64 lane accumulators; the NW wave sums are
-// then added in wave order. The mean is rounded once to
-// the cache dtype; a centroid without members keeps its value. The order of
-// every addition is fixed, so repeated runs give the same bits.
-constexpr int kUpdLane = 16;  // ids per lane per round
+// the block count, not the scan, sets the time). The head's ids are read as
+// 16-byte blocks aligned in memory (the first block may begin before the
+// head's first id and the last may end after its last; those bytes are
+// masked). Wave w owns the block range [w*bs, (w+1)*bs), one block per lane
+// and round; a wave prefix sum over the per-lane match counts lists the
+// centroid's members in token order in LDS. Member Key rows are fetched
+// kUpdRows at a time (each row by the whole wave, every load issued before
+// the first is used) and added into float64 lane accumulators; the NW wave
+// sums are then added in wave order. The mean is rounded once to the cache
+// dtype; a centroid without members keeps its value. The order of every
+// addition is fixed, so repeated runs give the same bits.
+constexpr int kUpdRows = 8;  // member rows in flight per wave
 
 template <int D, int DT, int NW>
-__global__ __launch_bounds__(NW * 64) void update_kernel(const void* keys, const uint8_t* ids, int64_t n, int m,
+__global__ __launch_bounds__(NW * 64) void update_kernel(const void* keys, const uint8_t* ids, int64_t n64, int m,
                                                          void* C, float* C32) {
   constexpr int PER = D / 64;  // channels per lane
   static_assert(NW * 64 >= D, "one thread per channel in the final sum");
-  __shared__ uint16_t list[NW][64 * kUpdLane];
+  __shared__ uint16_t list[NW][64 * 16];
   __shared__ double red[NW][D];
   __shared__ int cnt[NW];
+  const int n = (int)n64;  // n <= 2^22
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = blockIdx.x, h = blockIdx.y;
-  const uint8_t* idh = ids + (int64_t)h * n;
   uint16_t* lst = list[wave];
-  // per-head Key base (uniform); row offsets fit 32 bits (n <= 2^22)
+  // per-head bases (uniform); row offsets fit 32 bits
   const uint16_t* kh16 = reinterpret_cast<const uint16_t*>(keys) + (size_t)h * n * D;
   const float* kh32 = reinterpret_cast<const float*>(keys) + (size_t)h * n * D;
-
-  const int64_t span = ((n + NW - 1) / NW + 63) / 64 * 64;
-  const int per_lane = (int)(span / 64 < kUpdLane ? span / 64 : kUpdLane);
-  const int64_t round_len = 64 * (int64_t)per_lane;
-  const int64_t w0 = (int64_t)wave * span;
-  const int64_t w1 = (w0 + span < n) ? w0 + span : n;
+  const uint8_t* idh = ids + (size_t)h * n;
+  const int sh = (int)(reinterpret_cast<uintptr_t>(idh) & 15u);  // id 0 sits at byte sh of block 0
+  const uint4* blk = reinterpret_cast<const uint4*>(idh - sh);
+  const int nb = (sh + n + 15) >> 4;
+  const int bs = (nb + NW - 1) / NW;
+  const int b0 = wave * bs, b1 = (b0 + bs < nb) ? b0 + bs : nb;
 
   double acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0;
   int count = 0;
-  for (int64_t base = w0; base < w1; base += round_len) {
-    const int64_t t0 = base + (int64_t)per_lane * lane;
+  for (int rb = b0; rb < b1; rb += 64) {  // wave-uniform
+    const int bi = rb + lane;
+    const uint4 w = blk[bi < b1 ? bi : rb];  // every lane loads; lanes past the range are masked below
+    const int tb = 16 * rb - sh;             // token of byte 0 of the round's first block
+    const int t0 = tb + 16 * lane;           // token of byte 0 of this lane's block
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
     uint32_t match = 0;
 #pragma unroll
-    for (int b = 0; b < kUpdLane; ++b)
-      if (b < per_lane && t0 + b < w1 && idh[t0 + b] == (uint8_t)c) match |= 1u << b;
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) match |= (uint32_t)(((ww[q] >> (8 * k)) & 0xFFu) == (uint32_t)c) << (4 * q + k);
+    // bytes b with 0 <= t0 + b < n of a block inside the wave's range
+    const int lo = t0 < 0 ? -t0 : 0;
+    const int hi = (n - t0) < 16 ? (n - t0) : 16;
+    const uint32_t keep = (bi < b1 && hi > lo) ? (((1u << hi) - 1u) & ~((1u << lo) - 1u)) : 0u;
+    match &= keep;
     const int mc = __popc(match);
     int incl = mc;
 #pragma unroll
@@ -460,38 +504,41 @@ __global__ __launch_bounds__(NW * 64) void update_kernel(const void* keys, const
     while (match) {
       const int b = __ffs(match) - 1;
       match &= match - 1;
-      lst[pos++] = (uint16_t)(per_lane * lane + b);
+      lst[pos++] = (uint16_t)(16 * lane + b);  // token tb + entry
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // member rows 8 at a time (one 32- or 64-bit load per row and lane)
-    for (int u0 = 0; u0 < total; u0 += 8) {
-      float x[8][PER];
+    for (int u0 = 0; u0 < total; u0 += kUpdRows) {
+      uint32_t row[kUpdRows];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kUpdRows; ++u) {
         const int uu = (u0 + u < total) ? u0 + u : total - 1;
-        const uint32_t row = (uint32_t)(base + lst[uu]) * (uint32_t)D + PER * lane;
+        row[u] = (uint32_t)(tb + lst[uu]) * (uint32_t)D + PER * lane;
+      }
+      float x[kUpdRows][PER];
+#pragma unroll
+      for (int u = 0; u < kUpdRows; ++u) {
         if constexpr (DT == 0) {
           if constexpr (PER == 2) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(kh16 + row);
-            x[u][0] = __uint_as_float(w << 16);
-            x[u][1] = __uint_as_float(w & 0xFFFF0000u);
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(kh16 + row[u]);
+            x[u][0] = __uint_as_float(v << 16);
+            x[u][1] = __uint_as_float(v & 0xFFFF0000u);
           } else {
-            x[u][0] = __uint_as_float((uint32_t)kh16[row] << 16);
+            x[u][0] = __uint_as_float((uint32_t)kh16[row[u]] << 16);
           }
         } else {
           if constexpr (PER == 2) {
-            const float2 w = *reinterpret_cast<const float2*>(kh32 + row);
-            x[u][0] = w.x;
-            x[u][1] = w.y;
+            const float2 v = *reinterpret_cast<const float2*>(kh32 + row[u]);
+            x[u][0] = v.x;
+            x[u][1] = v.y;
           } else {
-            x[u][0] = kh32[row];
+            x[u][0] = kh32[row[u]];
           }
         }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < kUpdRows; ++u)
         if (u0 + u < total) {
 #pragma unroll
           for (int k = 0; k < PER; ++k) acc[k] += (double)x[u][k];
@@ -601,20 +648,27 @@ __global__ __launch_bounds__(1024) void bucket_kernel(const uint8_t* ids, int64_
   }
 }
 
-// One block of 4 waves per (previous centroid b, chunk of 64 of its tokens):
-// every wave forms the same keep mask, takes every 4th kept candidate, and
-// the four (J, id) minima are combined lexicographically, which is the
-// argmin with ties to the smallest id. The candidate rows are wave-uniform
-// scalar loads, so nothing before them may look like a memory clobber: the
-// centroid distances N(C_c - C_b) are recomputed by every wave (one lane per
-// candidate) instead of being shared through LDS behind a barrier.
-template <int D, int DT, int OBJ>
-__global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, int64_t n, int m, const float* C32,
-                                                            const float* S, const int32_t* perm, const int32_t* off,
-                                                            const int32_t* woff, uint8_t* ids_out) {
+// One block of NWB waves per (previous centroid b, chunk of 64 of its
+// tokens). Every wave scores b first (that gives the bound of the keep mask
+// and a starting minimum (J_b, b) per token), forms the same keep mask and
+// takes every NWB-th kept candidate; the NWB (J, id) minima are combined
+// lexicographically, which is the argmin over all candidates with ties to the
+// smallest id. A candidate's cost is built group by group; once every token
+// of the wave has a partial sum that already loses to its current minimum
+// (larger, or equal with a larger id), the remaining groups are skipped: the
+// full cost is at least the partial sum, so the candidate cannot win or tie
+// to a smaller id. The candidate rows are wave-uniform scalar loads, so
+// nothing before them may look like a memory clobber: the centroid distances
+// N(C_c - C_b) are recomputed by every wave (one lane per candidate) instead
+// of being shared through LDS behind a barrier.
+template <int D, int DT, int OBJ, int NWB>
+__global__ __launch_bounds__(NWB * 64) void assign_pruned_kernel(const void* keys, int64_t n, int m,
+                                                                 const float* C32, const float* S,
+                                                                 const int32_t* perm, const int32_t* off,
+                                                                 const int32_t* woff, uint8_t* ids_out) {
   constexpr int NG = D / kGroup;
-  __shared__ float bj[4][64];
-  __shared__ int bi[4][64];
+  __shared__ float bj[NWB][64];
+  __shared__ int bi[NWB][64];
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = blockIdx.x;
@@ -661,8 +715,9 @@ __global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, in
   for (int o = 32; o > 0; o >>= 1) d = fmaxf(d, __shfl_xor(d, o));
   const float bound = 2.0f * d * 1.001f;
 
-  float bestJ = (wave == 0) ? Jb : __builtin_inff();
-  int best = (wave == 0) ? b : 0x7fffffff;
+  float bestJ = Jb;
+  int best = b;
+  const bool idle = lane >= cnt;  // copies of the last token: never hold a candidate back
   int rank = 0;  // position in the kept list, to deal the candidates to the waves
 #pragma unroll
   for (int rd = 0; rd < 4; ++rd) {
@@ -672,28 +727,43 @@ __global__ __launch_bounds__(256) void assign_pruned_kernel(const void* keys, in
     while (keep) {
       const int c = 64 * rd + __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(keep));
       keep &= keep - 1;
-      if ((rank++ & 3) != wave) continue;
-      const float J = assign_cost<OBJ, D>(kf, Ch + (int64_t)c * D, SG);
-      if (J < bestJ || (J == bestJ && c < best)) {
+      if (NWB > 1 && (rank++ % NWB) != wave) continue;
+      const float* __restrict__ crow = Ch + (int64_t)c * D;
+      float J = 0.0f;
+      bool lost = false;
+#pragma unroll
+      for (int G = 0; G < NG; ++G) {
+        const float u = group_term<OBJ, D>(kf, crow, G, SG);
+        J = (G == 0) ? u : J + u;
+        if (G < NG - 1 && __all(idle || J > bestJ || (J == bestJ && c > best))) {
+          lost = true;
+          break;
+        }
+      }
+      if (!lost && (J < bestJ || (J == bestJ && c < best))) {
         bestJ = J;
         best = c;
       }
     }
   }
-  bj[wave][lane] = bestJ;
-  bi[wave][lane] = best;
-  __syncthreads();
-  if (tid < cnt) {
-    float J = bj[0][tid];
-    int id = bi[0][tid];
+  if constexpr (NWB == 1) {
+    if (lane < cnt) ids_out[(int64_t)h * n + tok] = (uint8_t)best;
+  } else {
+    bj[wave][lane] = bestJ;
+    bi[wave][lane] = best;
+    __syncthreads();
+    if (tid < cnt) {
+      float J = bj[0][tid];
+      int id = bi[0][tid];
 #pragma unroll
-    for (int v = 1; v < 4; ++v)
-      if (bj[v][tid] < J || (bj[v][tid] == J && bi[v][tid] < id)) {
-        J = bj[v][tid];
-        id = bi[v][tid];
-      }
-    const int t2 = perm[(int64_t)h * n + start + tid];
-    ids_out[(int64_t)h * n + t2] = (uint8_t)id;
+      for (int v = 1; v < NWB; ++v)
+        if (bj[v][tid] < J || (bj[v][tid] == J && bi[v][tid] < id)) {
+          J = bj[v][tid];
+          id = bi[v][tid];
+        }
+      const int t2 = perm[(int64_t)h * n + start + tid];
+      ids_out[(int64_t)h * n + t2] = (uint8_t)id;
+    }
   }
 }
 
@@ -784,19 +854,33 @@ hipError_t launch_kmeans_bucket(const uint8_t* ids, int64_t n, int H, int m, int
   return hipGetLastError();
 }
 
+// Waves per block of the pruned assignment: with few centroids the keep
+// mask leaves few candidates per block, and fewer waves per block means
+// fewer repeated bound computations.
+static int pruned_waves(int m) { return m < 128 ? 2 : 4; }
+
 hipError_t launch_kmeans_assign_pruned(int D, int dtype, int obj, const void* keys, int64_t n, int H, int m,
                                        const float* C32, const float* S, const int32_t* perm, const int32_t* off,
                                        const int32_t* woff, uint8_t* ids_out, hipStream_t s) {
-  dim3 grid((unsigned)((n + 63) / 64 + m), (unsigned)H), block(256);
+  dim3 grid((unsigned)((n + 63) / 64 + m), (unsigned)H);
   if (obj != kObjQsac && obj != kObjNearest) return hipErrorInvalidValue;
-#define QWM_PLAUNCH(DD, TT, OO)                                                                                  \
-  hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO>), grid, block, 0, s, keys, n, m, C32, S, perm, off, woff, \
-                     ids_out)
+  const int nwb = pruned_waves(m);
+#define QWM_PLAUNCH(DD, TT, OO)                                                                                      \
+  if (nwb == 1)                                                                                                      \
+    hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 1>), grid, dim3(64), 0, s, keys, n, m, C32, S, perm, off,   \
+                       woff, ids_out);                                                                               \
+  else if (nwb == 2)                                                                                                 \
+    hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 2>), grid, dim3(128), 0, s, keys, n, m, C32, S, perm, off,  \
+                       woff, ids_out);                                                                               \
+  else                                                                                                               \
+    hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 4>), grid, dim3(256), 0, s, keys, n, m, C32, S, perm, off,  \
+                       woff, ids_out);
 #define QWM_POBJ(DD, TT)                \
-  if (obj == kObjNearest)               \
-    QWM_PLAUNCH(DD, TT, kObjNearest);   \
-  else                                  \
-    QWM_PLAUNCH(DD, TT, kObjQsac);
+  if (obj == kObjNearest) {             \
+    QWM_PLAUNCH(DD, TT, kObjNearest)    \
+  } else {                              \
+    QWM_PLAUNCH(DD, TT, kObjQsac)       \
+  }
   if (D == 128 && dtype == 0) {
     QWM_POBJ(128, 0)
   } else if (D == 128) {
@@ -819,7 +903,7 @@ hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_
   if (small)                                                                                              \
     hipLaunchKernelGGL((update_kernel<DD, TT, 2>), grid, dim3(128), 0, s, keys, ids, n, m, C, C32);       \
   else                                                                                                    \
-    hipLaunchKernelGGL((update_kernel<DD, TT, 16>), grid, dim3(1024), 0, s, keys, ids, n, m, C, C32);
+    hipLaunchKernelGGL((update_kernel<DD, TT, 8>), grid, dim3(512), 0, s, keys, ids, n, m, C, C32);
   if (D == 128 && dtype == 0) {
     QWM_ULAUNCH(128, 0)
   } else if (D == 128) {

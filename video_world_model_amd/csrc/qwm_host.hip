@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Layout {
   size_t kcode, vcode, kparam, vparam, ids, coef;
-  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, build_ids, km_perm, km_off, km_woff, qU, qc, part_o, part_ml;
+  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, diag, build_ids, km_perm, km_off, km_woff, qU, qc, part_o, part_ml;
   size_t total;
   int64_t capP, part_rows;
 };
@@ -93,6 +93,7 @@ Layout make_layout(const qwm_desc* d) {
   L.kmC32 = take((size_t)(H * m * D * 4));
   L.U64 = take((size_t)(H * D * r * 8));
   L.gram = take((size_t)(H * qwm::kGramMaxChunks * D * D * 8));
+  L.diag = take((size_t)(H * qwm::kGramMaxChunks * D * 8));
   L.build_ids = take((size_t)(H * d->max_build_tokens));
   L.km_perm = take((size_t)(H * d->max_build_tokens * 4));
   L.km_off = take((size_t)(H * 257 * 4));
@@ -163,6 +164,7 @@ struct qwm_cache {
   float* kmC32() const { return reinterpret_cast<float*>(arena + L.kmC32); }
   double* U64() const { return reinterpret_cast<double*>(arena + L.U64); }
   double* gram() const { return reinterpret_cast<double*>(arena + L.gram); }
+  double* diag() const { return reinterpret_cast<double*>(arena + L.diag); }
   uint8_t* build_ids() const { return arena + L.build_ids; }
   int32_t* km_perm() const { return reinterpret_cast<int32_t*>(arena + L.km_perm); }
   int32_t* km_off() const { return reinterpret_cast<int32_t*>(arena + L.km_off); }
@@ -459,12 +461,14 @@ qwm_status qwm_build_subspace(qwm_cache* c, const void* q_hist, int64_t n_hist) 
   if ((e = c->join_side()) != hipSuccess) return fail_hip(e, "join eigensolve");
   const int st_slot = c->staged();
   const int nchunk = qwm::gram_chunks(n_hist);
+  // The sensitivity needs only the Gram diagonal: it is formed on the cache
+  // stream, while the full Gram and the eigensolve run on `side`.
   e = c->run(QWM_K_GRAM, [&] {
-    return qwm::launch_gram(c->D, c->dtype, q_hist, n_hist, c->H, c->gram(), c->stream);
+    return qwm::launch_diag(c->D, c->dtype, q_hist, n_hist, c->H, c->diag(), c->stream);
   });
-  if (e != hipSuccess) return fail_hip(e, "gram");
+  if (e != hipSuccess) return fail_hip(e, "gram diagonal");
   e = c->run(QWM_K_GRAM, [&] {
-    return qwm::launch_sens(c->D, c->gram(), nchunk, n_hist, c->H, c->slotS(st_slot), c->stream);
+    return qwm::launch_sens(c->D, c->diag(), nchunk, n_hist, c->H, c->slotS(st_slot), c->stream);
   });
   if (e != hipSuccess) return fail_hip(e, "sensitivity");
   if (c->r == 0) {  // PSAC off: no basis to compute
@@ -473,6 +477,10 @@ qwm_status qwm_build_subspace(qwm_cache* c, const void* q_hist, int64_t n_hist) 
   }
   if ((e = hipEventRecord(c->fork_ev, c->stream)) != hipSuccess) return fail_hip(e, "fork eigensolve");
   if ((e = hipStreamWaitEvent(c->side, c->fork_ev, 0)) != hipSuccess) return fail_hip(e, "fork eigensolve");
+  e = c->run_on(c->side, QWM_K_GRAM, [&] {
+    return qwm::launch_gram(c->D, c->dtype, q_hist, n_hist, c->H, c->gram(), c->side);
+  });
+  if (e != hipSuccess) return fail_hip(e, "gram");
   e = c->run_on(c->side, QWM_K_EIGEN, [&] {
     return qwm::launch_eigen(c->D, c->gram(), nchunk, c->H, c->r, c->slotU(st_slot), c->side);
   });
@@ -510,8 +518,9 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
   if (e != hipSuccess) return fail_hip(e, "kmeans seed");
   for (int it = 0; it < iters; ++it) {
     // Pruning pays for its grouping pass only with many centroids (below 128
-    // about half the candidates survive) that each hold enough Keys to fill
-    // waves of 64 (a wave serves the Keys of one previous centroid).
+    // the skipped work does not cover the bound computations and the
+    // serialized candidate loads) that each hold enough Keys to fill waves of
+    // 64 (a wave serves the Keys of one previous centroid).
     // (The post-rounding error is no seminorm: it always takes the full pass.)
     if (it == 0 || c->m < 128 || n_keys < 32 * (int64_t)c->m || c->obj == qwm::kObjPostq) {
       qwm::QuantArgs a{};

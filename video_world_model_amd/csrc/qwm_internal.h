@@ -81,8 +81,10 @@ hipError_t launch_shadow(int D, int dtype, const void* C, const float* U, int H,
 // Partial Grams [H][chunks][D][D] (chunks = gram_chunks(n) <= kGramMaxChunks).
 int gram_chunks(int64_t n);
 hipError_t launch_gram(int D, int dtype, const void* q, int64_t n, int H, double* gram, hipStream_t s);
-// S_G [H][D/32] from the Gram diagonal (sum of the chunk partials).
-hipError_t launch_sens(int D, const double* gram, int nchunk, int64_t n_hist, int H, float* S, hipStream_t s);
+// Per-chunk partials of the Gram diagonal [H][chunks][D] (the same chunks).
+hipError_t launch_diag(int D, int dtype, const void* q, int64_t n, int H, double* diag, hipStream_t s);
+// S_G [H][D/32] from the diagonal partials (added in chunk order).
+hipError_t launch_sens(int D, const double* diag, int nchunk, int64_t n_hist, int H, float* S, hipStream_t s);
 // Eigensolve of each head's Gram (sum of the chunk partials) -> U_r [H][D][r].
 hipError_t launch_eigen(int D, const double* gram, int nchunk, int H, int r, float* U, hipStream_t s);
 
