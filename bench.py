@@ -71,7 +71,8 @@ KERNELS = ["quantize", "attend", "merge", "qu", "gram", "eigen", "assign", "upda
 KERNEL_SOURCES = {
     "quantize": "kern_quant.hip", "assign": "kern_quant.hip", "update": "kern_quant.hip",
     "attend": "kern_attend.hip", "merge": "kern_attend.hip", "qu": "kern_attend.hip",
-    "gram": "kern_calib.hip", "eigen": "kern_calib.hip", "other": "kern_quant.hip",
+    "gram": "kern_calib.hip", "eigen": "kern_calib.hip", "diag": "kern_calib.hip", "other": "kern_quant.hip",
+    "decode": "kern_decode.hip", "qc": "kern_decode.hip",
 }
 
 
@@ -79,6 +80,20 @@ def source_hash(kernel: str) -> str:
     p = os.path.join(ROOT, "video_world_model_amd", "csrc", KERNEL_SOURCES[kernel])
     with open(p, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, profile: str):
+    """HBM bytes per launch of `kernel` from profiles/<kernel>_<profile>_pmc.json
+    (two rocprofv3 --pmc runs, scaled by the copy probe), or None when there is
+    no such file or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{profile}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        pmc = json.load(f)
+    if pmc.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return pmc.get("hbm_bytes_per_launch")
 
 
 def bytes_per_token_head(d, g, r):
@@ -278,11 +293,12 @@ def bench_streaming(args, w):
     if dom == "attend":
         achieved = a_flops / ta_k / 1e12
         roof = dict(bound="mfma", achieved=achieved, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / MFMA_F16_PEAK_TFLOPS, kernel="attend", traffic=None)
+                    frac=achieved / MFMA_F16_PEAK_TFLOPS, kernel="attend",
+                    traffic=measured_traffic("attend", w.name))
     else:
         achieved = q_ops / tq / 1e12
         roof = dict(bound="alu", achieved=achieved, peak=QSAC_OPS_PEAK / 1e12, unit="Top/s",
-                    frac=achieved * 1e12 / QSAC_OPS_PEAK, kernel=dom, traffic=None)
+                    frac=achieved * 1e12 / QSAC_OPS_PEAK, kernel=dom, traffic=measured_traffic(dom, w.name))
     rec = {
         "metric": METRIC,
         "value": w.heads * w.n_kv / (ms_step * 1e-3),
@@ -383,7 +399,7 @@ def bench_long_horizon(args, w):
         roof = dict(bound="mfma", achieved=achieved, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / MFMA_F16_PEAK_TFLOPS)
     roof["kernel"] = "decode" if decode else "attend"
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(roof["kernel"], f"{w.name}_nq{nq}" if args.nq else w.name)
     rec = {
         "metric": METRIC,
         "value": w.heads * w.n_kv / (ms_step * 1e-3),
@@ -554,14 +570,8 @@ def main():
     else:
         roof = dict(bound="alu", achieved=None, peak=None, unit=None, frac=None)
     roof["kernel"] = dom
-    roof["traffic"] = None
     suffix = "" if args.mode == "quantwm" else f"_{args.mode}"
-    pmc_path = os.path.join(ROOT, "profiles", f"{dom}_{w.name}{suffix}_pmc.json")
-    if os.path.exists(pmc_path):
-        with open(pmc_path) as f:
-            pmc = json.load(f)
-        if pmc.get("source_sha256_16") == source_hash(dom):
-            roof["traffic"] = pmc.get("hbm_bytes_per_launch")
+    roof["traffic"] = measured_traffic(dom, f"{w.name}{suffix}")
 
     extras = {}
     if "quantize" in kern:
