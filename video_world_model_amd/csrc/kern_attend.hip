@@ -40,7 +40,7 @@ struct AttnShape {
   static constexpr int VROW = kTileKV + 8;      // halfs per vhat^T row
   static constexpr int NG = D / kGroup;
   static constexpr int KITEMS = kTileKV * NG * 2;         // (token, 16-channel half group) items
-  static constexpr int VITEMS = (kTileKV / 4) * (D / 4);  // (4-token quad, 4-channel quad) items
+  static constexpr int VITEMS = kTileKV * NG * 2;         // (token, 16-channel half group) items
   static constexpr int KST = kTileKV * KROW;              // halfs of one khat stage
   static constexpr int VST = D * VROW;                    // halfs of one vhat^T (hi or lo) stage
 };
@@ -151,12 +151,11 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
   constexpr int KITEMS = Sh::KITEMS, VITEMS = Sh::VITEMS;
   static_assert(KITEMS <= kAttnThreads && VITEMS <= kAttnThreads, "dequant items must fit one pass");
   // Raw words one thread holds for the next tile: khat values (16 cache-dtype
-  // values), khat code/param word, 8 coefficients, vhat codes + params of 4
-  // tokens, and the 4x4 self Values.
+  // values), khat code/param word, 8 coefficients, vhat code/param word and
+  // 16 self Values of one token.
   constexpr int NK = (DT == 0) ? 2 : 4;  // uint4 words of 16 input values
-  constexpr int RK = 0, RKW = NK, RCF = NK + 1, RVC = NK + 2, RVS = NK + 4;
-  constexpr int NVS = (DT == 0) ? 2 : 4;  // uint4 words of 4 tokens x 4 channels
-  constexpr int NR = RVS + NVS;
+  constexpr int RK = 0, RKW = NK, RCF = NK + 1, RVC = NK + 2, RVS = NK + 3;
+  constexpr int NR = RVS + NK;
   __shared__ __attribute__((aligned(16))) _Float16 lds[2 * (KST + 2 * VST) + 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -178,10 +177,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
   const int tlo = (int)(((int64_t)T * split) / a.splits);
   const int thi = (int)(((int64_t)T * (split + 1)) / a.splits);
 
-  // producer items: khat (token kt, channels 16*kq .. 16*kq+15, group kq/2);
-  // vhat (tokens 4*vtq .. 4*vtq+3, channels 4*vc4 .. 4*vc4+3)
+  // producer items: khat and vhat of token kt, channels 16*kq .. 16*kq+15
+  // (group kq/2)
   const int kt = lane, kq = wave;
-  const int vtq = tid % (kTileKV / 4), vc4 = tid / (kTileKV / 4);
 
   uint4 raw[NR];
   int id_next = 0;
@@ -244,34 +242,14 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
       }
     }
     if (is_v) {
-      uint32_t slot[4], cs[4];
+      const uint32_t slot = (uint32_t)(ti.tstart + (kt < ti.tcount ? kt : ti.tcount - 1));
+      const uint32_t cs = cache ? slot : 0u;
+      raw[RVC].x = *reinterpret_cast<const uint32_t*>(vcode_h + cs * (D / 4) + 4 * kq);
+      raw[RVC].y = vparam_h[cs * NG + (kq >> 1)];
+      const uint4* src = cache ? reinterpret_cast<const uint4*>(vcode_h)
+                               : reinterpret_cast<const uint4*>(vself_h + (slot * D + 16 * kq) * ESZ);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = 4 * vtq + u;
-        slot[u] = (uint32_t)(ti.tstart + (t < ti.tcount ? t : ti.tcount - 1));
-        cs[u] = cache ? slot[u] : 0u;
-      }
-      // channels 4*vc4 .. +3 of a token: one byte of codes, group vc4/8
-      raw[RVC] = make_uint4(vcode_h[cs[0] * (D / 4) + vc4], vcode_h[cs[1] * (D / 4) + vc4],
-                            vcode_h[cs[2] * (D / 4) + vc4], vcode_h[cs[3] * (D / 4) + vc4]);
-      raw[RVC + 1] = make_uint4(vparam_h[cs[0] * NG + (vc4 >> 3)], vparam_h[cs[1] * NG + (vc4 >> 3)],
-                                vparam_h[cs[2] * NG + (vc4 >> 3)], vparam_h[cs[3] * NG + (vc4 >> 3)]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const char* src = cache ? reinterpret_cast<const char*>(vcode_h) : vself_h + (slot[u] * D + 4 * vc4) * ESZ;
-        if constexpr (DT == 0) {
-          const uint2 w = *reinterpret_cast<const uint2*>(src);
-          if (u & 1) {
-            raw[RVS + u / 2].z = w.x;
-            raw[RVS + u / 2].w = w.y;
-          } else {
-            raw[RVS + u / 2].x = w.x;
-            raw[RVS + u / 2].y = w.y;
-          }
-        } else {
-          raw[RVS + u] = *reinterpret_cast<const uint4*>(src);
-        }
-      }
+      for (int i = 0; i < NK; ++i) raw[RVS + i] = src[i];
     }
   };
   // Dequantize the loaded words into LDS stage `st`.
@@ -321,53 +299,33 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
       if (is_v) {
         _Float16* Vh = Ks + KST;
         _Float16* Vl = Vh + VST;
-        // token 4*vtq+u of the tile goes to column 32*ks + 8*gg + 4*b + u of the
-        // row, the order in which the P fragment of lane group gg holds tokens
-        // {4gg..4gg+3, 16+4gg..16+4gg+3} of each 32-token step ks
-        const int ks = vtq / 8, b = (vtq % 8) / 4, gg = vtq % 4;
-        const int col = 32 * ks + 8 * gg + 4 * b;
+        // token j of the tile goes to column 32*(j/32) + 8*gg + 4*b + u of
+        // the vhat^T rows (b = bit 4, gg = bits 2-3, u = bits 0-1 of j): the
+        // order in which the P fragment of lane group gg holds tokens
+        // {4gg..4gg+3, 16+4gg..16+4gg+3} of each 32-token step
+        const int col = (kt & ~31) + 8 * ((kt >> 2) & 3) + 4 * ((kt >> 4) & 1) + (kt & 3);
         const bool cache = ti.ep >= 0;
-        const uint32_t cws[4] = {raw[RVC].x, raw[RVC].y, raw[RVC].z, raw[RVC].w};
-        const uint32_t prs[4] = {raw[RVC + 1].x, raw[RVC + 1].y, raw[RVC + 1].z, raw[RVC + 1].w};
-        float xs[4][4];  // [token][channel]
-        if (!cache) {
+        const float zpf = half_bits_to_float(raw[RVC].y & 0xFFFFu), scf = half_bits_to_float(raw[RVC].y >> 16);
+        const uint32_t w = raw[RVC].x;  // codes of channels 16*kq .. +15
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if constexpr (DT == 0) {
-              const uint4 wq = raw[RVS + u / 2];
-              const uint32_t w0 = (u & 1) ? wq.z : wq.x, w1 = (u & 1) ? wq.w : wq.y;
-              xs[u][0] = __uint_as_float(w0 << 16);
-              xs[u][1] = __uint_as_float(w0 & 0xFFFF0000u);
-              xs[u][2] = __uint_as_float(w1 << 16);
-              xs[u][3] = __uint_as_float(w1 & 0xFFFF0000u);
-            } else {
-              const uint4 wq = raw[RVS + u];
-              xs[u][0] = __uint_as_float(wq.x);
-              xs[u][1] = __uint_as_float(wq.y);
-              xs[u][2] = __uint_as_float(wq.z);
-              xs[u][3] = __uint_as_float(wq.w);
-            }
+        for (int u = 0; u < 2; ++u) {
+          float x[8];
+          if (cache) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = __builtin_fmaf((float)((w >> (16 * u + 2 * c)) & 3u), scf, zpf);
+          } else {
+            unpack_span<DT, 8>(raw + RVS + u * (NK / 2), x);
           }
-        }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float xv[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float x;
-            if (cache) {
-              const float zp = half_bits_to_float(prs[u] & 0xFFFFu), sc = half_bits_to_float(prs[u] >> 16);
-              x = __builtin_fmaf((float)((cws[u] >> (2 * c)) & 3u), sc, zp);
-            } else {
-              x = xs[u][c];
-            }
-            xv[u] = x;
+          for (int c = 0; c < 8; c += 2) {
+            half2v hi, lo;
+            split2(x[c], x[c + 1], hi, lo);
+            const int row = 16 * kq + 8 * u + c;
+            Vh[row * VROW + col] = hi[0];
+            Vh[(row + 1) * VROW + col] = hi[1];
+            Vl[row * VROW + col] = lo[0];
+            Vl[(row + 1) * VROW + col] = lo[1];
           }
-          half2v h0, l0, h1, l1;
-          split2(xv[0], xv[1], h0, l0);
-          split2(xv[2], xv[3], h1, l1);
-          *reinterpret_cast<half4*>(Vh + (4 * vc4 + c) * VROW + col) = half4{h0[0], h0[1], h1[0], h1[1]};
-          *reinterpret_cast<half4*>(Vl + (4 * vc4 + c) * VROW + col) = half4{l0[0], l0[1], l1[0], l1[1]};
         }
       }
     }
