@@ -13,8 +13,8 @@
 //    sequence; the KV sequence is walked in 64-token tiles that never cross an
 //    epoch boundary or the cache/self boundary;
 //  * each tile is dequantized ONCE per workgroup into one of two LDS stages
-//    (every thread: one 16-channel half group of one token's khat and a
-//    4-token x 4-channel block of vhat^T): khat as float16 hi + lo pairs
+//    (every thread: one 16-channel half group of one token's khat and vhat):
+//    khat as float16 hi + lo pairs
 //    (hi = fp16(x), lo = fp16(x - hi), 22 significant bits) with the r PSAC
 //    coefficients next to them, vhat^T as hi + lo; the packed words of the
 //    next tile are loaded into registers before the current tile's MFMA work;
@@ -135,8 +135,8 @@ __device__ __forceinline__ TileInfo tile_info(const AttnPlan& p, int tile) {
 // softmax work of tile i from one stage, the packed words of tile i+1 are
 // already in registers (loaded before that work) and are dequantized into the
 // other stage after it, so global latency hides behind the MFMA chains and
-// one barrier per tile suffices. Threads 0..KITEMS-1 build khat rows, threads
-// 256.. build vhat^T.
+// one barrier per tile suffices. Every thread builds the khat and the vhat^T
+// entries of one token (its lane) and one 16-channel half group (its wave).
 // MODE: kModeAttend (softmax and P.V), kModeLogits (write one head's scaled
 // logits), kModeTop1 (per Query the index of the largest unscaled logit).
 constexpr int kModeAttend = 0, kModeLogits = 1, kModeTop1 = 2;
@@ -378,25 +378,15 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
   float mrow[2] = {-__builtin_inff(), -__builtin_inff()};
   const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
 
-  // Waves 0-3 and 4-7 share the four SIMDs pairwise and run the tile in
-  // opposite orders so that one wave's MFMA chains overlap the other's
-  // dequantization: group 0 loads tile i+1, computes tile i, then writes tile
-  // i+1 to LDS; group 1 writes tile i+1 (loaded during the previous tile),
-  // computes tile i, then loads tile i+2.
-  const bool late = (wave >> 2) & 1;  // wave-uniform
-
-  // prologue: tile tlo into stage 0; group 1 also has tile tlo+1 in registers
+  // Every wave loads the packed words of tile i+1, runs the MFMA and softmax
+  // work of tile i, then writes tile i+1 to the other LDS stage. (Running
+  // half of the waves in the opposite order, to overlap one wave's MFMA
+  // chains with the other's dequantization, measured slower.)
   if (tlo < thi) {
     const TileInfo t0 = tile_info(p, tlo);
     load_raw(t0, load_id(t0));
     store_stage(t0, 0);
-    if (!late) {
-      if (tlo + 1 < thi) id_next = load_id(tile_info(p, tlo + 1));
-    } else if (tlo + 1 < thi) {
-      const TileInfo t1 = tile_info(p, tlo + 1);
-      load_raw(t1, load_id(t1));
-      if (tlo + 2 < thi) id_next = load_id(tile_info(p, tlo + 2));
-    }
+    if (tlo + 1 < thi) id_next = load_id(tile_info(p, tlo + 1));
   }
   __syncthreads();
 
@@ -406,12 +396,8 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
     TileInfo tn{};
     if (tile + 1 < thi) tn = tile_info(p, tile + 1);
     if (tile + 1 < thi) {
-      if (!late) {
-        load_raw(tn, id_next);
-        if (tile + 2 < thi) id_next = load_id(tile_info(p, tile + 2));
-      } else {
-        store_stage(tn, st ^ 1);
-      }
+      load_raw(tn, id_next);
+      if (tile + 2 < thi) id_next = load_id(tile_info(p, tile + 2));
     }
 
     if (wave_live) {
@@ -582,12 +568,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
       }
     }
 
-    if (!late) {
-      if (tile + 1 < thi) store_stage(tn, st ^ 1);
-    } else if (tile + 2 < thi) {
-      load_raw(tile_info(p, tile + 2), id_next);
-      if (tile + 3 < thi) id_next = load_id(tile_info(p, tile + 3));
-    }
+    if (tile + 1 < thi) store_stage(tn, st ^ 1);
     __syncthreads();
   }
 
