@@ -248,3 +248,34 @@ def test_build_calibration(name, heads, n_keys, iters):
             # float64 sums of bf16 Keys are exact in any order, and the ids are
             # bit-exact: the centroids are the oracle's bits
             assert np.array_equal(C[h], Co)
+
+
+# Builds at the edges of the k-means kernels: fewer Keys than centroids
+# (duplicate seeds that never win a tie), a single Key, and odd Key counts
+# whose per-head id rows start off a 16-byte boundary (the update kernel reads
+# the ids as aligned 16-byte blocks and masks the bytes outside the head),
+# on both update shapes (2 waves up to 4,096 Keys, 8 beyond).
+@pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1, 3), ("tiny", 1, 5, 3),
+                                                     ("video_chunk", 3, 37, 3), ("video_chunk", 2, 70, 2),
+                                                     ("video_chunk", 3, 4097, 2)])
+def test_build_small_and_ragged(name, heads, n_keys, iters):
+    w = small(W.workload(name), heads=heads)
+    log(f"[build edge] {name} H={heads} n_keys={n_keys} iters={iters}")
+    gens = [W.HeadGen(w, h) for h in range(heads)]
+    qh = [g.hist_queries() for g in gens]
+    keys = [g.keys(0, n_keys) for g in gens]
+    cache = _cache(w, max_build=n_keys)
+    cache.build_subspace(to_dev(qh, w.dtype))
+    cache.build_centroids(to_dev(keys, w.dtype), iters)
+    C = cache.export_calibration(0)[0].cpu().float().numpy()
+    for h in range(heads):
+        So = O.sensitivity(qh[h], w.group)
+        Co = O.build_centroids(keys[h], So, w.n_centroids, w.group, iters, w.dtype)
+        same = np.array_equal(C[h], Co)
+        log(f"  head {h}: identical centroids {same}")
+        if w.dtype == "bf16":
+            assert same
+        else:
+            jg = O.mean_objective(keys[h], C[h], So, w.group)
+            jo = O.mean_objective(keys[h], Co, So, w.group)
+            assert abs(jg - jo) <= 0.01 * max(jo, 1e-30)
