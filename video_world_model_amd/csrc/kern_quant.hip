@@ -95,6 +95,26 @@ __device__ __forceinline__ uint32_t int2_code(float x, float zpf, float scf) {
   return (uint32_t)y;
 }
 
+// The same code without a divide per value: rcs = v_rcp_f32(step) is within
+// 1 ulp of 1/step, so for quotients below 4 the product (x - zp) * rcs lies
+// within 1e-6 of the correctly rounded quotient, and both round to the same
+// integer unless the product is within 4e-6 of a half-integer (0.5, 1.5, 2.5
+// decide the code; quotients past 3.5 or below -0.5 clamp the same either
+// way). Those lanes take the exact divide, behind a wave-uniform branch.
+// A zero step has rcs = 0: the product is 0 and so is the code.
+__device__ __forceinline__ float rcp_step(float scf) { return scf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(scf); }
+__device__ __forceinline__ uint32_t int2_code_rcp(float x, float zpf, float scf, float rcs) {
+  const float qa = (x - zpf) * rcs;
+  const float rq = rintf(qa);
+  const bool near = fabsf(qa - rq) > 0.5f - 4e-6f;
+  uint32_t code = (uint32_t)fminf(fmaxf(rq, 0.0f), 3.0f);
+  if (__builtin_expect(__any(near), 0)) {
+    const uint32_t ex = int2_code(x, zpf, scf);
+    code = near ? ex : code;
+  }
+  return code;
+}
+
 // Weighted error left by the INT2 quantization of r = k - c (float32, fixed
 // order): per group the quantizer of the cache (zero-point, step, codes),
 // e_j = r_j - (zp + code_j * step), E = t_0 + t_1 + ... of t_j = e_j * e_j,
@@ -118,10 +138,11 @@ __device__ __forceinline__ float postq_cost(const float (&kf)[D], const float* _
     uint32_t zpb, scb;
     float zpf, scf;
     int2_params(mn, mx, zpb, scb, zpf, scf);
+    const float rcs = rcp_step(scf);
     float E = 0.0f;
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const float rhat = zpf + (float)int2_code(r[j], zpf, scf) * scf;  // the product is exact
+      const float rhat = zpf + (float)int2_code_rcp(r[j], zpf, scf, rcs) * scf;  // the product is exact
       const float e = r[j] - rhat;
       const float t = e * e;
       E = (j == 0) ? t : E + t;
@@ -231,37 +252,6 @@ __device__ __forceinline__ void load_row_span(const void* base, int64_t off, flo
   }
 }
 
-// Plain per-group INT2 of one row x (Values): codes into words, params.
-template <int D>
-__device__ __forceinline__ void int2_row(const float (&x)[D], uint32_t (&words)[D / 16],
-                                         uint32_t (&params)[D / kGroup]) {
-  constexpr int NG = D / kGroup;
-#pragma unroll
-  for (int G = 0; G < NG; ++G) {
-    float mx = x[G * kGroup], mn = x[G * kGroup];
-#pragma unroll
-    for (int j = 1; j < kGroup; ++j) {
-      mx = fmaxf(mx, x[G * kGroup + j]);
-      mn = fminf(mn, x[G * kGroup + j]);
-    }
-    uint32_t zpb, scb;
-    float zpf, scf;
-    int2_params(mn, mx, zpb, scb, zpf, scf);
-    params[G] = zpb | (scb << 16);
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const uint32_t code = int2_code(x[G * kGroup + j], zpf, scf);
-      if (j < 16)
-        w0 |= code << (2 * j);
-      else
-        w1 |= code << (2 * (j - 16));
-    }
-    words[2 * G] = w0;
-    words[2 * G + 1] = w1;
-  }
-}
-
 // Block = 4 waves, 64 tokens of one head.
 //  phase 1: wave w scans candidates [w*mq, (w+1)*mq) for all 64 tokens (lane =
 //           token), keeping its lexicographic (J, id) minimum;
@@ -364,12 +354,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     uint32_t zpb, scb;
     float zpf, scf;
     int2_params(mn, mx, zpb, scb, zpf, scf);
+    const float rcs = rcp_step(scf);
     uint32_t w0 = 0, w1 = 0;
     float e[kGroup];
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
       const float r = k[j] - c[j];
-      const uint32_t code = int2_code(r, zpf, scf);
+      const uint32_t code = int2_code_rcp(r, zpf, scf, rcs);
       if (j < 16)
         w0 |= code << (2 * j);
       else
@@ -402,10 +393,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     uint32_t vzb, vsb;
     float vzf, vsf;
     int2_params(vmn, vmx, vzb, vsb, vzf, vsf);
+    const float vrcs = rcp_step(vsf);
     uint32_t u0 = 0, u1 = 0;
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const uint32_t code = int2_code(v[j], vzf, vsf);
+      const uint32_t code = int2_code_rcp(v[j], vzf, vsf, vrcs);
       if (j < 16)
         u0 |= code << (2 * j);
       else
