@@ -54,6 +54,57 @@ def test_quantize_bit_exact(name, heads, n_kv, cal_keys, iters):
     log(f"  coef fp16 one-ulp differences: {flips} of {heads * n_kv * w.rank}")
 
 
+
+def _tie_rows(rng, n, d, dtype):
+    """Rows whose 32-channel groups have min z and max z + 3s with s a power of
+    two, so zero-point = z and step = s exactly, and whose other channels sit
+    at z + (k + 1/2) s (ties: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2) or one ulp of the
+    input dtype to either side of them."""
+    ties = np.array([0.5, 1.5, 2.5], np.float32)
+    rows = np.empty((n, d), np.float32)
+    for t in range(n):
+        for g0 in range(0, d, 32):
+            s = np.float32(2.0) ** rng.integers(-6, 5)
+            z = np.float32(rng.choice([0.0, -1.25, 0.75, -3.0]))
+            q = ties[rng.integers(0, 3, 32)]
+            x = (z + q * s).astype(np.float32)
+            step = rng.integers(-1, 2, 32) * (x != 0)  # one ulp down, none, up (zeros stay)
+            if dtype == "bf16":
+                xb = W.bf16_bits(W.round_to_bf16(x)).astype(np.int32) + np.where(x < 0, -1, 1) * step
+                x = (xb.astype(np.uint32) << 16).view(np.float32)
+            else:
+                x = np.where(step > 0, np.nextafter(x, np.float32(np.inf)),
+                             np.where(step < 0, np.nextafter(x, np.float32(-np.inf)), x)).astype(np.float32)
+            x[0], x[1] = z, z + 3 * s
+            rows[t, g0:g0 + 32] = x
+    if dtype == "bf16":  # the values the device receives
+        rows = W.round_to_bf16(rows)
+    assert np.all(np.isfinite(rows))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["tiny", "video_chunk"])
+def test_quantize_half_integer_ties(name):
+    """INT2 codes of quotients at and one ulp around 0.5, 1.5, 2.5: the
+    kernels round the reciprocal product and fall back to the correctly
+    rounded divide next to a half-integer; the codes must be the oracle's."""
+    w = small(W.workload(name), heads=1, n_kv=256)
+    rng = np.random.default_rng(7)
+    g = W.HeadGen(w, 0)
+    keys = [_tie_rows(rng, 256, w.head_dim, w.dtype)]
+    vals = [_tie_rows(rng, 256, w.head_dim, w.dtype)]
+    C = np.zeros((w.n_centroids, w.head_dim), np.float32)  # residual = Key; every id ties to 0
+    S = O.sensitivity(g.hist_queries(), w.group)
+    U = O.subspace(g.hist_queries(), w.rank)
+    cals = [(C, S, U)]
+    cache = _cache(w)
+    import_calibration(cache, cals, w.dtype)
+    cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+    dec = cache.decode_export(cache.export().cpu().numpy(), 256)
+    rec = O.quantize_tokens(keys[0], vals[0], C, S, U, w.group)
+    compare_records(dec, 0, rec)
+    log(f"  {name}: codes equal the oracle's over {256 * w.head_dim} Key and Value channels")
+
 def _oracle_heads(w, keys, vals, cals):
     hcs = []
     for h in range(w.heads):
