@@ -103,16 +103,20 @@ __device__ __forceinline__ uint32_t int2_code(float x, float zpf, float scf) {
 // way). Those lanes take the exact divide, behind a wave-uniform branch.
 // A zero step has rcs = 0: the product is 0 and so is the code.
 __device__ __forceinline__ float rcp_step(float scf) { return scf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(scf); }
-__device__ __forceinline__ uint32_t int2_code_rcp(float x, float zpf, float scf, float rcs) {
+// The code as a float (0, 1, 2 or 3).
+__device__ __forceinline__ float int2_codef_rcp(float x, float zpf, float scf, float rcs) {
   const float qa = (x - zpf) * rcs;
   const float rq = rintf(qa);
   const bool near = fabsf(qa - rq) > 0.5f - 4e-6f;
-  uint32_t code = (uint32_t)fminf(fmaxf(rq, 0.0f), 3.0f);
+  float code = fminf(fmaxf(rq, 0.0f), 3.0f);
   if (__builtin_expect(__any(near), 0)) {
-    const uint32_t ex = int2_code(x, zpf, scf);
+    const float ex = (float)int2_code(x, zpf, scf);
     code = near ? ex : code;
   }
   return code;
+}
+__device__ __forceinline__ uint32_t int2_code_rcp(float x, float zpf, float scf, float rcs) {
+  return (uint32_t)int2_codef_rcp(x, zpf, scf, rcs);
 }
 
 // Weighted error left by the INT2 quantization of r = k - c (float32, fixed
@@ -142,7 +146,7 @@ __device__ __forceinline__ float postq_cost(const float (&kf)[D], const float* _
     float E = 0.0f;
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const float rhat = zpf + (float)int2_code_rcp(r[j], zpf, scf, rcs) * scf;  // the product is exact
+      const float rhat = zpf + int2_codef_rcp(r[j], zpf, scf, rcs) * scf;  // the product is exact
       const float e = r[j] - rhat;
       const float t = e * e;
       E = (j == 0) ? t : E + t;
