@@ -9,6 +9,10 @@
 //   U_r  = eigenvectors of Gram with the r largest eigenvalues, descending,
 //          each column's largest-magnitude entry positive (lowest index on ties).
 //
+// S_G needs only the Gram's diagonal: diag_kernel forms it (with the same fma
+// sequence as the Gram's diagonal entries) on the cache stream, so the k-means
+// does not wait for the full Gram, which runs beside the eigensolve.
+//
 // The eigensolve runs in one workgroup per head (the Gram in registers, the
 // float64 reflectors plus work arrays in ~140 KB of the 160 KB of LDS of a
 // CDNA4 CU): Householder tridiagonalization, multisection for the
