@@ -681,47 +681,64 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
 }
 
 // q . U_r for every epoch slot: qU[h][e][i][k] (k < 16, zero for k >= r).
-// Block = 16 Queries x 16 ranks of one (head, epoch slot): the 16 Query rows
-// and U (D x r, zero-padded to 16 columns) are staged in LDS with all loads
-// in flight together, then thread (i, k) forms its dot product by fma in
-// channel order.
+// One wave per 16 Queries of one head, all epoch slots: D[Query][rank] =
+// q U by v_mfma_f32_16x16x32_f16 with the Query fragments in fp16 (bf16
+// inputs are exact; float32 inputs add a lo part) and U as fp16 hi + lo
+// (products exact, float32 sums).
 template <int D, int DT>
-__global__ __launch_bounds__(256) void qu_kernel(const void* q, int64_t nq, int r, const float* Ubase,
-                                                 int64_t ustride, int E, float* qU) {
-  constexpr int QB = 256 / kRankPad;  // Queries per block
-  __shared__ float us[D][kRankPad];
-  __shared__ float qs[QB][D + 1];
-  const int h = blockIdx.y, e = blockIdx.z, tid = threadIdx.x;
-  const int64_t q0 = (int64_t)blockIdx.x * QB;
-  const float* U = Ubase + (int64_t)e * ustride + (int64_t)h * D * r;
+__global__ __launch_bounds__(64) void qu_kernel(const void* q, int64_t nq, int r, const float* Ubase,
+                                                int64_t ustride, int E, float* qU) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
+  const int h = blockIdx.y;
+  const int64_t q0 = (int64_t)blockIdx.x * 16;
+  // A: Query q0 + l16, channels 32ks + 8g .. +7
+  half8 qa[KS], qb[KS];
+  {
+    const int64_t qi = q0 + l16 < nq ? q0 + l16 : nq - 1;
 #pragma unroll
-  for (int i = tid; i < D * kRankPad; i += 256) {
-    const int j = i / kRankPad, k = i % kRankPad;
-    us[j][k] = (k < r) ? U[j * r + k] : 0.0f;
-  }
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-  for (int i = tid; i < QB * D; i += 256) {
-    const int qq = i / D, j = i % D;
-    const int64_t qi = q0 + qq < nq ? q0 + qq : nq - 1;
-    qs[qq][j] = load_in<DT>(q, ((int64_t)h * nq + qi) * D + j);
+      for (int e = 0; e < 8; ++e) {
+        const float x = load_in<DT>(q, ((int64_t)h * nq + qi) * D + 32 * ks + 8 * g + e);
+        const _Float16 hi = (_Float16)x;
+        qa[ks][e] = hi;
+        qb[ks][e] = (_Float16)(x - (float)hi);
+      }
   }
-  __syncthreads();
-  const int qq = tid / kRankPad, k = tid % kRankPad;
-  const int64_t qi = q0 + qq;
-  if (qi >= nq) return;
-  float acc = 0.0f;
-  if (k < r) {
-#pragma unroll 16
-    for (int j = 0; j < D; ++j) acc = fmaf(qs[qq][j], us[j][k], acc);
+  const bool rv = l16 < r;
+  for (int ep = 0; ep < E; ++ep) {
+    // B: U column l16 (rank), channels 32ks + 8g .. +7; ranks past r are zero
+    const float* U = Ubase + (int64_t)ep * ustride + (int64_t)h * D * r;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      half8 uh, ul;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = rv ? U[(32 * ks + 8 * g + e) * r + l16] : 0.0f;
+        const _Float16 hi = (_Float16)x;
+        uh[e] = hi;
+        ul[e] = (_Float16)(x - (float)hi);
+      }
+      acc = mfma16(qa[ks], uh, acc);
+      acc = mfma16(qa[ks], ul, acc);
+      if constexpr (DT == 1) acc = mfma16(qb[ks], uh, acc);
+    }
+    // D[Query 4g + v][rank l16]
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t qi = q0 + 4 * g + v;
+      if (qi < nq) qU[(((int64_t)h * E + ep) * nq + qi) * kRankPad + l16] = acc[v];
+    }
   }
-  qU[(((int64_t)h * E + e) * nq + qi) * kRankPad + k] = acc;
 }
 
 }  // namespace
 
 hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, const float* Ubase,
                      int64_t ustride, int E, float* qU, hipStream_t s) {
-  dim3 grid((unsigned)((nq + 256 / kRankPad - 1) / (256 / kRankPad)), (unsigned)H, (unsigned)E), block(256);
+  dim3 grid((unsigned)((nq + 15) / 16), (unsigned)H), block(64);
   if (D == 128 && dtype == 0)
     hipLaunchKernelGGL((qu_kernel<128, 0>), grid, block, 0, s, q, nq, r, Ubase, ustride, E, qU);
   else if (D == 128)
