@@ -115,10 +115,15 @@ def _oracle_heads(w, keys, vals, cals):
     return hcs
 
 
+# 65 Queries: the first count past the decode kernel's 64 (prefill path);
+# 257: one live Query in the second 256-Query workgroup; 1000 Keys: a ragged
+# last tile.
 @pytest.mark.parametrize("name,heads,n_kv,n_q,mask", [
     ("tiny", 1, 1024, 16, "none"),
     ("video_chunk", 12, 7040, 880, "full"),
     ("video_chunk", 2, 1000, 200, "none"),
+    ("video_chunk", 2, 1000, 65, "none"),
+    ("video_chunk", 2, 3001, 257, "none"),
 ])
 def test_attend_matches_oracle(name, heads, n_kv, n_q, mask):
     w = small(W.workload(name), heads=heads, n_kv=n_kv, n_q=n_q, n_self=n_q if mask != "none" else 0)
