@@ -9,7 +9,8 @@
 // over all visible tokens and o_i = sum_j p_ij vhat_j.
 //
 // Mapping to CDNA4:
-//  * one workgroup = 8 waves = 256 Queries of one head, one split of the KV
+//  * one workgroup = 8 waves = up to 256 Queries of one head (the Queries
+//    spread evenly over the workgroups in 32-Query waves), one split of the KV
 //    sequence; the KV sequence is walked in 64-token tiles that never cross an
 //    epoch boundary or the cache/self boundary;
 //  * each tile is dequantized ONCE per workgroup into one of two LDS stages
@@ -130,7 +131,7 @@ __device__ __forceinline__ TileInfo tile_info(const AttnPlan& p, int tile) {
   return ti;
 }
 
-// Attention workgroup: 8 waves = 256 Queries of one head over the tiles
+// Attention workgroup: 8 waves = up to 256 Queries of one head over the tiles
 // [tlo, thi) of one split. Two LDS stages: while the waves run the MFMA and
 // softmax work of tile i from one stage, the packed words of tile i+1 are
 // already in registers (loaded before that work) and are dequantized into the
@@ -163,8 +164,10 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
   const int g = lane >> 4, l16 = lane & 15;
   const int h = LOGITS ? a.logit_head : (int)blockIdx.z;
   const int split = blockIdx.y;
-  const int64_t qw0 = (int64_t)blockIdx.x * kTileQ + wave * 32;
-  const bool wave_live = qw0 < a.nq;  // waves whose 32 Queries are all padding skip the math
+  const int64_t qw0 = (int64_t)blockIdx.x * a.qpb + wave * 32;
+  // waves past the workgroup's Queries, or whose 32 Queries are all padding,
+  // skip the math (they still stage tiles)
+  const bool wave_live = wave * 32 < a.qpb && qw0 < a.nq;
   // wave-uniform producer roles (items are whole waves)
   const bool is_k = wave < KITEMS / 64;
   const bool is_v = !NOV && wave < VITEMS / 64;
@@ -752,7 +755,7 @@ hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, 
 
 template <int MODE>
 static hipError_t launch_attend_impl(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  dim3 grid((unsigned)((a.nq + kTileQ - 1) / kTileQ), (unsigned)a.splits,
+  dim3 grid((unsigned)((a.nq + a.qpb - 1) / a.qpb), (unsigned)a.splits,
             MODE == kModeLogits ? 1u : (unsigned)a.H);
   dim3 block(kAttnThreads);
   if (D == 128 && dtype == 0)

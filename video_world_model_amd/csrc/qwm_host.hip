@@ -285,6 +285,17 @@ qwm::AttnArgs base_args(qwm_cache* c) {
   return a;
 }
 
+// Queries per attention workgroup: the fewest workgroups of at most 256
+// Queries, with the 32-Query waves spread evenly over them (880 Queries: 4 x
+// 224 rather than 3 x 256 + 112), so no workgroup carries more live waves
+// than it must.
+int queries_per_block(int64_t n_q) {
+  if (n_q < 1) return qwm::kTileQ;
+  const int64_t nblk = (n_q + qwm::kTileQ - 1) / qwm::kTileQ;
+  const int64_t waves = (n_q + 31) / 32;
+  return (int)(32 * ((waves + nblk - 1) / nblk));
+}
+
 // Split the KV tiles so that the workgroups fill the device in as few
 // rounds as possible: cost = rounds x (tiles per workgroup + 2 for its
 // prologue and epilogue) + 2 for the merge pass when split; one 145 KB-LDS
@@ -681,6 +692,7 @@ qwm_status qwm_attend(qwm_cache* c, const void* q, int64_t n_q, const void* k_se
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.n_epoch_slots = E;
+  a.qpb = queries_per_block(n_q);
   a.out = out;
   // Few Queries over bf16 Keys: the decode kernel (2-bit codes as the MFMA
   // operand, one wave per workgroup, many splits)
@@ -727,6 +739,7 @@ qwm_status qwm_attend_logits(qwm_cache* c, const void* q, int64_t n_q, int32_t h
   a.nq = n_q;
   a.scale = softmax_scale;
   a.n_epoch_slots = E;
+  a.qpb = queries_per_block(n_q);
   a.logits = logits;
   a.logit_head = head;
   a.logit_len = c->length;
@@ -785,6 +798,7 @@ qwm_status qwm_attend_top1(qwm_cache* c, const void* q, int64_t n_q, const void*
   a.scale = 1.0f;
   a.scale_log2 = 1.4426950408889634f;
   a.n_epoch_slots = E;
+  a.qpb = queries_per_block(n_q);
   a.top1 = top1;
   a.splits = choose_splits(c, n_q, T);
   hipError_t e = hipSuccess;

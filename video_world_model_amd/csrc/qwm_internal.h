@@ -10,7 +10,7 @@ namespace qwm {
 constexpr int kGroup = 32;       // channels per INT2 group
 constexpr int kRankPad = 16;     // PSAC rank padded for the MFMA contraction
 constexpr int kTileKV = 64;      // tokens per attention tile
-constexpr int kTileQ = 256;      // Queries per attention workgroup (8 waves x 32)
+constexpr int kTileQ = 256;      // most Queries per attention workgroup (8 waves x 32)
 constexpr int kAttnThreads = 512;
 constexpr int kMaxEpochs = 64;
 constexpr int kMaxSegments = kMaxEpochs + 1;  // epochs + the self segment
@@ -112,6 +112,7 @@ struct AttnArgs {
   int n_epoch_slots;      // E of qU
   int H, m, r;
   int splits;
+  int qpb;                // Queries per workgroup: a multiple of 32, at most kTileQ
   float* out;             // [H][nq][D] (splits == 1)
   float* part_o;          // [splits][H][nq][D]
   float* part_ml;         // [splits][H][nq][2]
