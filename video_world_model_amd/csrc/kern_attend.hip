@@ -91,6 +91,21 @@ __device__ __forceinline__ void load_span(const void* base, int64_t off, float (
 }
 
 // Raw words of N input-dtype values -> floats (bf16: two per word).
+// Value c (0..7) of an 8-value span of raw words: bf16 pairs in one uint4,
+// or float32 in two.
+template <int DT>
+__device__ __forceinline__ float span_elem(const uint4* w, int c) {
+  if constexpr (DT == 0) {
+    const uint4 v = w[0];
+    const uint32_t ww = (c >> 1) == 0 ? v.x : (c >> 1) == 1 ? v.y : (c >> 1) == 2 ? v.z : v.w;
+    return __uint_as_float((c & 1) ? (ww & 0xFFFF0000u) : (ww << 16));
+  } else {
+    const uint4 v = w[c >> 2];
+    const int k = c & 3;
+    return __uint_as_float(k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w);
+  }
+}
+
 template <int DT, int N>
 __device__ __forceinline__ void unpack_span(const uint4* w, float (&x)[N]) {
   if constexpr (DT == 0) {
@@ -169,8 +184,10 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
   // skip the math (they still stage tiles)
   const bool wave_live = wave * 32 < a.qpb && qw0 < a.nq;
   // wave-uniform producer roles (items are whole waves)
-  const bool is_k = wave < KITEMS / 64;
-  const bool is_v = !NOV && wave < VITEMS / 64;
+  // (always true at head_dim 128, where every thread holds one khat and one
+  // vhat item; at 64 only waves 0-3 do)
+  const bool is_k = KITEMS >= kAttnThreads || wave < KITEMS / 64;
+  const bool is_v = !NOV && (VITEMS >= kAttnThreads || wave < VITEMS / 64);
   // softmax in the log2 domain with a positive factor; a negative scale is
   // carried by negated Queries (exact in fp16)
   const float qsign = (!NOV && a.scale_log2 < 0.0f) ? -1.0f : 1.0f;
@@ -255,83 +272,93 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
       for (int i = 0; i < NK; ++i) raw[RVS + i] = src[i];
     }
   };
-  // Dequantize the loaded words into LDS stage `st`.
-  auto store_stage = [&](const TileInfo& ti, int st) {
+  auto store_coef = [&](const TileInfo& ti, int st) {
+    if (kq < 2) {
+      _Float16* row = lds + st * (KST + 2 * VST) + kt * KROW;
+      uint4 cfw = raw[RCF];
+      const int j0 = 8 * kq;  // halves j0 .. j0+7; keep those below r
+      const bool use = ti.ep >= 0;
+      cfw.x = (use && j0 + 0 < a.r) ? (j0 + 1 < a.r ? cfw.x : cfw.x & 0xFFFFu) : 0u;
+      cfw.y = (use && j0 + 2 < a.r) ? (j0 + 3 < a.r ? cfw.y : cfw.y & 0xFFFFu) : 0u;
+      cfw.z = (use && j0 + 4 < a.r) ? (j0 + 5 < a.r ? cfw.z : cfw.z & 0xFFFFu) : 0u;
+      cfw.w = (use && j0 + 6 < a.r) ? (j0 + 7 < a.r ? cfw.w : cfw.w & 0xFFFFu) : 0u;
+      *reinterpret_cast<uint4*>(row + 2 * D + 8 * kq) = cfw;
+    }
+  };
+  // Dequantize the loaded words into LDS stage `st`, in 16 pieces: part 0
+  // and 1 are khat channels 16*kq .. +7 and +8 .. +15, parts 2 and 3 the same
+  // halves of vhat; piece pc of a part is its channels 2pc and 2pc+1. Pieces
+  // are branch-free (self tiles take zero step and zero point for khat and
+  // select the raw Values for vhat), so the caller can spread them between
+  // MFMAs; khat halves are stored with the part's last piece. The
+  // coefficients (waves 0 and 1) are stored by store_coef. All parts write
+  // disjoint LDS words.
+  struct DequantPieces {
+    half8 h8, l8;
+  };
+  auto dequant_piece = [&](const TileInfo& ti, int st, int part, int pc, DequantPieces& dq) {
     _Float16* Ks = lds + st * (KST + 2 * VST);
-    if (is_k) {
-      _Float16* row = Ks + kt * KROW;
-      const bool cache = ti.ep >= 0;
-      const float zpf = half_bits_to_float(raw[RKW].y & 0xFFFFu), scf = half_bits_to_float(raw[RKW].y >> 16);
-      const uint32_t w = raw[RKW].x;  // codes of channels 16*kq .. +15
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        half8 h8, l8;
-        float x[8];
-        unpack_span<DT, 8>(raw + RK + u * (NK / 2), x);
-        if (cache) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float code = (float)((w >> (16 * u + 2 * c)) & 3u);
-            x[c] = x[c] + __builtin_fmaf(code, scf, zpf);  // zp + code*step: exact
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          half2v hi, lo;
-          split2(x[2 * c], x[2 * c + 1], hi, lo);
-          h8[2 * c] = hi[0];
-          h8[2 * c + 1] = hi[1];
-          l8[2 * c] = lo[0];
-          l8[2 * c + 1] = lo[1];
-        }
-        *reinterpret_cast<half8*>(row + 16 * kq + 8 * u) = h8;
-        *reinterpret_cast<half8*>(row + D + 16 * kq + 8 * u) = l8;
+    const bool cache = ti.ep >= 0;
+    const int c = 2 * pc;
+    if (part < 2) {
+      if (!is_k) return;
+      const int u = part;
+      const uint32_t kp = cache ? raw[RKW].y : 0u;  // self: k + (code*0 + 0) = k
+      const float zpf = half_bits_to_float(kp & 0xFFFFu), scf = half_bits_to_float(kp >> 16);
+      const uint32_t w = raw[RKW].x;
+      float x0 = span_elem<DT>(raw + RK + u * (NK / 2), c);
+      float x1 = span_elem<DT>(raw + RK + u * (NK / 2), c + 1);
+      x0 = x0 + __builtin_fmaf((float)((w >> (16 * u + 2 * c)) & 3u), scf, zpf);
+      x1 = x1 + __builtin_fmaf((float)((w >> (16 * u + 2 * c + 2)) & 3u), scf, zpf);
+      half2v hi, lo;
+      split2(x0, x1, hi, lo);
+      dq.h8[c] = hi[0];
+      dq.h8[c + 1] = hi[1];
+      dq.l8[c] = lo[0];
+      dq.l8[c + 1] = lo[1];
+      if (pc == 3) {
+        _Float16* row = Ks + kt * KROW;
+        *reinterpret_cast<half8*>(row + 16 * kq + 8 * u) = dq.h8;
+        *reinterpret_cast<half8*>(row + D + 16 * kq + 8 * u) = dq.l8;
       }
-      if (kq < 2) {
-        uint4 cfw = raw[RCF];
-        const int j0 = 8 * kq;  // halves j0 .. j0+7; keep those below r
-        const bool use = cache;
-        cfw.x = (use && j0 + 0 < a.r) ? (j0 + 1 < a.r ? cfw.x : cfw.x & 0xFFFFu) : 0u;
-        cfw.y = (use && j0 + 2 < a.r) ? (j0 + 3 < a.r ? cfw.y : cfw.y & 0xFFFFu) : 0u;
-        cfw.z = (use && j0 + 4 < a.r) ? (j0 + 5 < a.r ? cfw.z : cfw.z & 0xFFFFu) : 0u;
-        cfw.w = (use && j0 + 6 < a.r) ? (j0 + 7 < a.r ? cfw.w : cfw.w & 0xFFFFu) : 0u;
-        *reinterpret_cast<uint4*>(row + 2 * D + 8 * kq) = cfw;
+    } else if constexpr (!NOV) {
+      if (!is_v) return;
+      const int u = part - 2;
+      _Float16* Vh = Ks + KST;
+      _Float16* Vl = Vh + VST;
+      // token j of the tile goes to column 32*(j/32) + 8*gg + 4*b + u of
+      // the vhat^T rows (b = bit 4, gg = bits 2-3, u = bits 0-1 of j): the
+      // order in which the P fragment of lane group gg holds tokens
+      // {4gg..4gg+3, 16+4gg..16+4gg+3} of each 32-token step
+      const int col = (kt & ~31) + 8 * ((kt >> 2) & 3) + 4 * ((kt >> 4) & 1) + (kt & 3);
+      const float zpf = half_bits_to_float(raw[RVC].y & 0xFFFFu), scf = half_bits_to_float(raw[RVC].y >> 16);
+      const uint32_t w = raw[RVC].x;
+      const uint32_t msel = cache ? 0xFFFFFFFFu : 0u;
+      float x[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float xc = __builtin_fmaf((float)((w >> (16 * u + 2 * (c + e))) & 3u), scf, zpf);
+        const float xs = span_elem<DT>(raw + RVS + u * (NK / 2), c + e);
+        x[e] = __uint_as_float((__float_as_uint(xc) & msel) | (__float_as_uint(xs) & ~msel));
       }
+      half2v hi, lo;
+      split2(x[0], x[1], hi, lo);
+      const int row = 16 * kq + 8 * u + c;
+      Vh[row * VROW + col] = hi[0];
+      Vh[(row + 1) * VROW + col] = hi[1];
+      Vl[row * VROW + col] = lo[0];
+      Vl[(row + 1) * VROW + col] = lo[1];
     }
-    if constexpr (!NOV) {
-      if (is_v) {
-        _Float16* Vh = Ks + KST;
-        _Float16* Vl = Vh + VST;
-        // token j of the tile goes to column 32*(j/32) + 8*gg + 4*b + u of
-        // the vhat^T rows (b = bit 4, gg = bits 2-3, u = bits 0-1 of j): the
-        // order in which the P fragment of lane group gg holds tokens
-        // {4gg..4gg+3, 16+4gg..16+4gg+3} of each 32-token step
-        const int col = (kt & ~31) + 8 * ((kt >> 2) & 3) + 4 * ((kt >> 4) & 1) + (kt & 3);
-        const bool cache = ti.ep >= 0;
-        const float zpf = half_bits_to_float(raw[RVC].y & 0xFFFFu), scf = half_bits_to_float(raw[RVC].y >> 16);
-        const uint32_t w = raw[RVC].x;  // codes of channels 16*kq .. +15
+  };
+  auto store_part = [&](const TileInfo& ti, int st, int part) {
+    DequantPieces dq;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float x[8];
-          if (cache) {
+    for (int pc = 0; pc < 4; ++pc) dequant_piece(ti, st, part, pc, dq);
+  };
+  auto store_stage = [&](const TileInfo& ti, int st) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) x[c] = __builtin_fmaf((float)((w >> (16 * u + 2 * c)) & 3u), scf, zpf);
-          } else {
-            unpack_span<DT, 8>(raw + RVS + u * (NK / 2), x);
-          }
-#pragma unroll
-          for (int c = 0; c < 8; c += 2) {
-            half2v hi, lo;
-            split2(x[c], x[c + 1], hi, lo);
-            const int row = 16 * kq + 8 * u + c;
-            Vh[row * VROW + col] = hi[0];
-            Vh[(row + 1) * VROW + col] = hi[1];
-            Vl[row * VROW + col] = lo[0];
-            Vl[(row + 1) * VROW + col] = lo[1];
-          }
-        }
-      }
-    }
+    for (int part = 0; part < 4; ++part) store_part(ti, st, part);
+    store_coef(ti, st);
   };
 
   // Query fragments (B operand): Query qw0 + 16*qb + l16, channels 32*ks + 8*g .. +7.
@@ -550,28 +577,69 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttnArgs a, 
             lrow[qb] = l;
           }
         }
-        // ---- o^T += vhat^T P^T
+        // ---- o^T += vhat^T P^T, with the next tile's dequantization spread
+        // between the MFMAs: independent VALU work the wave issues while its
+        // MFMAs run (it writes the other LDS stage). After the last tile this
+        // stages stale words into the unused stage: harmless, and it keeps
+        // the code branch-free.
         const _Float16* Vh = Ks + KST;
         const _Float16* Vl = Vh + VST;
+        if constexpr (D == 128) {
+          // 16 steps of (ks, cb); step i also runs piece i % 4 of dequant
+          // part i / 4. The next step's operands are read before the piece.
+          constexpr int NSTEP = 2 * (D / 16);
+          half8 ah = *reinterpret_cast<const half8*>(Vh + l16 * VROW + 8 * g);
+          half8 al = *reinterpret_cast<const half8*>(Vl + l16 * VROW + 8 * g);
+          DequantPieces dq;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+          for (int i = 0; i < NSTEP; ++i) {
+            const int ks = i / (D / 16), cb = i % (D / 16);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int cb = 0; cb < D / 16; ++cb) {
-            if (cb % 4 == 0) __builtin_amdgcn_sched_barrier(0);
-            const int off = (16 * cb + l16) * VROW + 32 * ks + 8 * g;
-            const half8 ah = *reinterpret_cast<const half8*>(Vh + off);
-            const half8 al = *reinterpret_cast<const half8*>(Vl + off);
+            for (int qb = 0; qb < 2; ++qb) O[qb][cb] = mfma16(ah, pf[qb][ks], O[qb][cb]);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              O[qb][cb] = mfma16(ah, pf[qb][ks], O[qb][cb]);
-              O[qb][cb] = mfma16(al, pf[qb][ks], O[qb][cb]);
+            for (int qb = 0; qb < 2; ++qb) O[qb][cb] = mfma16(al, pf[qb][ks], O[qb][cb]);
+            if (i + 1 < NSTEP) {
+              const int ks1 = (i + 1) / (D / 16), cb1 = (i + 1) % (D / 16);
+              const int off = (16 * cb1 + l16) * VROW + 32 * ks1 + 8 * g;
+              ah = *reinterpret_cast<const half8*>(Vh + off);
+              al = *reinterpret_cast<const half8*>(Vl + off);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            dequant_piece(tn, st ^ 1, i / 4, i % 4, dq);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            store_part(tn, st ^ 1, 2 * ks);
+            store_part(tn, st ^ 1, 2 * ks + 1);
+#pragma unroll
+            for (int cb = 0; cb < D / 16; ++cb) {
+              const int off = (16 * cb + l16) * VROW + 32 * ks + 8 * g;
+              const half8 ah = *reinterpret_cast<const half8*>(Vh + off);
+              const half8 al = *reinterpret_cast<const half8*>(Vl + off);
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb) {
+                O[qb][cb] = mfma16(ah, pf[qb][ks], O[qb][cb]);
+                O[qb][cb] = mfma16(al, pf[qb][ks], O[qb][cb]);
+              }
             }
           }
         }
       }
     }
 
-    if (tile + 1 < thi) store_stage(tn, st ^ 1);
+    // waves that ran the P.V product have staged the next tile's khat and
+    // vhat already
+    if (tile + 1 < thi) {
+      if (NOV || !wave_live) {
+        store_stage(tn, st ^ 1);
+      } else {
+        store_coef(tn, st ^ 1);
+      }
+    }
     __syncthreads();
   }
 
