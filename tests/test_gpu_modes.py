@@ -146,8 +146,8 @@ def test_postq_build(name, heads, n_keys, iters):
 @pytest.mark.parametrize("name,heads,n_keys,iters,with_subspace", [
     ("tiny", 1, 1024, 10, False),
     ("video_chunk", 3, 1760, 4, True),
-    ("video_chunk", 2, 4000, 4, False),  # 64 centroids, enough Keys: the pruned assignment
-    ("wm_layer", 2, 6000, 5, False),  # 256 centroids: the pruned assignment
+    ("video_chunk", 2, 4000, 4, False),  # 64 centroids: the full pass every iteration
+    ("wm_layer", 2, 9000, 5, False),  # 256 centroids, >= 32 Keys each: the pruned assignment
 ])
 def test_nearest_build(name, heads, n_keys, iters, with_subspace):
     """GPU k-means with the nearest-centroid rule (QVG, rank 0) reaches the

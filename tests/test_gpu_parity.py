@@ -261,8 +261,9 @@ def test_determinism():
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
 
-# video_chunk at 4000 Keys (64 centroids) and wm_layer at 9000 (256) take the
-# pruned assignment after the first iteration; the others the full pass.
+# wm_layer at 9000 Keys (256 centroids, at least 32 Keys per centroid) takes
+# the pruned assignment after the first iteration; the others run the full
+# pass (the pruned pass needs 128 or more centroids).
 @pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1024, 10), ("video_chunk", 4, 1760, 4),
                                                      ("video_chunk", 2, 4000, 4), ("wm_layer", 2, 1560, 4),
                                                      ("wm_layer", 2, 9000, 4)])
