@@ -657,11 +657,40 @@ __global__ __launch_bounds__(1024) void bucket_kernel(const uint8_t* ids, int64_
 // nothing before them may look like a memory clobber: the centroid distances
 // N(C_c - C_b) are recomputed by every wave (one lane per candidate) instead
 // of being shared through LDS behind a barrier.
+// Distances N(C_c - C_b) = sqrt(J) between every two centroids of a head,
+// row b of the table = [h][b][0 .. m): the bound the pruned assignment
+// compares with, computed once per iteration instead of in every wave that
+// needs a row. Lane c holds centroid c in registers (as a Key in the
+// assignment) and the wave walks its share of the rows b with scalar loads;
+// the same function of the same rows as the assignment's own cost.
+constexpr int kCcdSplit = 16;  // b ranges per (64 rows, head)
+
+template <int D, int OBJ>
+__global__ __launch_bounds__(64) void ccd_kernel(int m, const float* __restrict__ C32, const float* __restrict__ S,
+                                                 float* __restrict__ ccd) {
+  constexpr int NG = D / kGroup;
+  const int lane = threadIdx.x, h = blockIdx.y;
+  const int c = blockIdx.x * 64 + lane;
+  const int nb = (m + kCcdSplit - 1) / kCcdSplit;
+  const int b0 = blockIdx.z * nb, b1 = (b0 + nb) < m ? (b0 + nb) : m;
+  const float* __restrict__ Ch = C32 + (int64_t)h * m * D;
+  float SG[NG];
+#pragma unroll
+  for (int G = 0; G < NG; ++G) SG[G] = S[h * NG + G];
+  float x[D];
+  load_row_span<D, 1>(Ch, (int64_t)(c < m ? c : 0) * D, x);
+  for (int b = b0; b < b1; ++b) {
+    const float v = sqrtf(assign_cost<OBJ, D>(x, Ch + (int64_t)b * D, SG));
+    if (c < m) ccd[((int64_t)h * m + b) * m + c] = v;
+  }
+}
+
 template <int D, int DT, int OBJ, int NWB>
 __global__ __launch_bounds__(NWB * 64) void assign_pruned_kernel(const void* keys, int64_t n, int m,
                                                                  const float* C32, const float* S,
                                                                  const int32_t* perm, const int32_t* off,
-                                                                 const int32_t* woff, uint8_t* ids_out) {
+                                                                 const int32_t* woff, const float* ccdtab,
+                                                                 uint8_t* ids_out) {
   constexpr int NG = D / kGroup;
   __shared__ float bj[NWB][64];
   __shared__ int bi[NWB][64];
@@ -689,17 +718,13 @@ __global__ __launch_bounds__(NWB * 64) void assign_pruned_kernel(const void* key
 #pragma unroll
   for (int G = 0; G < NG; ++G) SG[G] = S[h * NG + G];
 
-  // N(C_c - C_b) for c = 64*round + lane
+  // N(C_c - C_b) for c = 64*round + lane, from the table of this iteration
+  const float* __restrict__ ccd_b = ccdtab + ((int64_t)h * m + b) * m;
   float ccd[4];
 #pragma unroll
   for (int rd = 0; rd < 4; ++rd) {
-    ccd[rd] = 0.0f;
     const int c = 64 * rd + lane;
-    if (64 * rd < m) {
-      float x[D];
-      load_row_span<D, 1>(Ch, (int64_t)(c < m ? c : 0) * D, x);
-      ccd[rd] = sqrtf(assign_cost<OBJ, D>(x, Cb, SG));
-    }
+    ccd[rd] = (64 * rd < m) ? ccd_b[c < m ? c : 0] : 0.0f;
   }
 
   const int tok = perm[(int64_t)h * n + start + (lane < cnt ? lane : cnt - 1)];
@@ -850,27 +875,47 @@ hipError_t launch_kmeans_bucket(const uint8_t* ids, int64_t n, int H, int m, int
   return hipGetLastError();
 }
 
-// Waves per block of the pruned assignment: with few centroids the keep
-// mask leaves few candidates per block, and fewer waves per block means
-// fewer repeated bound computations.
-static int pruned_waves(int m) { return m < 128 ? 2 : 4; }
+// Waves per block of the pruned assignment (the waves of a block share its
+// 64 Keys and deal the kept candidates among themselves). At 256 centroids,
+// with the centroid distances read from the table, one wave per block does
+// best: 0.85 ms per wm_layer launch against 0.86 with 2 waves and 0.97
+// with 4. Below 128 centroids the host takes the full pass; 2 waves measured
+// best there.
+static int pruned_waves(int m) { return m < 128 ? 2 : 1; }
+
+hipError_t launch_kmeans_ccd(int D, int obj, int H, int m, const float* C32, const float* S, float* ccd,
+                             hipStream_t s) {
+  if (m < 1 || m > 256) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((m + 63) / 64), (unsigned)H, (unsigned)kCcdSplit), block(64);
+  if (obj == kObjQsac && D == 128)
+    hipLaunchKernelGGL((ccd_kernel<128, kObjQsac>), grid, block, 0, s, m, C32, S, ccd);
+  else if (obj == kObjQsac && D == 64)
+    hipLaunchKernelGGL((ccd_kernel<64, kObjQsac>), grid, block, 0, s, m, C32, S, ccd);
+  else if (obj == kObjNearest && D == 128)
+    hipLaunchKernelGGL((ccd_kernel<128, kObjNearest>), grid, block, 0, s, m, C32, S, ccd);
+  else if (obj == kObjNearest && D == 64)
+    hipLaunchKernelGGL((ccd_kernel<64, kObjNearest>), grid, block, 0, s, m, C32, S, ccd);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_kmeans_assign_pruned(int D, int dtype, int obj, const void* keys, int64_t n, int H, int m,
                                        const float* C32, const float* S, const int32_t* perm, const int32_t* off,
-                                       const int32_t* woff, uint8_t* ids_out, hipStream_t s) {
+                                       const int32_t* woff, const float* ccd, uint8_t* ids_out, hipStream_t s) {
   dim3 grid((unsigned)((n + 63) / 64 + m), (unsigned)H);
   if (obj != kObjQsac && obj != kObjNearest) return hipErrorInvalidValue;
   const int nwb = pruned_waves(m);
 #define QWM_PLAUNCH(DD, TT, OO)                                                                                      \
   if (nwb == 1)                                                                                                      \
     hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 1>), grid, dim3(64), 0, s, keys, n, m, C32, S, perm, off,   \
-                       woff, ids_out);                                                                               \
+                       woff, ccd, ids_out);                                                                               \
   else if (nwb == 2)                                                                                                 \
     hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 2>), grid, dim3(128), 0, s, keys, n, m, C32, S, perm, off,  \
-                       woff, ids_out);                                                                               \
+                       woff, ccd, ids_out);                                                                               \
   else                                                                                                               \
     hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 4>), grid, dim3(256), 0, s, keys, n, m, C32, S, perm, off,  \
-                       woff, ids_out);
+                       woff, ccd, ids_out);
 #define QWM_POBJ(DD, TT)                \
   if (obj == kObjNearest) {             \
     QWM_PLAUNCH(DD, TT, kObjNearest)    \

@@ -32,7 +32,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Layout {
   size_t kcode, vcode, kparam, vparam, ids, coef;
-  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, diag, build_ids, km_perm, km_off, km_woff, qU, qc, part_o, part_ml;
+  size_t epochC, epochS, epochU, C32, kmC32, U64, gram, diag, build_ids, km_perm, km_off, km_woff, km_ccd, qU, qc,
+      part_o, part_ml;
   size_t total;
   int64_t capP, part_rows;
 };
@@ -98,6 +99,8 @@ Layout make_layout(const qwm_desc* d) {
   L.km_perm = take((size_t)(H * d->max_build_tokens * 4));
   L.km_off = take((size_t)(H * 257 * 4));
   L.km_woff = take((size_t)(H * 257 * 4));
+  // centroid-to-centroid bounds of the pruned assignment (128 or more centroids)
+  L.km_ccd = take(m >= 128 ? (size_t)(H * m * m * 4) : 0);
   L.qU = take((size_t)(H * E * maxq * qwm::kRankPad * 4));
   L.qc = take((size_t)(H * E * m * nqp_max * 4));
   L.part_o = take((size_t)(pr * D * 4));
@@ -169,6 +172,7 @@ struct qwm_cache {
   int32_t* km_perm() const { return reinterpret_cast<int32_t*>(arena + L.km_perm); }
   int32_t* km_off() const { return reinterpret_cast<int32_t*>(arena + L.km_off); }
   int32_t* km_woff() const { return reinterpret_cast<int32_t*>(arena + L.km_woff); }
+  float* km_ccd() const { return reinterpret_cast<float*>(arena + L.km_ccd); }
   float* qU() const { return reinterpret_cast<float*>(arena + L.qU); }
   float* qc() const { return reinterpret_cast<float*>(arena + L.qc); }
   float* part_o() const { return reinterpret_cast<float*>(arena + L.part_o); }
@@ -549,13 +553,18 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
       if (e != hipSuccess) return fail_hip(e, "kmeans assign");
     } else {  // the same ids, skipping candidates the triangle inequality rules out
       e = c->run(QWM_K_OTHER, [&] {
+        return qwm::launch_kmeans_ccd(c->D, c->obj, c->H, c->m, c->kmC32(), c->slotS(stg), c->km_ccd(), c->stream);
+      });
+      if (e != hipSuccess) return fail_hip(e, "kmeans centroid distances");
+      e = c->run(QWM_K_OTHER, [&] {
         return qwm::launch_kmeans_bucket(c->build_ids(), n_keys, c->H, c->m, c->km_perm(), c->km_off(), c->km_woff(),
                                          c->stream);
       });
       if (e != hipSuccess) return fail_hip(e, "kmeans bucket");
       e = c->run(QWM_K_ASSIGN, [&] {
         return qwm::launch_kmeans_assign_pruned(c->D, c->dtype, c->obj, keys, n_keys, c->H, c->m, c->kmC32(), c->slotS(stg),
-                                                c->km_perm(), c->km_off(), c->km_woff(), c->build_ids(), c->stream);
+                                                c->km_perm(), c->km_off(), c->km_woff(), c->km_ccd(), c->build_ids(),
+                                                c->stream);
       });
       if (e != hipSuccess) return fail_hip(e, "kmeans assign");
     }
