@@ -644,19 +644,6 @@ __global__ __launch_bounds__(1024) void bucket_kernel(const uint8_t* ids, int64_
   }
 }
 
-// One block of NWB waves per (previous centroid b, chunk of 64 of its
-// tokens). Every wave scores b first (that gives the bound of the keep mask
-// and a starting minimum (J_b, b) per token), forms the same keep mask and
-// takes every NWB-th kept candidate; the NWB (J, id) minima are combined
-// lexicographically, which is the argmin over all candidates with ties to the
-// smallest id. A candidate's cost is built group by group; once every token
-// of the wave has a partial sum that already loses to its current minimum
-// (larger, or equal with a larger id), the remaining groups are skipped: the
-// full cost is at least the partial sum, so the candidate cannot win or tie
-// to a smaller id. The candidate rows are wave-uniform scalar loads, so
-// nothing before them may look like a memory clobber: the centroid distances
-// N(C_c - C_b) are recomputed by every wave (one lane per candidate) instead
-// of being shared through LDS behind a barrier.
 // Distances N(C_c - C_b) = sqrt(J) between every two centroids of a head,
 // row b of the table = [h][b][0 .. m): the bound the pruned assignment
 // compares with, computed once per iteration instead of in every wave that
@@ -685,6 +672,19 @@ __global__ __launch_bounds__(64) void ccd_kernel(int m, const float* __restrict_
   }
 }
 
+// One block of NWB waves per (previous centroid b, chunk of 64 of its
+// tokens). Every wave scores b first (that gives the bound of the keep mask
+// and a starting minimum (J_b, b) per token), forms the same keep mask and
+// takes every NWB-th kept candidate; the NWB (J, id) minima are combined
+// lexicographically, which is the argmin over all candidates with ties to the
+// smallest id. A candidate's cost is built group by group; once every token
+// of the wave has a partial sum that already loses to its current minimum
+// (larger, or equal with a larger id), the remaining groups are skipped: the
+// full cost is at least the partial sum, so the candidate cannot win or tie
+// to a smaller id. The candidate rows are wave-uniform scalar loads, so
+// nothing before them may look like a memory clobber (no barrier): the
+// centroid distances N(C_c - C_b) come from the table ccd_kernel fills
+// before the launch.
 template <int D, int DT, int OBJ, int NWB>
 __global__ __launch_bounds__(NWB * 64) void assign_pruned_kernel(const void* keys, int64_t n, int m,
                                                                  const float* C32, const float* S,
