@@ -95,28 +95,36 @@ __device__ __forceinline__ uint32_t int2_code(float x, float zpf, float scf) {
   return (uint32_t)y;
 }
 
-// The same code without a divide per value: rcs = v_rcp_f32(step) is within
+// The same codes without a divide per value: rcs = v_rcp_f32(step) is within
 // 1 ulp of 1/step, so for quotients below 4 the product (x - zp) * rcs lies
 // within 1e-6 of the correctly rounded quotient, and both round to the same
 // integer unless the product is within 4e-6 of a half-integer (0.5, 1.5, 2.5
 // decide the code; quotients past 3.5 or below -0.5 clamp the same either
-// way). Those lanes take the exact divide, behind a wave-uniform branch.
-// A zero step has rcs = 0: the product is 0 and so is the code.
+// way). Such values take the exact divide. A zero step has rcs = 0: the
+// product is 0 and so is the code.
 __device__ __forceinline__ float rcp_step(float scf) { return scf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(scf); }
-// The code as a float (0, 1, 2 or 3).
-__device__ __forceinline__ float int2_codef_rcp(float x, float zpf, float scf, float rcs) {
-  const float qa = (x - zpf) * rcs;
-  const float rq = rintf(qa);
-  const bool near = fabsf(qa - rq) > 0.5f - 4e-6f;
-  float code = fminf(fmaxf(rq, 0.0f), 3.0f);
-  if (__builtin_expect(__any(near), 0)) {
-    const float ex = (float)int2_code(x, zpf, scf);
-    code = near ? ex : code;
+// The codes (as floats 0..3) of a whole group, with one wave-uniform check
+// for the group instead of one per value (each check is a branch): only when
+// some lane holds a value that close to a boundary are that lane's boundary
+// values redone with the correctly rounded divide.
+template <int N>
+__device__ __forceinline__ void int2_codes_rcp(const float (&x)[N], float zpf, float scf, float (&code)[N]) {
+  const float rcs = rcp_step(scf);
+  bool anynear = false;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const float qa = (x[j] - zpf) * rcs;
+    const float rq = rintf(qa);
+    anynear = anynear | (fabsf(qa - rq) > 0.5f - 4e-6f);
+    code[j] = fminf(fmaxf(rq, 0.0f), 3.0f);
   }
-  return code;
-}
-__device__ __forceinline__ uint32_t int2_code_rcp(float x, float zpf, float scf, float rcs) {
-  return (uint32_t)int2_codef_rcp(x, zpf, scf, rcs);
+  if (__builtin_expect(__any(anynear), 0)) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float qa = (x[j] - zpf) * rcs;
+      if (fabsf(qa - rintf(qa)) > 0.5f - 4e-6f) code[j] = (float)int2_code(x[j], zpf, scf);
+    }
+  }
 }
 
 // Weighted error left by the INT2 quantization of r = k - c (float32, fixed
@@ -142,11 +150,12 @@ __device__ __forceinline__ float postq_cost(const float (&kf)[D], const float* _
     uint32_t zpb, scb;
     float zpf, scf;
     int2_params(mn, mx, zpb, scb, zpf, scf);
-    const float rcs = rcp_step(scf);
+    float code[kGroup];
+    int2_codes_rcp(r, zpf, scf, code);
     float E = 0.0f;
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const float rhat = zpf + int2_codef_rcp(r[j], zpf, scf, rcs) * scf;  // the product is exact
+      const float rhat = zpf + code[j] * scf;  // the product is exact
       const float e = r[j] - rhat;
       const float t = e * e;
       E = (j == 0) ? t : E + t;
@@ -358,13 +367,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     uint32_t zpb, scb;
     float zpf, scf;
     int2_params(mn, mx, zpb, scb, zpf, scf);
-    const float rcs = rcp_step(scf);
+    float rr[kGroup], kc[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) rr[j] = k[j] - c[j];
+    int2_codes_rcp(rr, zpf, scf, kc);
     uint32_t w0 = 0, w1 = 0;
     float e[kGroup];
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const float r = k[j] - c[j];
-      const uint32_t code = int2_code_rcp(r, zpf, scf, rcs);
+      const uint32_t code = (uint32_t)kc[j];
       if (j < 16)
         w0 |= code << (2 * j);
       else
@@ -397,11 +408,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     uint32_t vzb, vsb;
     float vzf, vsf;
     int2_params(vmn, vmx, vzb, vsb, vzf, vsf);
-    const float vrcs = rcp_step(vsf);
+    float vc[kGroup];
+    int2_codes_rcp(v, vzf, vsf, vc);
     uint32_t u0 = 0, u1 = 0;
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const uint32_t code = int2_code_rcp(v[j], vzf, vsf, vrcs);
+      const uint32_t code = (uint32_t)vc[j];
       if (j < 16)
         u0 |= code << (2 * j);
       else
