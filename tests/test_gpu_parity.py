@@ -25,23 +25,26 @@ def _cache(w, capacity=None, max_epochs=1, max_q=None, max_build=None):
                  max_build_tokens=max_build or max(w.n_kv, 64))
 
 
-def _setup(w, n_kv, cal_keys, iters):
+def _setup(w, n_kv, cal_keys, iters, seed=0):
     """Generator arrays + oracle calibration + oracle head caches for heads 0..H-1."""
-    gens = [W.HeadGen(w, h) for h in range(w.heads)]
+    gens = [W.HeadGen(w, h, seed) for h in range(w.heads)]
     keys = [g.keys(0, n_kv) for g in gens]
     vals = [g.values(0, n_kv) for g in gens]
     cals = [oracle_calibration(w, g, k[:cal_keys], g.hist_queries(), iters) for g, k in zip(gens, keys)]
     return gens, keys, vals, cals
 
 
-@pytest.mark.parametrize("name,heads,n_kv,cal_keys,iters", [
-    ("tiny", 1, 1024, 1024, 10),
-    ("video_chunk", 12, 7040, 880, 2),
+# (seeds 1 and 2: the same shapes from other generator streams)
+@pytest.mark.parametrize("name,heads,n_kv,cal_keys,iters,seed", [
+    ("tiny", 1, 1024, 1024, 10, 0),
+    ("video_chunk", 12, 7040, 880, 2, 0),
+    ("tiny", 1, 1024, 1024, 10, 1),
+    ("video_chunk", 2, 2000, 880, 2, 2),
 ])
-def test_quantize_bit_exact(name, heads, n_kv, cal_keys, iters):
+def test_quantize_bit_exact(name, heads, n_kv, cal_keys, iters, seed):
     w = small(W.workload(name), heads=heads, n_kv=n_kv)
-    log(f"[quantize parity] {name} H={heads} n={n_kv}")
-    gens, keys, vals, cals = _setup(w, n_kv, cal_keys, iters)
+    log(f"[quantize parity] {name} H={heads} n={n_kv} seed={seed}")
+    gens, keys, vals, cals = _setup(w, n_kv, cal_keys, iters, seed)
     cache = _cache(w)
     import_calibration(cache, cals, w.dtype)
     cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
@@ -264,17 +267,18 @@ def test_determinism():
 # wm_layer at 9000 Keys (256 centroids, at least 32 Keys per centroid) takes
 # the pruned assignment after the first iteration; the others run the full
 # pass (the pruned pass needs 128 or more centroids).
-@pytest.mark.parametrize("name,heads,n_keys,iters", [("tiny", 1, 1024, 10), ("video_chunk", 4, 1760, 4),
-                                                     ("video_chunk", 2, 4000, 4), ("wm_layer", 2, 1560, 4),
-                                                     ("wm_layer", 2, 9000, 4)])
-def test_build_calibration(name, heads, n_keys, iters):
+@pytest.mark.parametrize("name,heads,n_keys,iters,seed", [("tiny", 1, 1024, 10, 0), ("video_chunk", 4, 1760, 4, 0),
+                                                          ("video_chunk", 2, 4000, 4, 0), ("wm_layer", 2, 1560, 4, 0),
+                                                          ("wm_layer", 2, 9000, 4, 0), ("wm_layer", 1, 9000, 3, 1),
+                                                          ("video_chunk", 2, 1760, 4, 2)])
+def test_build_calibration(name, heads, n_keys, iters, seed):
     """GPU-built calibration: S_G bit-exact (exact float64 sums of bf16/fp32
     squares), U_r spans the oracle's subspace (projector within 1e-4), and the
     GPU k-means reaches the oracle's mean QSAC objective within 1% (bf16
     Keys: the oracle's centroids bit for bit)."""
     w = small(W.workload(name), heads=heads)
-    log(f"[build] {name} H={heads} n_keys={n_keys} iters={iters}")
-    gens = [W.HeadGen(w, h) for h in range(heads)]
+    log(f"[build] {name} H={heads} n_keys={n_keys} iters={iters} seed={seed}")
+    gens = [W.HeadGen(w, h, seed) for h in range(heads)]
     qh = [g.hist_queries() for g in gens]
     keys = [g.keys(0, n_keys) for g in gens]
     cache = _cache(w, max_build=n_keys)
