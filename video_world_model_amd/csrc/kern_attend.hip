@@ -90,7 +90,6 @@ __device__ __forceinline__ void load_span(const void* base, int64_t off, float (
   }
 }
 
-// Raw words of N input-dtype values -> floats (bf16: two per word).
 // Value c (0..7) of an 8-value span of raw words: bf16 pairs in one uint4,
 // or float32 in two.
 template <int DT>
@@ -103,29 +102,6 @@ __device__ __forceinline__ float span_elem(const uint4* w, int c) {
     const uint4 v = w[c >> 2];
     const int k = c & 3;
     return __uint_as_float(k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w);
-  }
-}
-
-template <int DT, int N>
-__device__ __forceinline__ void unpack_span(const uint4* w, float (&x)[N]) {
-  if constexpr (DT == 0) {
-#pragma unroll
-    for (int i = 0; i < N / 8; ++i) {
-      const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[8 * i + 2 * k] = __uint_as_float(ww[k] << 16);
-        x[8 * i + 2 * k + 1] = __uint_as_float(ww[k] & 0xFFFF0000u);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      x[4 * i] = __uint_as_float(w[i].x);
-      x[4 * i + 1] = __uint_as_float(w[i].y);
-      x[4 * i + 2] = __uint_as_float(w[i].z);
-      x[4 * i + 3] = __uint_as_float(w[i].w);
-    }
   }
 }
 

@@ -210,33 +210,6 @@ __device__ __forceinline__ float assign_cost(const float (&kf)[D], const float* 
     return qsac_cost<D>(kf, crow, SG);
 }
 
-template <int D, int DT>
-__device__ __forceinline__ void load_row(const void* base, int64_t off, float (&x)[D]) {
-  if constexpr (DT == 0) {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      const uint4 w = p[i];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[8 * i + 2 * k] = __uint_as_float(ww[k] << 16);
-        x[8 * i + 2 * k + 1] = __uint_as_float(ww[k] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      const float4 w = p[i];
-      x[4 * i] = w.x;
-      x[4 * i + 1] = w.y;
-      x[4 * i + 2] = w.z;
-      x[4 * i + 3] = w.w;
-    }
-  }
-}
-
 // N consecutive input elements (bf16 or float) -> float, 16-byte loads.
 template <int N, int DT>
 __device__ __forceinline__ void load_row_span(const void* base, int64_t off, float (&x)[N]) {
