@@ -47,7 +47,9 @@
  *   on the host before anything is enqueued; a call that fails a check has
  *   no side effect. qwm_last_error() returns a message for the last failure
  *   of the calling thread.
- * - Non-finite inputs are undefined behaviour.
+ * - Non-finite inputs are undefined behaviour, and so are Key and Value
+ *   magnitudes at or above 65504: zero-points, steps and the dequantized
+ *   k and v are fp16.
  */
 #ifndef QWM_H_
 #define QWM_H_

@@ -108,6 +108,76 @@ def test_quantize_half_integer_ties(name):
     compare_records(dec, 0, rec)
     log(f"  {name}: codes equal the oracle's over {256 * w.head_dim} Key and Value channels")
 
+def _degenerate_rows(rng, n, d, dtype, C):
+    """Rows whose 32-channel groups are edge cases of the quantizer: constant
+    groups (zero range: step 0, codes 0), tiny magnitudes (fp16 zero-points
+    and steps in the subnormal range), one outlier among zeros, signed zeros,
+    large magnitudes (steps near 10^4), plain values, and whole rows equal to
+    a centroid (zero residual)."""
+    rows = np.empty((n, d), np.float32)
+    for t in range(n):
+        if t % 7 == 6:
+            rows[t] = C[rng.integers(0, C.shape[0])]
+            continue
+        for g0 in range(0, d, 32):
+            kind = rng.integers(0, 6)
+            if kind == 0:
+                x = np.full(32, rng.choice([0.0, -1.5, 0.3125, 7.0]), np.float32)
+            elif kind == 1:
+                x = (rng.standard_normal(32) * 1e-6).astype(np.float32)
+            elif kind == 2:
+                x = np.zeros(32, np.float32)
+                x[rng.integers(0, 32)] = rng.choice([-1.0, 1.0]) * rng.uniform(0.5, 50.0)
+            elif kind == 3:
+                x = np.where(rng.integers(0, 2, 32) == 1, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+            elif kind == 4:
+                x = (rng.standard_normal(32) * 1e4).astype(np.float32)
+            else:
+                x = rng.standard_normal(32).astype(np.float32)
+            rows[t, g0:g0 + 32] = x
+    if dtype == "bf16":
+        rows = W.round_to_bf16(rows)
+    assert np.all(np.isfinite(rows))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["tiny", "video_chunk"])
+def test_quantize_degenerate_groups(name):
+    """Quantize-append and attention over Keys and Values made of degenerate
+    groups: the records equal the oracle's bit for bit and the outputs stay
+    within 1e-3 of its rows."""
+    n = 448
+    w = small(W.workload(name), heads=1, n_kv=n, n_q=64)
+    rng = np.random.default_rng(11)
+    g = W.HeadGen(w, 0)
+    C = W.round_to_bf16(g.keys(0, w.n_centroids)) if w.dtype == "bf16" else g.keys(0, w.n_centroids)
+    S = O.sensitivity(g.hist_queries(), w.group)
+    U = O.subspace(g.hist_queries(), w.rank)
+    cals = [(C, S, U)]
+    keys = [_degenerate_rows(rng, n, w.head_dim, w.dtype, C)]
+    vals = [_degenerate_rows(rng, n, w.head_dim, w.dtype, C)]
+    cache = _cache(w)
+    import_calibration(cache, cals, w.dtype)
+    cache.quantize_append(to_dev(keys, w.dtype), to_dev(vals, w.dtype))
+    dec = cache.decode_export(cache.export().cpu().numpy(), n)
+    rec = O.quantize_tokens(keys[0], vals[0], C, S, U, w.group)
+    compare_records(dec, 0, rec)
+    q = [g.current_queries()[:w.n_q]]
+    out = cache.attend(to_dev(q, w.dtype)).cpu().numpy()
+    ref = O.attend(q[0], _oracle_heads(w, keys, vals, cals)[0], None, None, mask="none")
+    assert np.all(np.isfinite(out[0]))
+    # the spread of logits is in the tens of thousands: some rows put all
+    # their weight on a token whose Values are zero, so the reference row is
+    # exactly 0 and the relative measure is undefined; those rows must be
+    # (near) zero on the GPU too
+    zero = np.abs(ref).max(axis=1) == 0
+    e = row_rel_err(out[0][~zero], ref[~zero])
+    log(f"  {name}: degenerate groups: records equal the oracle's, worst row error {e.max():.3e}, "
+        f"{int(zero.sum())} all-zero rows")
+    assert e.max() <= ROW_TOL
+    assert np.abs(out[0][zero]).max(initial=0.0) <= 1e-6
+
+
 def _oracle_heads(w, keys, vals, cals):
     hcs = []
     for h in range(w.heads):
