@@ -699,8 +699,14 @@ __global__ __launch_bounds__(256) void top1_merge_kernel(const AttnArgs a) {
   a.top1[row] = bi;
 }
 
-// Log-sum-exp merge of the split-KV partials (log2 domain): one thread per
-// (head, Query, 4 channels), every split's partial row read once.
+// Log-sum-exp merge of the split-KV partials (log2 domain), two shapes:
+// merge_kernel runs one thread per (head, Query, 4 channels) over every
+// split, for many rows and few splits (the prefill path); merge_rows_kernel
+// runs one workgroup per (head, Query) row with thread = (4 channels, split
+// group), split group sg taking splits sg, sg + SG, ... with a running
+// maximum of its own, and combines the SG partial sums in group order
+// through LDS, for few rows and many splits (the decode path: up to 64).
+// Every split's partial row is read once.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -722,6 +728,66 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnArgs a) {
     o.y += po.y * w;
     o.z += po.z * w;
     o.w += po.w * w;
+  }
+  const float inv = 1.0f / L;
+  *reinterpret_cast<float4*>(a.out + row * D + 4 * c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+}
+
+constexpr int kMergeRowThreads = 512;
+
+template <int D>
+__global__ __launch_bounds__(kMergeRowThreads) void merge_rows_kernel(const AttnArgs a) {
+  constexpr int CQ = D / 4;                   // channel quads per row
+  constexpr int SG = kMergeRowThreads / CQ;  // split groups
+  __shared__ float4 red_o[SG][CQ];
+  __shared__ float red_l[SG][CQ], red_m[SG][CQ];
+  const int64_t row = blockIdx.x;  // h * nq + qi
+  const int64_t rows = (int64_t)a.H * a.nq;
+  const int c4 = threadIdx.x % CQ, sg = threadIdx.x / CQ;
+  // each split group keeps its own running maximum (partials rescaled when
+  // it grows), so no thread has to read every split's maximum first
+  float mg = -__builtin_inff(), L = 0.0f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = sg; s < a.splits; s += SG) {
+    const int64_t pr = s * rows + row;
+    const float m = a.part_ml[pr * 2];
+    if (m > mg) {
+      const float f = (mg == -__builtin_inff()) ? 0.0f : exp2f(mg - m);
+      L *= f;
+      o.x *= f;
+      o.y *= f;
+      o.z *= f;
+      o.w *= f;
+      mg = m;
+    }
+    const float w = (m == -__builtin_inff()) ? 0.0f : exp2f(m - mg);
+    L += a.part_ml[pr * 2 + 1] * w;
+    const float4 po = *reinterpret_cast<const float4*>(a.part_o + pr * D + 4 * c4);
+    o.x += po.x * w;
+    o.y += po.y * w;
+    o.z += po.z * w;
+    o.w += po.w * w;
+  }
+  red_o[sg][c4] = o;
+  red_l[sg][c4] = L;
+  red_m[sg][c4] = mg;
+  __syncthreads();
+  if (sg != 0) return;
+  float M = mg;
+#pragma unroll
+  for (int g = 1; g < SG; ++g) M = fmaxf(M, red_m[g][c4]);
+  o = make_float4(0.f, 0.f, 0.f, 0.f);
+  L = 0.0f;
+#pragma unroll
+  for (int g = 0; g < SG; ++g) {
+    const float m = red_m[g][c4];
+    const float f = (m == -__builtin_inff()) ? 0.0f : exp2f(m - M);
+    const float4 p = red_o[g][c4];
+    o.x += p.x * f;
+    o.y += p.y * f;
+    o.z += p.z * f;
+    o.w += p.w * f;
+    L += red_l[g][c4] * f;
   }
   const float inv = 1.0f / L;
   *reinterpret_cast<float4*>(a.out + row * D + 4 * c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
@@ -830,12 +896,20 @@ hipError_t launch_top1_merge(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(int D, const AttnArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.H * a.nq * (D / 4);
-  dim3 grid((unsigned)((n + 255) / 256)), block(256);
-  if (D == 128)
-    hipLaunchKernelGGL((merge_kernel<128>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((merge_kernel<64>), grid, block, 0, s, a);
+  const int64_t rows = (int64_t)a.H * a.nq;
+  if (a.splits >= 16) {  // few rows, many splits: a workgroup per row
+    dim3 grid((unsigned)rows), block(kMergeRowThreads);
+    if (D == 128)
+      hipLaunchKernelGGL((merge_rows_kernel<128>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_rows_kernel<64>), grid, block, 0, s, a);
+  } else {
+    dim3 grid((unsigned)((rows * (D / 4) + 255) / 256)), block(256);
+    if (D == 128)
+      hipLaunchKernelGGL((merge_kernel<128>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<64>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
