@@ -34,14 +34,17 @@
  * - The library allocates nothing. All of its state lives in a caller
  *   supplied device arena of qwm_arena_bytes() bytes (e.g. a torch uint8
  *   tensor). The handle itself is a small host object.
- * - Work is enqueued on the HIP stream given at qwm_create and every call is
- *   asynchronous with respect to the host; the caller keeps input buffers
- *   alive until the stream has passed the call. No call synchronizes. The one
- *   exception to the single stream is the eigensolve of qwm_build_subspace,
- *   which runs on a stream of the library's own (default priority) so that
- *   later work overlaps it; the cache stream waits for it before the staged
- *   calibration is committed, imported over or exported, and before the next
- *   qwm_build_subspace.
+ * - Work is enqueued on the HIP stream given at qwm_create; the caller keeps
+ *   input buffers alive until that stream has passed the call (every read of
+ *   a caller buffer is enqueued on it). Two calls block the host:
+ *   qwm_profile_read waits for the timing events it reads, and qwm_destroy
+ *   waits for the eigensolve stream (when one was started) before releasing
+ *   it. Every other call only enqueues work. The one exception
+ *   to the single stream is the eigensolve of qwm_build_subspace, which
+ *   reads arena memory only and runs on a stream of the library's own
+ *   (default priority) so that later work overlaps it; the cache stream
+ *   waits for it before the staged calibration is committed, imported over
+ *   or exported, and before the next qwm_build_subspace.
  * - A handle is not thread-safe; calls on one handle must not overlap.
  * - Every call returns a qwm_status and never throws. Arguments are checked
  *   on the host before anything is enqueued; a call that fails a check has

@@ -78,6 +78,18 @@ def test_arena_bytes_accounts_for_every_region():
     assert nbytes % 256 == 0
 
 
+def _device_may_be_visible() -> bool:
+    """True where a HIP device could be found. The handles below sit on a fake
+    arena address, so a call that passes every check would enqueue kernels
+    against unmapped memory on such a host: those calls are made only where
+    no device exists, where they must fail with QWM_ERR_HIP after their
+    checks. (Counting devices does not initialize the runtime.)"""
+    if os.path.exists("/dev/kfd"):
+        return True
+    import torch
+    return torch.cuda.device_count() > 0
+
+
 def _handle(**kw):
     d = _desc(**kw)
     h = ctypes.c_void_p()
@@ -140,19 +152,21 @@ def test_call_order_and_argument_checks():
 
 def test_mode_state_rules_and_top1_checks():
     """build_centroids needs a staged subspace except for the nearest-centroid
-    rule at rank 0 (QVG), which then gets past the state check and fails only
-    for want of a device. qwm_attend_top1 checks its arguments first."""
+    rule at rank 0 (QVG), which then gets past the state check and, on a host
+    without a device, fails only for want of one. qwm_attend_top1 checks its
+    arguments first. Every call that could pass all checks is skipped where
+    a device may exist (the handles' arena address is fake)."""
     L = Q.lib()
     P = ctypes.c_void_p(4096)
     top = ctypes.c_void_p(8192)
+    no_device = not _device_may_be_visible()
     for kw, status in ((dict(), Q.QWM_ERR_STATE), (dict(rank=0), Q.QWM_ERR_STATE),
                        (dict(objective=1), Q.QWM_ERR_STATE), (dict(rank=0, objective=1), None)):
         h = _handle(**kw)
-        st = L.qwm_build_centroids(h, P, 100, 3)
-        if status is None:
-            assert st in (Q.QWM_OK, Q.QWM_ERR_HIP), Q.last_error()
-        else:
-            assert st == status
+        if status is not None:
+            assert L.qwm_build_centroids(h, P, 100, 3) == status
+        elif no_device:  # past the state check, stopped only by the missing device
+            assert L.qwm_build_centroids(h, P, 100, 3) == Q.QWM_ERR_HIP, Q.last_error()
         assert L.qwm_destroy(h) == Q.QWM_OK
     h = _handle()
     assert L.qwm_attend_top1(h, P, 4, None, 0, top) == Q.QWM_ERR_STATE  # empty cache
@@ -166,7 +180,8 @@ def test_mode_state_rules_and_top1_checks():
     assert L.qwm_import_calibration(h, P, P, None) == Q.QWM_ERR_INVALID_ARG
     assert L.qwm_destroy(h) == Q.QWM_OK
     h = _handle(rank=0, objective=1)
-    assert L.qwm_import_calibration(h, P, None, None) in (Q.QWM_OK, Q.QWM_ERR_HIP)
+    if no_device:  # a valid import; only the missing device stops it
+        assert L.qwm_import_calibration(h, P, None, None) == Q.QWM_ERR_HIP, Q.last_error()
     assert L.qwm_destroy(h) == Q.QWM_OK
 
 

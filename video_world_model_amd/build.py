@@ -12,6 +12,7 @@ emitting packed float32 VALU instructions.
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -43,6 +44,28 @@ CFLAGS = [
 ]
 
 
+def source_files():
+    """Every file the library is compiled from, as (path relative to the repo, absolute path)."""
+    files = [("include/qwm.h", os.path.join(INCLUDE, "qwm.h"))]
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            files.append((f"video_world_model_amd/csrc/{f}", os.path.join(CSRC, f)))
+    return files
+
+
+def source_hash() -> str:
+    """First 16 hex digits of a SHA-256 over the library's sources (name and
+    bytes of each file, in name order). The build stamps it into
+    qwm_version(), so a loaded library can be matched against the tree."""
+    h = hashlib.sha256()
+    for rel, path in source_files():
+        h.update(rel.encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -62,12 +85,13 @@ def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link libqwm.so; returns its path."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
+    stamp = f'-DQWM_SOURCE_HASH="{source_hash()}"'
     objs = []
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *CFLAGS, stamp, "-c", os.path.join(CSRC, src), "-o", obj])
     workers = min(len(cmds), int(os.environ.get("MAX_JOBS", "4")) or 1)
     with ThreadPoolExecutor(max_workers=workers) as ex:
         outs = list(ex.map(_run, cmds))

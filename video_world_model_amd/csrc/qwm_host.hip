@@ -144,7 +144,8 @@ struct qwm_cache {
   // The eigensolve of build_subspace runs on `side` (created on first use,
   // default priority) so the k-means of build_centroids, which needs only the
   // sensitivity, overlaps it; `stream` waits for `join_ev` before the staged
-  // U is read or the Gram buffer is written again.
+  // U is read or the Gram buffer is written again. The eigensolve reads
+  // arena memory only, never a caller buffer.
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   bool side_pending = false;
@@ -380,7 +381,12 @@ qwm_status attend_decode(qwm_cache* c, const void* q, int64_t n_q, float softmax
 extern "C" {
 
 const char* qwm_last_error(void) { return g_last_error.c_str(); }
-const char* qwm_version(void) { return "qwm 0.1 gfx950"; }
+#ifndef QWM_SOURCE_HASH
+#define QWM_SOURCE_HASH "unstamped"
+#endif
+// "qwm <version> gfx950 src:<hash>": the hash covers every source file of the
+// library (video_world_model_amd/build.py computes and stamps it).
+const char* qwm_version(void) { return "qwm 0.2 gfx950 src:" QWM_SOURCE_HASH; }
 
 qwm_status qwm_arena_bytes(const qwm_desc* desc, size_t* bytes) {
   qwm_status st = check_desc(desc);
@@ -476,8 +482,10 @@ qwm_status qwm_build_subspace(qwm_cache* c, const void* q_hist, int64_t n_hist) 
   if ((e = c->join_side()) != hipSuccess) return fail_hip(e, "join eigensolve");
   const int st_slot = c->staged();
   const int nchunk = qwm::gram_chunks(n_hist);
-  // The sensitivity needs only the Gram diagonal: it is formed on the cache
-  // stream, while the full Gram and the eigensolve run on `side`.
+  // Every read of q_hist stays on the cache stream (the caller may release
+  // it once that stream has passed this call): the Gram diagonal and the
+  // sensitivity, then the full Gram. Only the eigensolve, which reads arena
+  // memory alone, runs on `side`, overlapping the k-means that follows.
   e = c->run(QWM_K_GRAM, [&] {
     return qwm::launch_diag(c->D, c->dtype, q_hist, n_hist, c->H, c->diag(), c->stream);
   });
@@ -490,12 +498,12 @@ qwm_status qwm_build_subspace(qwm_cache* c, const void* q_hist, int64_t n_hist) 
     c->staged_subspace = true;
     return QWM_OK;
   }
-  if ((e = hipEventRecord(c->fork_ev, c->stream)) != hipSuccess) return fail_hip(e, "fork eigensolve");
-  if ((e = hipStreamWaitEvent(c->side, c->fork_ev, 0)) != hipSuccess) return fail_hip(e, "fork eigensolve");
-  e = c->run_on(c->side, QWM_K_GRAM, [&] {
-    return qwm::launch_gram(c->D, c->dtype, q_hist, n_hist, c->H, c->gram(), c->side);
+  e = c->run(QWM_K_GRAM, [&] {
+    return qwm::launch_gram(c->D, c->dtype, q_hist, n_hist, c->H, c->gram(), c->stream);
   });
   if (e != hipSuccess) return fail_hip(e, "gram");
+  if ((e = hipEventRecord(c->fork_ev, c->stream)) != hipSuccess) return fail_hip(e, "fork eigensolve");
+  if ((e = hipStreamWaitEvent(c->side, c->fork_ev, 0)) != hipSuccess) return fail_hip(e, "fork eigensolve");
   e = c->run_on(c->side, QWM_K_EIGEN, [&] {
     return qwm::launch_eigen(c->D, c->gram(), nchunk, c->H, c->r, c->slotU(st_slot), c->side);
   });

@@ -103,6 +103,27 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+def version() -> str:
+    return lib().qwm_version().decode()
+
+
+def loaded_source_hash() -> str:
+    """Source hash stamped into the loaded library ("" when unstamped)."""
+    v = version()
+    return v.split("src:", 1)[1] if "src:" in v else ""
+
+
+def check_build() -> str:
+    """Raise unless the loaded library was built from the sources in this
+    tree; returns the hash."""
+    from video_world_model_amd.build import source_hash
+    want, got = source_hash(), loaded_source_hash()
+    if got != want:
+        raise RuntimeError(f"{LIB_PATH} was built from other sources (library src:{got or 'none'}, tree src:{want}); "
+                           "rebuild with `python -m video_world_model_amd.build`")
+    return got
+
+
 def last_error() -> str:
     return lib().qwm_last_error().decode()
 
