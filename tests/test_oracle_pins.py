@@ -285,6 +285,26 @@ def test_int2_half_step_bound_and_coverage():
     assert codes.max() <= 3
 
 
+def test_int2_half_integer_ties_golden():
+    """Hand-derived fixture (tests/golden/int2_ties.json): quotients of exactly
+    0.5, 1.5 and 2.5 go to the even code (0, 2, 2). Run through the plain
+    quantizer and through quantize-on-insert, as the Key residual (one
+    all-zero centroid, so r = k) and as the Value."""
+    fx = _load("int2_ties.json")
+    x = np.array(fx["x"], np.float32)
+    codes, zp, sc = O.int2_quantize(x, fx["g"])
+    assert codes.tolist() == fx["codes"]
+    assert [[_f16_hex(v) for v in row] for row in zp] == fx["zp_f16_hex"]
+    assert [[_f16_hex(v) for v in row] for row in sc] == fx["step_f16_hex"]
+    d = x.shape[1]
+    rec = O.quantize_tokens(x, x, np.zeros((1, d), np.float32), np.ones(d // fx["g"], np.float32),
+                            np.zeros((d, 0), np.float32), fx["g"])
+    for code_f, zp_f, sc_f in (("kcode", "kzp", "kscale"), ("vcode", "vzp", "vscale")):
+        assert rec[code_f].tolist() == fx["codes"]
+        assert [[_f16_hex(v) for v in row] for row in rec[zp_f]] == fx["zp_f16_hex"]
+        assert [[_f16_hex(v) for v in row] for row in rec[sc_f]] == fx["step_f16_hex"]
+
+
 def test_int2_grid_values_reproduce_exactly():
     """Values built on a fp16-exact grid with codes 0 and 3 present in every
     group come back bit for bit; constant groups give scale 0 and codes 0."""
