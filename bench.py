@@ -1,31 +1,31 @@
 #!/usr/bin/env python3
 """Throughput of the QuantWM 2-bit KV-cache hot path on one MI355X.
 
-One step is one pass of the whole path over one chunk of synthetic input:
-  1. build_subspace   -- Gram of the historical Queries, eigensolve
-                         (PSAC basis U_r) and QSAC sensitivity S_G;
-  2. build_centroids  -- QSAC k-means (seeding + 10 Lloyd iterations);
-  3. quantize_append  -- QSAC assignment, INT2 residual, PSAC coefficients
-                         and INT2 Values for every cached token;
-  4. attend           -- the Query chunk attends to the 2-bit cache (with
-                         the PSAC logit term) plus its own bf16 K/V.
-The default workload is the "small video chunk": 12 heads, head_dim 128,
-8 frames x 880 tokens cached, 64 centroids, rank 8, one 880-Query frame.
+Default workload: the streaming-insert step. A 100,000-token cache of 40
+heads (head_dim 128, 256 centroids, PSAC rank 16, 9 calibration epochs
+refreshed every 8 frames) is built once, untimed, with GPU calibration at
+every epoch boundary. One step is
+  1. quantize_append  -- QSAC assignment, INT2 residual, PSAC coefficients
+                         and INT2 Values of one new 1,560-token frame;
+  2. attend           -- a 1,560-Query chunk attends to all 101,560 cached
+                         tokens (PSAC logit term per epoch).
+Before every timed step a write of --flush-mib MiB (default 1024) evicts the
+L2 caches and the 256 MB MALL, outside the timed region; each step is timed
+with HIP events on the library's stream. The every-8-frames refresh (subspace
+from 12,480 historical Queries, 10-iteration centroid build) is timed apart
+and reported per refresh and per frame.
 
---mode picks the method: "quantwm" (QSAC + PSAC, the default), "qvg" (the
-baseline of the article's "Step 1": nearest centroid, no compensation, no
-historical Queries, so step 1 is skipped), or the two ablations "qsac"
-(PSAC off), "nearest-psac", and "postq" (centroids chosen by the weighted
-error the INT2 quantization actually leaves). After the timed steps the run also reports
-the top-1 change rate of the article's "Table 1" analysis: the share of
-(head, Query) pairs whose top-scoring cached token differs from the one
-full-precision Keys give.
+Other workloads (--workload): video_chunk (a whole step of calibration,
+quantize-append of 7,040 tokens and attention of 880 Queries with their own
+K/V; --mode picks QVG and the ablations), wm_layer, long_horizon (attention
+over a prebuilt 131,072-token cache; decode-shaped with --nq <= 64).
 
 Prints ONE JSON line. `value` = cache token-heads attended per second of
-whole-step time (H * N_kv / t_step). Per-kernel times come from HIP events
-the library records around each launch on its stream during the timed
-steps; `roofline` reports the kernel that takes the most time against the
-MI355X peak of the unit that bounds it.
+step time (H * N_kv / t_step). `roofline` reports the kernel with the most
+time per step against the MI355X peak of the unit that bounds it; its
+average launch time comes from HIP events the library records on its own
+stream. `cpu_baseline` is the CPU oracle timed on the host's cores on a
+stated sample of the same step.
 """
 
 from __future__ import annotations
@@ -169,6 +169,132 @@ def cpu_baseline(w: W.Workload, n_heads: int, objective: str, r: int):
     }
 
 
+def _oracle_stream_epoch(args):
+    """One epoch of one head of the streaming cache, built by the oracle
+    (untimed set-up): calibration from the epoch's historical Queries and
+    first frame, then its tokens of the 100,000-token base cache."""
+    name, head, e = args
+    from threadpoolctl import threadpool_limits
+
+    import oracle.qwm_oracle as O
+    w = W.workload(name)
+    hg = W.HeadGen(w, head)
+    base = w.n_kv - w.n_append
+    s0, s1 = w.epoch_start(e), min(w.epoch_end(e), base)
+    a0, a1 = w.centroid_keys_range(e)
+    with threadpool_limits(1):
+        qh = hg.hist_queries(e)
+        S = O.sensitivity(qh, w.group)
+        U = O.subspace(qh, w.rank)
+        C = O.build_centroids(hg.keys(a0, a1), S, w.n_centroids, w.group, w.kmeans_iters, w.dtype)
+        hc = O.HeadCache(w.group, w.dtype)
+        hc.add_epoch(C, S, U)
+        hc.append(hg.keys(s0, s1), hg.values(s0, s1))
+    return head, e, (C, S, U), hc.records[0][1]
+
+
+# Oracle head caches of the streaming base cache, filled before the step
+# workers are forked (they inherit them).
+_STREAM_CACHES = {}
+
+
+def _oracle_stream_step(args):
+    """The timed oracle work of one (head, slice) of a streaming step: the
+    append of the slice's share of the new frame (HeadCache.append:
+    quantize-on-insert of those tokens), then the attention of the slice's
+    share of the Query chunk over the whole 101,560-token cache. Between the
+    two, untimed, the frame is appended whole in token order so that the
+    attention sees the GPU step's cache."""
+    name, head, j, nsl, nq = args
+    from threadpoolctl import threadpool_limits
+
+    import oracle.qwm_oracle as O
+    w = W.workload(name)
+    hg = W.HeadGen(w, head)
+    hc = _STREAM_CACHES[head]
+    base = w.n_kv - w.n_append
+    cuts = [base + (w.n_append * i) // nsl for i in range(nsl + 1)]
+    qcuts = [(nq * i) // nsl for i in range(nsl + 1)]
+    q = hg.queries(W.Q_CURRENT, nq)[qcuts[j]:qcuts[j + 1]]
+    tq = 0.0
+    with threadpool_limits(1):
+        if w.n_append:
+            k = [hg.keys(cuts[i], cuts[i + 1]) for i in range(nsl)]
+            v = [hg.values(cuts[i], cuts[i + 1]) for i in range(nsl)]
+            n_rec = len(hc.records)
+            t0 = time.perf_counter()
+            hc.append(k[j], v[j])
+            tq = time.perf_counter() - t0
+            del hc.records[n_rec:]
+            hc.length = base
+            for i in range(nsl):
+                hc.append(k[i], v[i])
+        t0 = time.perf_counter()
+        O.attend(q, hc)
+        ta = time.perf_counter() - t0
+    return tq, ta
+
+
+def cpu_baseline_streaming(w: W.Workload, n_heads: int, cores: int, nq: int = 0):
+    """The oracle's step of a multi-epoch workload (streaming: append one
+    frame and attend; long_horizon: attend only) on `n_heads` heads over
+    `cores` forked processes (one per core, run before the GPU is
+    initialized): each head's frame and Query chunk are cut into
+    cores / n_heads slices, one process per (head, slice). Each head's base
+    cache is built first by the oracle, untimed, one process per (head,
+    epoch)."""
+    nq = nq or w.n_q
+    import multiprocessing as mp
+
+    import oracle.qwm_oracle as O
+    n_heads = max(1, min(n_heads, w.heads))
+    nsl = max(1, cores // n_heads)
+    ctx = mp.get_context("fork")
+    base = w.n_kv - w.n_append
+    n_ep = -(-base // w.epoch_tokens)
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        parts = pool.map(_oracle_stream_epoch, [(w.name, h, e) for h in range(n_heads) for e in range(n_ep)])
+    t_setup = time.perf_counter() - t0
+    for h in range(n_heads):
+        # the oracle's HeadCache, filled with the per-epoch results in order
+        # (what add_epoch and append would have produced one after the other)
+        hc = O.HeadCache(w.group, w.dtype)
+        for hh, e, cal, rec in sorted(parts, key=lambda x: (x[0], x[1])):
+            if hh != h:
+                continue
+            hc.epochs.append((hc.length, *cal))
+            rec["epoch"] = np.full(len(rec["ids"]), e, np.int64)
+            hc.records.append((hc.length, rec))
+            hc.length += len(rec["ids"])
+        assert hc.length == base
+        _STREAM_CACHES[h] = hc
+    del parts
+    t0 = time.perf_counter()
+    with ctx.Pool(n_heads * nsl) as pool:
+        res = pool.map(_oracle_stream_step, [(w.name, h, j, nsl, nq) for h in range(n_heads) for j in range(nsl)])
+    wall = time.perf_counter() - t0
+    _STREAM_CACHES.clear()
+    per = [tq + ta for tq, ta in res]
+    busy = max(per)
+    return {
+        "value": n_heads * w.n_kv / busy,
+        "unit": "KV tokens/s",
+        "cores": n_heads * nsl,
+        "kind": "oracle",
+        "sample": (f"the {w.name} step ("
+                   + (f"quantize-append of the {w.n_append}-token frame, " if w.n_append else "")
+                   + f"attention of {nq} Queries over {w.n_kv} tokens) on {n_heads} of {w.heads} heads; each head's "
+                   f"work cut into {nsl} slices, one forked process per (head, slice), BLAS 1 thread; "
+                   f"value = {n_heads} heads x {w.n_kv} tokens / slowest process ({busy:.2f} s: append "
+                   f"{max(r[0] for r in res):.2f} s + attention {max(r[1] for r in res):.2f} s at most); "
+                   f"pool wall {wall:.2f} s; the oracle built the {base}-token base caches first "
+                   f"({t_setup:.1f} s, untimed)"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "numpy": np.__version__,
+    }
+
+
 # ----------------------------------------------------------------- GPU
 
 def _build_epochs(cache, w, gens, dev, n_tokens):
@@ -201,16 +327,73 @@ def _kernel_times(cache, steps):
     return kern
 
 
+def _copy_probe(args):
+    """One plain elementwise copy (torch.neg) of --copy-probe-mib MiB: a kernel
+    of known traffic (read and write that many bytes) whose FETCH_SIZE and
+    WRITE_SIZE, in the same profiled run, calibrate the counters."""
+    import torch
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib * (1 << 18), dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+
+def _event_timer(stream, flush):
+    """timed(fn, n): mean milliseconds of n runs of fn, each between two HIP
+    events on `stream`; before each run (outside its events) the flush
+    buffer is rewritten, so the L2 caches and the MALL hold none of the
+    step's data."""
+    import torch
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i, (e0, e1) in enumerate(evs):
+                if flush is not None:
+                    flush.fill_(i & 0xFF)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in evs) / n
+
+    def profiled(cache, fn, n):
+        """n runs of fn with the library's event timing on, flushed the same way."""
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            cache.profile_enable(True)
+            for i in range(n):
+                if flush is not None:
+                    flush.fill_(i & 0xFF)
+                fn()
+        torch.cuda.synchronize()
+        kern = _kernel_times(cache, n)
+        cache.profile_enable(False)
+        return kern
+
+    return timed, profiled
+
+
 def bench_streaming(args, w):
     """The streaming-insert step on the 100,000-token cache (built once,
-    untimed): quantize-append one 1,560-token frame, then attention of a
-    1,560-Query chunk over all 101,560 tokens. The calibration refresh (every
-    8 frames: subspace from the last 8 frames' 12,480 Queries, 10-iteration
-    centroid build on the refresh frame) is timed on its own and reported per
-    refresh and per frame."""
+    untimed, with GPU calibration at every epoch boundary): quantize-append
+    one 1,560-token frame, then attention of a 1,560-Query chunk over all
+    101,560 tokens. The calibration refresh (every 8 frames: subspace from
+    the last 8 frames' 12,480 Queries, 10-iteration centroid build on the
+    refresh frame) is timed on its own and reported per refresh and per
+    frame."""
+    cpu = None
+    if args.cpu_heads > 0:
+        cpu = cpu_baseline_streaming(w, args.cpu_heads, args.cpu_cores or len(os.sched_getaffinity(0)))
     import torch
     from video_world_model_amd import Cache
+    from video_world_model_amd import qwm as Q
+    src_hash = Q.check_build()
     torch.cuda.set_device(0)
+    _copy_probe(args)
     gens = [W.HeadGen(w, h) for h in range(w.heads)]
     base = w.n_kv - w.n_append
     stream = torch.cuda.Stream()
@@ -226,6 +409,9 @@ def bench_streaming(args, w):
         a0, a1 = w.centroid_keys_range(e_last)
         kref = _bf16_dev([g.keys(a0, a1) for g in gens])
         out = torch.empty((w.heads, w.n_q, w.head_dim), dtype=torch.float32, device="cuda")
+        flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda") if args.flush_mib > 0 else None
+    torch.cuda.synchronize()
+    timed, profiled = _event_timer(stream, flush)
 
     def step():
         cache.truncate(base)
@@ -240,23 +426,12 @@ def bench_streaming(args, w):
         cache.build_subspace(qh)
         cache.build_centroids(kref, w.kmeans_iters)
 
-    def timed(fn, steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        with torch.cuda.stream(stream):
-            for _ in range(steps):
-                fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
+    n_ref = max(1, args.steps // 4)
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             refresh()
-        cache.truncate(refresh_at)
-    torch.cuda.synchronize()
-    ms_refresh = timed(refresh, max(1, args.steps // 4))
+    ms_refresh = timed(refresh, n_ref)
+    kref_t = profiled(cache, refresh, n_ref)
     # back to the 100,000-token cache: the last epoch rebuilt the same way
     with torch.cuda.stream(stream):
         cache.truncate(refresh_at)
@@ -265,21 +440,11 @@ def bench_streaming(args, w):
         for _ in range(args.warmup):
             step()
     torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, each flushed before its events
     ms_step = timed(step, args.steps)
-    with torch.cuda.stream(stream):
-        cache.profile_enable(True)
-        for _ in range(args.steps):
-            step()
-    torch.cuda.synchronize()
-    kern = _kernel_times(cache, args.steps)
-    cache.profile_enable(False)
-    with torch.cuda.stream(stream):
-        cache.profile_enable(True)
-        for _ in range(max(1, args.steps // 4)):
-            refresh()
-    torch.cuda.synchronize()
-    kref_t = _kernel_times(cache, max(1, args.steps // 4))
-    cache.profile_enable(False)
+    kern = profiled(cache, step, args.steps)
+    assert cache.length() == w.n_kv and cache.epochs() == w.n_epochs
+    rb, tb = cache.storage_bytes()
 
     B = bytes_per_token_head(w.head_dim, w.group, w.rank)
     tq = kern["quantize"]["avg_launch_ms"] * 1e-3
@@ -294,7 +459,9 @@ def bench_streaming(args, w):
         achieved = a_flops / ta_k / 1e12
         roof = dict(bound="mfma", achieved=achieved, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / MFMA_F16_PEAK_TFLOPS, kernel="attend",
-                    traffic=measured_traffic("attend", w.name))
+                    traffic=measured_traffic("attend", w.name),
+                    work=f"{w.heads} heads x {w.n_q} Queries x {w.n_kv} tokens x (4*{w.head_dim} + 2*{w.rank}) "
+                         f"flops = {a_flops:.4g} per launch")
     else:
         achieved = q_ops / tq / 1e12
         roof = dict(bound="alu", achieved=achieved, peak=QSAC_OPS_PEAK / 1e12, unit="Top/s",
@@ -312,11 +479,12 @@ def bench_streaming(args, w):
         "vs_baseline": None,
         "dtype": "f32-valu+f16-mfma",
         "data": "synthetic",
-        "config": {"workload": w.name, "step": "append 1 frame + attend", "heads": w.heads,
+        "config": {"workload": w.name, "step": "quantize-append 1 frame + attend 1 chunk", "heads": w.heads,
                    "head_dim": w.head_dim, "n_centroids": w.n_centroids, "rank": w.rank, "n_kv": w.n_kv,
-                   "n_append": w.n_append, "n_q": w.n_q, "epochs": w.n_epochs, "input_dtype": w.dtype},
+                   "n_append": w.n_append, "n_q": w.n_q, "epochs": w.n_epochs, "input_dtype": w.dtype,
+                   "flush_mib": args.flush_mib},
         "roofline": roof,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "kernels": kern,
         "phases": {
             "quantize": dict(ms=tq * 1e3, GBps=q_bytes / tq / 1e9, hbm_frac=q_bytes / tq / 1e9 / HBM_PEAK_GBPS,
@@ -327,6 +495,9 @@ def bench_streaming(args, w):
             "refresh": dict(ms=ms_refresh, ms_per_frame=ms_refresh / (w.epoch_tokens // w.frame_tokens),
                             kernels=kref_t),
         },
+        "storage": dict(bytes_per_token_head=B, record_bytes=rb, table_bytes=tb,
+                        compression_vs_bf16=w.heads * w.n_kv * 4 * w.head_dim / (rb + tb)),
+        "lib_source_hash": src_hash,
     }
     print(json.dumps(rec), flush=True)
 
@@ -334,58 +505,38 @@ def bench_streaming(args, w):
 def bench_long_horizon(args, w):
     """Attention over the long-horizon cache (built once per epoch from the
     epoch's historical Queries and first frame, untimed): a step is one
-    qwm_attend of n_q Queries per head, no self segment."""
+    qwm_attend of n_q Queries per head, no self segment, flushed before its
+    events like the streaming step."""
+    nq = args.nq or w.n_q
+    cpu = None
+    if args.cpu_heads > 0:
+        cpu = cpu_baseline_streaming(w, args.cpu_heads, args.cpu_cores or len(os.sched_getaffinity(0)), nq)
     import torch
     from video_world_model_amd import Cache
-    nq = args.nq or w.n_q
+    from video_world_model_amd import qwm as Q
+    src_hash = Q.check_build()
     torch.cuda.set_device(0)
-    if args.copy_probe_mib:
-        src = torch.ones(args.copy_probe_mib * (1 << 18), dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    _copy_probe(args)
     gens = [W.HeadGen(w, h) for h in range(w.heads)]
-
-    def dev(arrs):
-        x = np.ascontiguousarray(np.stack(arrs))
-        return torch.from_numpy(W.bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
-
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         cache = Cache(w.heads, w.head_dim, w.n_centroids, w.rank, w.n_kv, dtype=torch.bfloat16,
                       max_epochs=w.n_epochs, max_query_tokens=max(nq, 16), max_build_tokens=w.frame_tokens)
-        for e in range(w.n_epochs):
-            s0, s1 = w.epoch_start(e), w.epoch_end(e)
-            a0, a1 = w.centroid_keys_range(e)
-            cache.build_subspace(dev([g.hist_queries(e) for g in gens]))
-            cache.build_centroids(dev([g.keys(a0, a1) for g in gens]), w.kmeans_iters)
-            cache.quantize_append(dev([g.keys(s0, s1) for g in gens]), dev([g.values(s0, s1) for g in gens]))
-            torch.cuda.synchronize()
-        q = dev([g.queries(W.Q_CURRENT, nq) for g in gens])
+        _build_epochs(cache, w, gens, _bf16_dev, w.n_kv)
+        q = _bf16_dev([g.queries(W.Q_CURRENT, nq) for g in gens])
         out = torch.empty((w.heads, nq, w.head_dim), dtype=torch.float32, device="cuda")
+        flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda") if args.flush_mib > 0 else None
         for _ in range(args.warmup):
             cache.attend(q, out=out)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            cache.attend(q, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    with torch.cuda.stream(stream):
-        cache.profile_enable(True)
-        for _ in range(args.steps):
-            cache.attend(q, out=out)
-    torch.cuda.synchronize()
-    kern = {}
-    for k in KERNELS:
-        ms, n = cache.profile_read(k)
-        if n:
-            kern[k] = dict(ms_per_step=ms / args.steps, launches_per_step=n / args.steps, avg_launch_ms=ms / n)
-    cache.profile_enable(False)
+    timed, profiled = _event_timer(stream, flush)
+
+    def step():
+        cache.attend(q, out=out)
+
+    ms_step = timed(step, args.steps)
+    kern = profiled(cache, step, args.steps)
+    rb, tb = cache.storage_bytes()
     B = bytes_per_token_head(w.head_dim, w.group, w.rank)
     attend_bytes = w.heads * (w.n_kv * B + nq * w.head_dim * 2 + nq * w.head_dim * 4)
     attend_flops = w.heads * nq * w.n_kv * (4 * w.head_dim + 2 * w.rank)
@@ -393,11 +544,15 @@ def bench_long_horizon(args, w):
     decode = nq <= 64
     if decode:
         achieved = attend_bytes / ta / 1e9
-        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS)
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS,
+                    work=f"{w.heads} heads x ({w.n_kv} tokens x {B} B + {nq} Queries x {w.head_dim} x (2 + 4) B) "
+                         f"= {attend_bytes:.4g} B per launch")
     else:
         achieved = attend_flops / ta / 1e12
         roof = dict(bound="mfma", achieved=achieved, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / MFMA_F16_PEAK_TFLOPS)
+                    frac=achieved / MFMA_F16_PEAK_TFLOPS,
+                    work=f"{w.heads} heads x {nq} Queries x {w.n_kv} tokens x (4*{w.head_dim} + 2*{w.rank}) flops "
+                         f"= {attend_flops:.4g} per launch")
     roof["kernel"] = "decode" if decode else "attend"
     roof["traffic"] = measured_traffic(roof["kernel"], f"{w.name}_nq{nq}" if args.nq else w.name)
     rec = {
@@ -415,12 +570,16 @@ def bench_long_horizon(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "step": "attend", "heads": w.heads, "head_dim": w.head_dim,
                    "n_centroids": w.n_centroids, "rank": w.rank, "n_kv": w.n_kv, "n_q": nq, "epochs": w.n_epochs,
-                   "input_dtype": w.dtype},
+                   "input_dtype": w.dtype, "flush_mib": args.flush_mib},
         "roofline": roof,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "kernels": kern,
         "phases": {"attend": dict(GBps=attend_bytes / ta / 1e9, hbm_frac=attend_bytes / ta / 1e9 / HBM_PEAK_GBPS,
+                                  mfma_frac=attend_flops / ta / 1e12 / MFMA_F16_PEAK_TFLOPS,
                                   ms=ta * 1e3, pair_per_s=w.heads * nq * w.n_kv / (ms_step * 1e-3))},
+        "storage": dict(bytes_per_token_head=B, record_bytes=rb, table_bytes=tb,
+                        compression_vs_bf16=w.heads * w.n_kv * 4 * w.head_dim / (rb + tb)),
+        "lib_source_hash": src_hash,
     }
     print(json.dumps(rec), flush=True)
 
@@ -430,7 +589,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video_chunk",
+    ap.add_argument("--workload", default="streaming",
                     choices=["tiny", "video_chunk", "wm_layer", "streaming", "long_horizon"],
                     help="streaming: the 100,000-token cache is built once (untimed); a step appends one "
                          "1,560-token frame and attends with 1,560 Queries; the every-8-frames refresh is timed "
@@ -442,6 +601,11 @@ def main():
                     help="1: capture one step in a HIP graph (through torch.cuda.graph) and time its replays; "
                          "0: time eager calls")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's timed sample (0: skip)")
+    ap.add_argument("--cpu-cores", type=int, default=0,
+                    help="processes of the streaming oracle sample (default: one per available core)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB written before every timed step, outside its events, to evict the L2 caches and "
+                         "the 256 MB MALL (streaming and long_horizon; 0: no flush)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg) over this many MiB first, as a known-size "
                          "reference for HBM byte counters")
@@ -463,14 +627,11 @@ def main():
 
     import torch
     from video_world_model_amd import Cache
+    from video_world_model_amd import qwm as Q
 
+    src_hash = Q.check_build()
     torch.cuda.set_device(0)
-    if args.copy_probe_mib:
-        src = torch.ones(args.copy_probe_mib * (1 << 18), dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    _copy_probe(args)
     gens = [W.HeadGen(w, h) for h in range(w.heads)]
 
     def dev(arrs):
@@ -612,6 +773,9 @@ def main():
         "kernels": kern,
         "phases": extras,
         "diagnostics": {"top1_change_rate": top1_rate},
+        "storage": dict(zip(("record_bytes", "table_bytes"), cache.storage_bytes()),
+                        compression_vs_bf16=cache.compression_ratio()),
+        "lib_source_hash": src_hash,
     }
     print(json.dumps(rec), flush=True)
 

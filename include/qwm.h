@@ -113,6 +113,21 @@ typedef struct {
 /* Bytes of device arena a cache with this description needs (alignment 256). */
 qwm_status qwm_arena_bytes(const qwm_desc* desc, size_t* bytes);
 
+/* Bytes the stored state of a cache with this description occupies when it
+ * holds n_tokens tokens per head in n_epochs epochs, from the arena layout:
+ *   record_bytes = heads * n_tokens * (head_dim/4 K codes + head_dim/4 V codes
+ *                  + 4 (head_dim/group) K zero-point|step words + the same for
+ *                  V + 1 centroid id + 2 rank PSAC coefficients),
+ *   table_bytes  = n_epochs * heads * (n_centroids * head_dim centroid values
+ *                  in the cache dtype + 4 (head_dim/group) S_G + 4 head_dim rank U_r).
+ * A bf16 K/V cache of the same tokens takes heads * n_tokens * 4 * head_dim
+ * bytes; their ratio is the compression the roboind.com article reports
+ * ("Figure 4"), which counts centroids, quantization parameters and
+ * compensation data. Host arithmetic only (no device needed).
+ * 0 <= n_tokens <= capacity_tokens, 0 <= n_epochs <= max_epochs. */
+qwm_status qwm_storage_bytes(const qwm_desc* desc, int64_t n_tokens, int32_t n_epochs, size_t* record_bytes,
+                             size_t* table_bytes);
+
 /* Create a cache in `dev_arena` (device memory, 256-byte aligned, at least
  * qwm_arena_bytes bytes, owned by the caller and kept alive until
  * qwm_destroy). `stream` is a hipStream_t (NULL = the default stream). The

@@ -21,7 +21,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     L = Q.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -88,6 +88,33 @@ def _device_may_be_visible() -> bool:
         return True
     import torch
     return torch.cuda.device_count() > 0
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(rank=0), dict(rank=16, n_centroids=256), dict(dtype=Q.QWM_F32, head_dim=64,
+                                                                                      rank=4, n_centroids=16)])
+@pytest.mark.parametrize("n_tokens,n_epochs", [(0, 0), (1, 1), (777, 2), (1000, 2)])
+def test_storage_bytes_equals_the_oracle_accounting(kw, n_tokens, n_epochs):
+    """The library's stored bytes (from its arena layout) give the oracle's
+    compression ratio: packed bytes per token-head plus the per-epoch tables
+    (roboind.com article, "Figure 4": centroids, quantization parameters and
+    compensation data all count)."""
+    import oracle.qwm_oracle as O
+    d = _desc(**kw)
+    rb, tb = Q.storage_bytes(d, n_tokens, n_epochs)
+    H, D, m, r = d.heads, d.head_dim, d.n_centroids, d.rank
+    esz = 2 if d.dtype == Q.QWM_BF16 else 4
+    assert rb == H * n_tokens * O.bytes_per_token_head(D, 32, r)
+    assert tb == n_epochs * H * O.table_bytes_per_head_epoch(D, 32, m, r, esz)
+    if n_tokens and n_epochs:
+        ratio = H * n_tokens * 4 * D / (rb + tb)
+        assert ratio == pytest.approx(O.compression_ratio(n_tokens, D, 32, m, r, esz, n_epochs), rel=1e-12)
+    L = Q.lib()
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.qwm_storage_bytes(ctypes.byref(d), d.capacity_tokens + 1, 0, ctypes.byref(a), ctypes.byref(b)) == \
+        Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_storage_bytes(ctypes.byref(d), 0, d.max_epochs + 1, ctypes.byref(a), ctypes.byref(b)) == \
+        Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_storage_bytes(ctypes.byref(d), 0, 0, None, ctypes.byref(b)) == Q.QWM_ERR_INVALID_ARG
 
 
 def _handle(**kw):

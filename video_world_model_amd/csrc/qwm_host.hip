@@ -59,6 +59,19 @@ qwm_status check_desc(const qwm_desc* d) {
   return QWM_OK;
 }
 
+// Bytes one token of one head occupies in the record regions (K codes, V
+// codes, K params, V params, id, coefficients), and one epoch slot of one
+// head in the calibration regions (C, S, U). make_layout sizes the regions
+// from these, and qwm_storage_bytes reports them.
+int64_t token_record_bytes(const qwm_desc* d) {
+  const int64_t D = d->head_dim, nG = D / qwm::kGroup;
+  return D / 4 + D / 4 + nG * 4 + nG * 4 + 1 + (int64_t)d->rank * 2;
+}
+int64_t epoch_table_bytes(const qwm_desc* d) {
+  const int64_t D = d->head_dim, nG = D / qwm::kGroup, esz = d->dtype == QWM_BF16 ? 2 : 4;
+  return (int64_t)d->n_centroids * D * esz + nG * 4 + D * (int64_t)d->rank * 4;
+}
+
 Layout make_layout(const qwm_desc* d) {
   Layout L{};
   const int64_t H = d->heads, D = d->head_dim, nG = D / qwm::kGroup, m = d->n_centroids, r = d->rank;
@@ -87,9 +100,11 @@ Layout make_layout(const qwm_desc* d) {
   // the attention tile loads read 16 coefficient halves per token whatever r
   // is (those past r are discarded), hence the tail
   L.coef = take((size_t)(H * L.capP * r * 2 + 64));
+  // (the record regions hold token_record_bytes per token-head)
   L.epochC = take((size_t)((E + 1) * H * m * D * esz));
   L.epochS = take((size_t)((E + 1) * H * nG * 4));
   L.epochU = take((size_t)((E + 1) * H * D * r * 4));
+  // (each epoch slot holds epoch_table_bytes per head)
   L.C32 = take((size_t)(H * m * D * 4));
   L.kmC32 = take((size_t)(H * m * D * 4));
   L.U64 = take((size_t)(H * D * r * 8));
@@ -393,6 +408,19 @@ qwm_status qwm_arena_bytes(const qwm_desc* desc, size_t* bytes) {
   if (st != QWM_OK) return st;
   if (!bytes) return fail(QWM_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = make_layout(desc).total;
+  return QWM_OK;
+}
+
+qwm_status qwm_storage_bytes(const qwm_desc* desc, int64_t n_tokens, int32_t n_epochs, size_t* record_bytes,
+                             size_t* table_bytes) {
+  qwm_status st = check_desc(desc);
+  if (st != QWM_OK) return st;
+  if (!record_bytes || !table_bytes) return fail(QWM_ERR_INVALID_ARG, "NULL argument");
+  if (n_tokens < 0 || n_tokens > desc->capacity_tokens)
+    return fail(QWM_ERR_INVALID_ARG, "n_tokens must be in [0, capacity_tokens]");
+  if (n_epochs < 0 || n_epochs > desc->max_epochs) return fail(QWM_ERR_INVALID_ARG, "n_epochs must be in [0, max_epochs]");
+  *record_bytes = (size_t)desc->heads * (size_t)n_tokens * (size_t)token_record_bytes(desc);
+  *table_bytes = (size_t)n_epochs * (size_t)desc->heads * (size_t)epoch_table_bytes(desc);
   return QWM_OK;
 }
 

@@ -64,6 +64,8 @@ _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _SIGS = {
     "qwm_arena_bytes": [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)],
+    "qwm_storage_bytes": [ctypes.POINTER(Desc), _I64, _I32, ctypes.POINTER(ctypes.c_size_t),
+                          ctypes.POINTER(ctypes.c_size_t)],
     "qwm_create": [ctypes.POINTER(Desc), _VP, ctypes.c_size_t, _VP, ctypes.POINTER(_VP)],
     "qwm_destroy": [_VP],
     "qwm_build_subspace": [_VP, _VP, _I64],
@@ -143,6 +145,14 @@ def arena_bytes(desc: Desc) -> int:
     n = ctypes.c_size_t(0)
     check(lib().qwm_arena_bytes(ctypes.byref(desc), ctypes.byref(n)))
     return int(n.value)
+
+
+def storage_bytes(desc: Desc, n_tokens: int, n_epochs: int):
+    """(record bytes, calibration-table bytes) of the stored state at n_tokens
+    tokens per head in n_epochs epochs (qwm_storage_bytes)."""
+    rb, tb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    check(lib().qwm_storage_bytes(ctypes.byref(desc), n_tokens, n_epochs, ctypes.byref(rb), ctypes.byref(tb)))
+    return int(rb.value), int(tb.value)
 
 
 def _ptr(t) -> int:
@@ -269,6 +279,16 @@ class Cache:
         out = torch.empty((self.heads, q.shape[1]), dtype=torch.int32, device=self.device)
         check(lib().qwm_attend_top1(self._h, _ptr(q), q.shape[1], _ptr(k_ref), nref, _ptr(out)))
         return out
+
+    def storage_bytes(self):
+        """(record bytes, calibration-table bytes) the cache holds now."""
+        return storage_bytes(self.desc, self.length(), self.epochs())
+
+    def compression_ratio(self) -> float:
+        """bf16 K/V bytes of the cached tokens over the bytes stored for them,
+        centroids, parameters and PSAC data included."""
+        rb, tb = self.storage_bytes()
+        return self.heads * self.length() * 4 * self.head_dim / (rb + tb)
 
     def length(self) -> int:
         n = _I64(0)
