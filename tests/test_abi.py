@@ -212,6 +212,18 @@ def test_mode_state_rules_and_top1_checks():
     assert L.qwm_destroy(h) == Q.QWM_OK
 
 
+def test_one_hip_runtime_per_process():
+    """Loading the library before anything imported torch must still leave one
+    HIP runtime mapped in the process (torch's), not two."""
+    import subprocess
+    import sys
+    code = ("import video_world_model_amd.qwm as Q; Q.lib(); import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, check=True).stdout
+    libs = eval(out.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
+
+
 def test_no_oracle_in_product_path():
     """The product package never imports the oracle."""
     pkg = os.path.join(ROOT, "video_world_model_amd")

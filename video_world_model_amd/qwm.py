@@ -90,6 +90,11 @@ def lib() -> ctypes.CDLL:
     """Load libqwm.so (built in-tree by video_world_model_amd.build)."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime under the same soname as the one
+        # libqwm.so was linked against. Loading torch first makes libqwm.so
+        # bind to that already-loaded runtime; loaded the other way round the
+        # process would map two HIP runtimes, and the first GPU call crashes.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m video_world_model_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
