@@ -194,6 +194,24 @@ qwm_status qwm_attend(qwm_cache* cache, const void* q, int64_t n_q, const void* 
                       const void* v_self, int64_t n_self, int32_t mask, float softmax_scale,
                       float* out);
 
+/* qwm_attend for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments and result, but the call's scratch (the q . U_r table,
+ * the q . C table of the decode path and the split-KV partials) lives in a
+ * static device array of the library, 64 MiB on each device, instead of the
+ * cache's arena. n_q is bounded by that array, not by max_query_tokens: the
+ * tables need heads * epochs * n_q * 64 bytes (plus heads * epochs *
+ * n_centroids * 16 * ceil(n_q / 16) * 4 on the decode path, n_q <= 64), and
+ * a call whose tables do not fit returns QWM_ERR_CAPACITY before anything is
+ * enqueued; the partials take what is left (fewer KV splits, down to none).
+ * It calls nothing that allocates (no hipMalloc, no hipEventCreate: kernel
+ * timing is not recorded for it). Every call on one device shares the array,
+ * which keeps the previous call's contents (a call writes every entry it
+ * reads, so nothing needs clearing): calls that overlap on one device, from
+ * any caches or streams, race. */
+qwm_status qwm_attend_noalloc(qwm_cache* cache, const void* q, int64_t n_q, const void* k_self,
+                              const void* v_self, int64_t n_self, int32_t mask, float softmax_scale, float* out);
+
 qwm_status qwm_length(const qwm_cache* cache, int64_t* n_tokens);
 qwm_status qwm_epochs(const qwm_cache* cache, int32_t* n_epochs);
 

@@ -21,7 +21,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     L = Q.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -162,6 +162,14 @@ def test_call_order_and_argument_checks():
     assert L.qwm_attend(h, P, 4, P, P, 3, 2, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG  # causal n_self != n_q
     assert L.qwm_attend(h, P, 4, P, None, 4, 1, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG
     assert L.qwm_attend(h, P, 4, None, None, 0, 0, ctypes.c_float(float("nan")), out) == Q.QWM_ERR_INVALID_ARG
+    # the allocation-free attention: the same checks, no max_query_tokens bound
+    assert L.qwm_attend_noalloc(h, P, 4, None, None, 0, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_STATE
+    assert L.qwm_attend_noalloc(h, P, 65, None, None, 0, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_STATE
+    assert L.qwm_attend_noalloc(h, P, (1 << 24) + 1, None, None, 0, 0, ctypes.c_float(0.1), out) == \
+        Q.QWM_ERR_CAPACITY
+    assert L.qwm_attend_noalloc(h, P, 0, None, None, 0, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend_noalloc(h, P, 4, P, P, 3, 2, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_attend_noalloc(h, P, 4, None, None, 0, 0, ctypes.c_float(0.1), None) == Q.QWM_ERR_INVALID_ARG
     assert L.qwm_truncate(h, 1) == Q.QWM_ERR_INVALID_ARG
     assert L.qwm_export_calibration(h, 0, P, None, None) == Q.QWM_ERR_INVALID_ARG
     n = ctypes.c_int64(-1)

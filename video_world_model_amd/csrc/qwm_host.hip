@@ -9,8 +9,19 @@
 #include <string>
 #include <vector>
 
+#include <mutex>
+
 #include "qwm.h"
 #include "qwm_internal.h"
+
+// Scratch of qwm_attend_noalloc: the q . U_r table, the decode path's q . C
+// table and the split-KV partials of one call, in a fixed device array
+// (64 MiB on every device the library runs on, held until the process
+// ends) instead of the caller's arena. In host code `scratch` names a host
+// stand-in; its device address, resolved once per device, is what kernels
+// receive.
+static constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -124,6 +135,25 @@ Layout make_layout(const qwm_desc* d) {
   return L;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Device address of `scratch` on device `dev`, which must be current:
+// hipGetSymbolAddress on first use per device, then the kept pointer.
+qwm_status static_scratch(int dev, uint8_t** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(QWM_ERR_HIP, "no device for the static scratch");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail_hip(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch address");
+    g_scratch_dev[dev] = reinterpret_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return QWM_OK;
+}
+
 struct DeviceGuard {
   int prev = -1, dev;
   explicit DeviceGuard(int d) : dev(d) {
@@ -195,15 +225,17 @@ struct qwm_cache {
   float* part_ml() const { return reinterpret_cast<float*>(arena + L.part_ml); }
 
   // Launch wrapper: optional event timing around one launch on stream `s`.
+  bool no_events = false;  // set by qwm_attend_noalloc: record no timing events
   template <class F>
   hipError_t run_on(hipStream_t s, int kid, F&& f) {
     hipEvent_t a = nullptr, b = nullptr;
-    if (profile) {
+    const bool timed = profile && !no_events;
+    if (timed) {
       if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return hipErrorOutOfMemory;
       (void)hipEventRecord(a, s);
     }
     hipError_t e = f();
-    if (profile) {
+    if (timed) {
       (void)hipEventRecord(b, s);
       pending.push_back({kid, a, b});
     }
@@ -292,7 +324,21 @@ void make_plan(const qwm_cache* c, int64_t nself, bool with_self, qwm::AttnPlan&
     p.tile_prefix[i + 1] = p.tile_prefix[i] + (p.seg_len[i] + qwm::kTileKV - 1) / qwm::kTileKV;
 }
 
-qwm::AttnArgs base_args(qwm_cache* c) {
+// Per-call scratch of the attention paths: the q . U_r table [H][E][n_q][16],
+// the decode path's q . C table [H][E][m][nqp] and the split-KV partials
+// (part_rows rows of D floats in part_o, (max, sum) pairs in part_ml). Every
+// entry a call reads is written by that call first.
+struct AttnWork {
+  float* qU;
+  float* qc;
+  float* part_o;
+  float* part_ml;
+  int64_t part_rows;
+};
+
+AttnWork arena_work(const qwm_cache* c) { return {c->qU(), c->qc(), c->part_o(), c->part_ml(), c->L.part_rows}; }
+
+qwm::AttnArgs base_args(qwm_cache* c, const AttnWork& w) {
   qwm::AttnArgs a{};
   a.cache = c->view;
   a.Cbase = c->slotC(0);
@@ -300,8 +346,8 @@ qwm::AttnArgs base_args(qwm_cache* c) {
   a.H = c->H;
   a.m = c->m;
   a.r = c->r;
-  a.part_o = c->part_o();
-  a.part_ml = c->part_ml();
+  a.part_o = w.part_o;
+  a.part_ml = w.part_ml;
   return a;
 }
 
@@ -320,12 +366,12 @@ int queries_per_block(int64_t n_q) {
 // rounds as possible: cost = rounds x (tiles per workgroup + 2 for its
 // prologue and epilogue) + 2 for the merge pass when split; one 145 KB-LDS
 // workgroup per CU for head_dim 128.
-int choose_splits(const qwm_cache* c, int64_t n_q, int T) {
+int choose_splits(const qwm_cache* c, int64_t n_q, int T, int64_t part_rows) {
   const int64_t qtiles = (n_q + qwm::kTileQ - 1) / qwm::kTileQ;
   const int64_t slots = (int64_t)c->ncu * (c->D == 128 ? 1 : 2);
   int64_t splits = 1, best = -1;
   for (int64_t sp = 1; sp <= 16 && sp <= T; ++sp) {
-    if (sp > 1 && sp * c->H * n_q > c->L.part_rows) break;
+    if (sp > 1 && sp * c->H * n_q > part_rows) break;
     const int64_t rounds = (qtiles * c->H * sp + slots - 1) / slots;
     const int64_t cost = rounds * ((T + sp - 1) / sp + 2) + (sp > 1 ? 2 : 0);
     if (best < 0 || cost < best) {
@@ -338,8 +384,12 @@ int choose_splits(const qwm_cache* c, int64_t n_q, int T) {
 
 // The decode path of qwm_attend: q . U_r and q . C tables, then the decode
 // kernel over splits of the tiles and the log-sum-exp merge.
+bool use_decode(const qwm_cache* c, int32_t mask, int64_t n_q) {
+  return c->dtype == QWM_BF16 && c->D == 128 && mask == QWM_SELF_NONE && n_q <= qwm::kDecodeMaxQ && (c->r % 2) == 0;
+}
+
 qwm_status attend_decode(qwm_cache* c, const void* q, int64_t n_q, float softmax_scale, float* out,
-                         const qwm::AttnPlan& p) {
+                         const qwm::AttnPlan& p, const AttnWork& w) {
   const int T = p.tile_prefix[p.n_seg];
   const int E = (int)c->epoch_start.size();
   const int64_t qtiles = (n_q + qwm::kDecodeQ - 1) / qwm::kDecodeQ;
@@ -349,11 +399,11 @@ qwm_status attend_decode(qwm_cache* c, const void* q, int64_t n_q, float softmax
   const int64_t cap = T / 4 > 1 ? T / 4 : 1;
   if (splits > cap) splits = cap;
   if (splits > 64) splits = 64;
-  while (splits > 1 && splits * c->H * n_q > c->L.part_rows) --splits;
+  while (splits > 1 && splits * c->H * n_q > w.part_rows) --splits;
   qwm::DecodeArgs d{};
   d.q = q;
-  d.qc = c->qc();
-  d.qU = c->qU();
+  d.qc = w.qc;
+  d.qU = w.qU;
   d.cache = c->view;
   d.nq = n_q;
   d.nqp = nqp;
@@ -364,27 +414,98 @@ qwm_status attend_decode(qwm_cache* c, const void* q, int64_t n_q, float softmax
   d.scale_log2 = softmax_scale * 1.4426950408889634f;
   d.splits = (int)splits;
   d.out = out;
-  d.part_o = c->part_o();
-  d.part_ml = c->part_ml();
+  d.part_o = w.part_o;
+  d.part_ml = w.part_ml;
   hipError_t e = hipSuccess;
   if (c->r > 0) {
     e = c->run(QWM_K_QU, [&] {
-      return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
+      return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, w.qU,
                             c->stream);
     });
     if (e != hipSuccess) return fail_hip(e, "qU");
   }
   e = c->run(QWM_K_QU, [&] {
-    return qwm::launch_qc(q, n_q, nqp, c->slotC(0), (int64_t)c->H * c->m * c->D, c->H, c->m, E, c->qc(), c->stream);
+    return qwm::launch_qc(q, n_q, nqp, c->slotC(0), (int64_t)c->H * c->m * c->D, c->H, c->m, E, w.qc, c->stream);
   });
   if (e != hipSuccess) return fail_hip(e, "qC");
   e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_decode(d, p, c->stream); });
   if (e != hipSuccess) return fail_hip(e, "decode");
   if (splits > 1) {
-    qwm::AttnArgs a = base_args(c);
+    qwm::AttnArgs a = base_args(c, w);
     a.nq = n_q;
     a.splits = (int)splits;
     a.out = out;
+    e = c->run(QWM_K_MERGE, [&] { return qwm::launch_merge(c->D, a, c->stream); });
+    if (e != hipSuccess) return fail_hip(e, "merge");
+  }
+  return QWM_OK;
+}
+
+// Argument and state checks shared by qwm_attend and qwm_attend_noalloc,
+// which differ in the bound on n_q (max_query_tokens; for the static scratch
+// 2^24 here and the size of its tables later).
+qwm_status check_attend(qwm_cache* c, const void* q, int64_t n_q, const void* k_self, const void* v_self,
+                        int64_t n_self, int32_t mask, float softmax_scale, float* out, bool arena_scratch) {
+  qwm_status st;
+  if ((st = check_cache(c)) != QWM_OK) return st;
+  if ((st = check_ptr(q, "q")) != QWM_OK) return st;
+  if ((st = check_ptr(out, "out")) != QWM_OK) return st;
+  if (n_q < 1) return fail(QWM_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (arena_scratch && n_q > c->desc.max_query_tokens) return fail(QWM_ERR_CAPACITY, "n_q exceeds max_query_tokens");
+  if (n_q > ((int64_t)1 << 24)) return fail(QWM_ERR_CAPACITY, "n_q beyond 2^24");
+  if (mask != QWM_SELF_NONE && mask != QWM_SELF_FULL && mask != QWM_SELF_CAUSAL)
+    return fail(QWM_ERR_INVALID_ARG, "bad mask");
+  if (!std::isfinite(softmax_scale) || softmax_scale == 0.0f)
+    return fail(QWM_ERR_INVALID_ARG, "softmax_scale must be finite and nonzero");
+  if (mask == QWM_SELF_NONE) {
+    if (n_self != 0) return fail(QWM_ERR_INVALID_ARG, "n_self must be 0 with QWM_SELF_NONE");
+  } else {
+    if (n_self < 1) return fail(QWM_ERR_INVALID_ARG, "a self mask needs n_self >= 1");
+    if (n_self > ((int64_t)1 << 22)) return fail(QWM_ERR_CAPACITY, "n_self beyond 2^22");
+    if ((st = check_ptr(k_self, "k_self")) != QWM_OK) return st;
+    if ((st = check_ptr(v_self, "v_self")) != QWM_OK) return st;
+    if (mask == QWM_SELF_CAUSAL && n_self != n_q) return fail(QWM_ERR_INVALID_ARG, "causal self needs n_self == n_q");
+  }
+  if (c->epoch_start.empty()) return fail(QWM_ERR_STATE, "attend before a committed epoch");
+  if (c->length == 0 && mask == QWM_SELF_NONE) return fail(QWM_ERR_STATE, "nothing to attend to");
+  return need_device(c);
+}
+
+// The attention of qwm_attend with its scratch in `w` (device current).
+qwm_status attend_impl(qwm_cache* c, const void* q, int64_t n_q, const void* k_self, const void* v_self,
+                       int64_t n_self, int32_t mask, float softmax_scale, float* out, const AttnWork& w) {
+  qwm::AttnPlan p;
+  make_plan(c, n_self, mask != QWM_SELF_NONE, p);
+  const int T = p.tile_prefix[p.n_seg];
+  const int E = (int)c->epoch_start.size();
+  qwm::AttnArgs a = base_args(c, w);
+  a.q = q;
+  a.qU = w.qU;
+  a.kself = k_self;
+  a.vself = v_self;
+  a.nq = n_q;
+  a.nself = n_self;
+  a.causal_self = (mask == QWM_SELF_CAUSAL) ? 1 : 0;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.n_epoch_slots = E;
+  a.qpb = queries_per_block(n_q);
+  a.out = out;
+  // Few Queries over bf16 Keys: the decode kernel (2-bit codes as the MFMA
+  // operand, one wave per workgroup, many splits)
+  if (use_decode(c, mask, n_q)) return attend_decode(c, q, n_q, softmax_scale, out, p, w);
+  a.splits = choose_splits(c, n_q, T, w.part_rows);
+  hipError_t e = hipSuccess;
+  if (c->r > 0) {  // the kernels read no qU at rank 0
+    e = c->run(QWM_K_QU, [&] {
+      return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, w.qU,
+                            c->stream);
+    });
+    if (e != hipSuccess) return fail_hip(e, "qU");
+  }
+  e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_attend(c->D, c->dtype, a, p, c->stream); });
+  if (e != hipSuccess) return fail_hip(e, "attend");
+  if (a.splits > 1) {
     e = c->run(QWM_K_MERGE, [&] { return qwm::launch_merge(c->D, a, c->stream); });
     if (e != hipSuccess) return fail_hip(e, "merge");
   }
@@ -457,6 +578,12 @@ qwm_status qwm_create(const qwm_desc* desc, void* dev_arena, size_t arena_bytes,
   if (dev >= 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) c->ncu = n;
+    // set-up of qwm_attend_noalloc on this (current) device
+    uint8_t* sp = nullptr;
+    if ((st = static_scratch(dev, &sp)) != QWM_OK) {
+      delete c;
+      return st;
+    }
   }
   c->stream = reinterpret_cast<hipStream_t>(stream);
   c->arena = reinterpret_cast<uint8_t*>(dev_arena);
@@ -699,66 +826,44 @@ qwm_status qwm_quantize_append(qwm_cache* c, const void* k, const void* v, int64
 
 qwm_status qwm_attend(qwm_cache* c, const void* q, int64_t n_q, const void* k_self, const void* v_self,
                       int64_t n_self, int32_t mask, float softmax_scale, float* out) {
-  qwm_status st;
-  if ((st = check_cache(c)) != QWM_OK) return st;
-  if ((st = check_ptr(q, "q")) != QWM_OK) return st;
-  if ((st = check_ptr(out, "out")) != QWM_OK) return st;
-  if (n_q < 1) return fail(QWM_ERR_INVALID_ARG, "n_q must be >= 1");
-  if (n_q > c->desc.max_query_tokens) return fail(QWM_ERR_CAPACITY, "n_q exceeds max_query_tokens");
-  if (mask != QWM_SELF_NONE && mask != QWM_SELF_FULL && mask != QWM_SELF_CAUSAL)
-    return fail(QWM_ERR_INVALID_ARG, "bad mask");
-  if (!std::isfinite(softmax_scale) || softmax_scale == 0.0f)
-    return fail(QWM_ERR_INVALID_ARG, "softmax_scale must be finite and nonzero");
-  if (mask == QWM_SELF_NONE) {
-    if (n_self != 0) return fail(QWM_ERR_INVALID_ARG, "n_self must be 0 with QWM_SELF_NONE");
-  } else {
-    if (n_self < 1) return fail(QWM_ERR_INVALID_ARG, "a self mask needs n_self >= 1");
-    if (n_self > ((int64_t)1 << 22)) return fail(QWM_ERR_CAPACITY, "n_self beyond 2^22");
-    if ((st = check_ptr(k_self, "k_self")) != QWM_OK) return st;
-    if ((st = check_ptr(v_self, "v_self")) != QWM_OK) return st;
-    if (mask == QWM_SELF_CAUSAL && n_self != n_q) return fail(QWM_ERR_INVALID_ARG, "causal self needs n_self == n_q");
-  }
-  if (c->epoch_start.empty()) return fail(QWM_ERR_STATE, "attend before a committed epoch");
-  if (c->length == 0 && mask == QWM_SELF_NONE) return fail(QWM_ERR_STATE, "nothing to attend to");
-  if ((st = need_device(c)) != QWM_OK) return st;
+  qwm_status st = check_attend(c, q, n_q, k_self, v_self, n_self, mask, softmax_scale, out, true);
+  if (st != QWM_OK) return st;
   DeviceGuard g(c->device);
-  qwm::AttnPlan p;
-  make_plan(c, n_self, mask != QWM_SELF_NONE, p);
-  const int T = p.tile_prefix[p.n_seg];
-  const int E = (int)c->epoch_start.size();
-  qwm::AttnArgs a = base_args(c);
-  a.q = q;
-  a.qU = c->qU();
-  a.kself = k_self;
-  a.vself = v_self;
-  a.nq = n_q;
-  a.nself = n_self;
-  a.causal_self = (mask == QWM_SELF_CAUSAL) ? 1 : 0;
-  a.scale = softmax_scale;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.n_epoch_slots = E;
-  a.qpb = queries_per_block(n_q);
-  a.out = out;
-  // Few Queries over bf16 Keys: the decode kernel (2-bit codes as the MFMA
-  // operand, one wave per workgroup, many splits)
-  if (c->dtype == QWM_BF16 && c->D == 128 && mask == QWM_SELF_NONE && n_q <= qwm::kDecodeMaxQ && (c->r % 2) == 0)
-    return attend_decode(c, q, n_q, softmax_scale, out, p);
-  a.splits = choose_splits(c, n_q, T);
-  hipError_t e = hipSuccess;
-  if (c->r > 0) {  // the kernels read no qU at rank 0
-    e = c->run(QWM_K_QU, [&] {
-      return qwm::launch_qu(c->D, c->dtype, q, n_q, c->H, c->r, c->slotU(0), (int64_t)c->H * c->D * c->r, E, c->qU(),
-                            c->stream);
-    });
-    if (e != hipSuccess) return fail_hip(e, "qU");
-  }
-  e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_attend(c->D, c->dtype, a, p, c->stream); });
-  if (e != hipSuccess) return fail_hip(e, "attend");
-  if (a.splits > 1) {
-    e = c->run(QWM_K_MERGE, [&] { return qwm::launch_merge(c->D, a, c->stream); });
-    if (e != hipSuccess) return fail_hip(e, "merge");
-  }
-  return QWM_OK;
+  return attend_impl(c, q, n_q, k_self, v_self, n_self, mask, softmax_scale, out, arena_work(c));
+}
+
+qwm_status qwm_attend_noalloc(qwm_cache* c, const void* q, int64_t n_q, const void* k_self, const void* v_self,
+                              int64_t n_self, int32_t mask, float softmax_scale, float* out) {
+  qwm_status st = check_attend(c, q, n_q, k_self, v_self, n_self, mask, softmax_scale, out, false);
+  if (st != QWM_OK) return st;
+  DeviceGuard g(c->device);
+  uint8_t* base = nullptr;
+  if ((st = static_scratch(c->device, &base)) != QWM_OK) return st;
+  // carve the call's tables out of the static scratch; the partials take
+  // what is left (splits are cut to fit, down to none)
+  const size_t E = c->epoch_start.size(), H = (size_t)c->H;
+  const bool decode = use_decode(c, mask, n_q);
+  const size_t nqp = (size_t)((n_q + qwm::kDecodeQ - 1) / qwm::kDecodeQ * qwm::kDecodeQ);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t oU = take(H * E * (size_t)n_q * qwm::kRankPad * 4);
+  const size_t oC = decode ? take(H * E * (size_t)c->m * nqp * 4) : off;
+  if (off + 2 * kAlign > kScratchBytes)
+    return fail(QWM_ERR_CAPACITY, "qwm_attend_noalloc: n_q = " + std::to_string(n_q) + " needs " + std::to_string(off) +
+                                      " bytes of tables, beyond the " + std::to_string(kScratchBytes >> 20) +
+                                      " MiB static scratch");
+  const size_t rows = (kScratchBytes - off - 2 * kAlign) / ((size_t)c->D * 4 + 8);
+  const size_t oO = take(rows * c->D * 4), oML = take(rows * 8);
+  AttnWork w{reinterpret_cast<float*>(base + oU), reinterpret_cast<float*>(base + oC),
+             reinterpret_cast<float*>(base + oO), reinterpret_cast<float*>(base + oML), (int64_t)rows};
+  c->no_events = true;  // hipEventCreate is not called on this path
+  st = attend_impl(c, q, n_q, k_self, v_self, n_self, mask, softmax_scale, out, w);
+  c->no_events = false;
+  return st;
 }
 
 qwm_status qwm_attend_logits(qwm_cache* c, const void* q, int64_t n_q, int32_t head, float softmax_scale,
@@ -778,7 +883,7 @@ qwm_status qwm_attend_logits(qwm_cache* c, const void* q, int64_t n_q, int32_t h
   make_plan(c, 0, false, p);
   const int T = p.tile_prefix[p.n_seg];
   const int E = (int)c->epoch_start.size();
-  qwm::AttnArgs a = base_args(c);
+  qwm::AttnArgs a = base_args(c, arena_work(c));
   a.q = q;
   a.qU = c->qU();
   a.nq = n_q;
@@ -834,7 +939,7 @@ qwm_status qwm_attend_top1(qwm_cache* c, const void* q, int64_t n_q, const void*
   }
   const int T = p.tile_prefix[p.n_seg];
   const int E = (int)c->epoch_start.size();
-  qwm::AttnArgs a = base_args(c);
+  qwm::AttnArgs a = base_args(c, arena_work(c));
   a.q = q;
   a.qU = c->qU();
   a.kself = ref ? k_ref : nullptr;
@@ -845,7 +950,7 @@ qwm_status qwm_attend_top1(qwm_cache* c, const void* q, int64_t n_q, const void*
   a.n_epoch_slots = E;
   a.qpb = queries_per_block(n_q);
   a.top1 = top1;
-  a.splits = choose_splits(c, n_q, T);
+  a.splits = choose_splits(c, n_q, T, c->L.part_rows);
   hipError_t e = hipSuccess;
   if (!ref && c->r > 0) {
     e = c->run(QWM_K_QU, [&] {

@@ -72,6 +72,7 @@ _SIGS = {
     "qwm_build_centroids": [_VP, _VP, _I64, _I32],
     "qwm_quantize_append": [_VP, _VP, _VP, _I64],
     "qwm_attend": [_VP, _VP, _I64, _VP, _VP, _I64, _I32, ctypes.c_float, _VP],
+    "qwm_attend_noalloc": [_VP, _VP, _I64, _VP, _VP, _I64, _I32, ctypes.c_float, _VP],
     "qwm_length": [_VP, ctypes.POINTER(_I64)],
     "qwm_epochs": [_VP, ctypes.POINTER(_I32)],
     "qwm_truncate": [_VP, _I64],
@@ -260,6 +261,23 @@ class Cache:
             self._chk(out, "out", nq, torch.float32)
         check(lib().qwm_attend(self._h, _ptr(q), nq, _ptr(k_self), _ptr(v_self), ns, MASKS[mask],
                                ctypes.c_float(scale), _ptr(out)))
+        return out
+
+    def attend_noalloc(self, q, out, k_self=None, v_self=None, mask: str = "none", scale: Optional[float] = None):
+        """qwm_attend_noalloc: attend() with its scratch in the library's static
+        device array; `out` [heads][n_q][head_dim] float32 is the caller's."""
+        self._chk(q, "q")
+        nq = q.shape[1]
+        ns = 0
+        if mask != "none":
+            self._chk(k_self, "k_self")
+            ns = k_self.shape[1]
+            self._chk(v_self, "v_self", ns)
+        if scale is None:
+            scale = 1.0 / float(np.sqrt(self.head_dim))
+        self._chk(out, "out", nq, self.torch.float32)
+        check(lib().qwm_attend_noalloc(self._h, _ptr(q), nq, _ptr(k_self), _ptr(v_self), ns, MASKS[mask],
+                                       ctypes.c_float(scale), _ptr(out)))
         return out
 
     def attend_logits(self, q, head: int, scale: Optional[float] = None):
