@@ -56,7 +56,7 @@ def test_noalloc_attend_matches_attend():
         log(f"  worst row error against qwm_attend {err:.2e}, bit-identical {np.array_equal(got, ref)}")
         assert err <= ROW_TOL
     # beyond max_query_tokens: only the static array bounds this call
-    nq = 900
+    nq = 880
     q = to_dev([g.current_queries()[:nq] for g in gens], "bf16")
     out = torch.empty((H, nq, w.head_dim), dtype=torch.float32, device="cuda")
     cache.attend_noalloc(q, out)
