@@ -51,8 +51,9 @@
  *   no side effect. qwm_last_error() returns a message for the last failure
  *   of the calling thread.
  * - Non-finite inputs are undefined behaviour, and so are Key and Value
- *   magnitudes at or above 65504: zero-points, steps and the dequantized
- *   k and v are fp16.
+ *   magnitudes at or above 65504 and group ranges (max - min of 32 channels,
+ *   Key residuals included) at or above 65472: zero-points, steps, their
+ *   triples and the dequantized k and v are fp16.
  */
 #ifndef QWM_H_
 #define QWM_H_
@@ -172,7 +173,8 @@ qwm_status qwm_build_centroids(qwm_cache* cache, const void* keys, int64_t n_key
  *        the weighted post-quantization error (qwm_objective);
  *   the residual k - c_id and the Value each get per-group (32 channels)
  *   asymmetric INT2: fp16 zero-point = largest fp16 <= group min, fp16 step =
- *   smallest fp16 >= (max - zp) / 3, codes = clamp(rint((x - zp) / step), 0, 3);
+ *   smallest fp16 >= (max - zp) / 3 whose triple is an fp16 value (so every
+ *   code * step is exactly an fp16), codes = clamp(rint((x - zp) / step), 0, 3);
  *   coef = U_r^T (k - (c_id + reconstructed residual)), float64, rounded once
  *   to fp16 (PSAC, "Step 2"); none at rank 0.
  * The records go to positions length .. length + n_tokens - 1 and the length

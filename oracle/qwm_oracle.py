@@ -75,6 +75,25 @@ def fp16_round_up(x: np.ndarray) -> np.ndarray:
     return h
 
 
+def fp16_step_up(x: np.ndarray) -> np.ndarray:
+    """Smallest float16 value s >= x (x float32, >= 0) such that 3 s is a
+    float16 value too. Used for the INT2 step: every reconstruction offset
+    code * s (code 0..3) is then exactly an fp16 value. Computed as
+    fp16_round_up, then at most three steps of one fp16 ulp upward while 3 s
+    (exact in float32) is not an fp16 value. Steps whose triple would exceed
+    the fp16 range (group ranges of 65,472 or more) are outside the supported
+    range."""
+    s = fp16_round_up(x)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for _ in range(3):
+            t = s.astype(F32) * THREE32
+            bad = t.astype(np.float16).astype(F32) != t
+            if not np.any(bad):
+                break
+            s = np.where(bad, np.nextafter(s, np.float16(np.inf)), s)
+    return s
+
+
 def f64_to_fp16(x: np.ndarray) -> np.ndarray:
     """float64 -> float16, round to nearest, ties to even (one rounding)."""
     return np.asarray(x, dtype=F64).astype(np.float16)
@@ -337,11 +356,13 @@ def int2_quantize(x: np.ndarray, g: int):
     per-group INT2 (no centroid). The quantizer is the min/max asymmetric one:
     for each group, mn and mx of the values (signed zeros folded to +0);
     zero-point zp = the largest float16 <= mn; step scale = the smallest
-    float16 >= (mx - zp) / 3 (float32 correctly rounded divide); codes
+    float16 >= (mx - zp) / 3 (float32 correctly rounded divide) whose triple
+    is a float16 as well (``fp16_step_up``); codes
     c_j = min(max(rint((x_j - zp) / scale), 0), 3) with rint ties-to-even and
     zp, scale taken as the float32 values of the stored float16; a zero step
     gives all-zero codes. Directed rounding of the stored parameters keeps the
-    stored grid [zp, zp + 3 scale] covering [mn, mx].
+    stored grid [zp, zp + 3 scale] covering [mn, mx], and the step rule makes
+    each offset code * scale exactly a float16 value.
 
     Returns (codes u8 [N][d], zp f16 [N][nG], scale f16 [N][nG]).
     """
@@ -354,7 +375,7 @@ def int2_quantize(x: np.ndarray, g: int):
     zp = fp16_round_down(mn)
     zpf = zp.astype(F32)
     step32 = (mx - zpf) / THREE32
-    sc = fp16_round_up(step32)
+    sc = fp16_step_up(step32)
     scf = sc.astype(F32)
     num = xg - zpf[:, :, None]
     with np.errstate(divide="ignore", invalid="ignore"):

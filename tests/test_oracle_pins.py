@@ -57,6 +57,32 @@ def test_fp16_directed_rounding_exact():
     assert np.array_equal(up, FP16_VALUES[i_up])
 
 
+def test_fp16_step_up_exact():
+    """fp16_step_up gives the smallest fp16 s >= x with 3 s an fp16 value
+    (exhaustive search over the fp16 grid, exact float64 arithmetic):
+    normal and subnormal steps, exact fp16 inputs (odd and even
+    significands), values just above an fp16, and zero."""
+    rng = np.random.default_rng(4)
+    grid = FP16_VALUES[(FP16_VALUES >= 0) & (FP16_VALUES < 20000)]
+    x = np.concatenate([
+        np.abs(rng.standard_normal(3000)).astype(np.float32) * np.float32(2),
+        (np.abs(rng.standard_normal(500)) * 1e-5).astype(np.float32),
+        grid[rng.integers(0, len(grid), 1000)].astype(np.float32),
+        np.nextafter(grid[rng.integers(0, len(grid), 300)].astype(np.float32), np.float32(np.inf)),
+        np.array([0.0, 2.0 / 3.0, 1.0, 21824.0, 6.1e-5, 5.96e-8], np.float32),
+    ])
+    got = O.fp16_step_up(x).astype(np.float64)
+    trip = set((3 * FP16_VALUES[FP16_VALUES >= 0]).tolist()) & set(FP16_VALUES.tolist())
+    ok = np.array(sorted(v / 3 for v in trip))  # the fp16 steps whose triple is an fp16
+    assert np.all(np.isin(ok, FP16_VALUES))
+    want = ok[np.searchsorted(ok, x.astype(np.float64), side="left")]
+    assert np.array_equal(got, want)
+    # at most three ulps above plain upward rounding
+    up = O.fp16_round_up(x)
+    steps = (got.astype(np.float16).view(np.uint16).astype(np.int64) - up.view(np.uint16).astype(np.int64))
+    assert steps.min() >= 0 and steps.max() <= 3
+
+
 def test_f64_to_fp16_is_single_rounding():
     """float64 -> fp16 is one nearest-even rounding, including values just off a
     float16 midpoint that a float32 detour would round onto it."""
@@ -254,8 +280,9 @@ def test_qsac_not_nearest_and_cuts_weighted_error():
 
 def test_int2_half_step_bound_and_coverage():
     """The stored grid covers [mn, mx] (exact comparison), zp is the largest
-    fp16 <= mn, scale the smallest fp16 >= (mx - zp)/3, and every element is
-    within half a step (plus float32 rounding) of its reconstruction."""
+    fp16 <= mn, scale the smallest fp16 >= (mx - zp)/3 whose triple is an
+    fp16, and every element is within half a step (plus float32 rounding) of
+    its reconstruction."""
     rng = np.random.default_rng(8)
     x = np.concatenate([
         rng.standard_normal((300, 128)).astype(np.float32) * np.float32(4),
@@ -275,9 +302,14 @@ def test_int2_half_step_bound_and_coverage():
     nxt = np.nextafter(zp, np.float16(np.inf)).astype(np.float64)
     assert np.all(nxt > xg.min(2))
     step32 = ((xg.max(2).astype(np.float32) - zp.astype(np.float32)) / np.float32(3)).astype(np.float64)
-    prv = np.nextafter(sc, np.float16(-np.inf)).astype(np.float64)
     assert np.all(scf >= step32)
-    assert np.all((prv < step32) | (sc == 0))
+    # minimal among the fp16 values >= step32 whose triple is an fp16
+    assert np.all(np.isin(3 * scf, FP16_VALUES))
+    for want, got in zip(step32.ravel(), scf.ravel()):
+        i = np.searchsorted(FP16_VALUES, want, side="left")
+        while not np.isin(3 * FP16_VALUES[i], FP16_VALUES):
+            i += 1
+        assert got == FP16_VALUES[i]
     err = np.abs(x.astype(np.float64) - rh.astype(np.float64)).reshape(len(x), 4, 32)
     mag = np.maximum(np.abs(xg), np.abs(zpf)[:, :, None] + 3 * scf[:, :, None])
     bound = scf[:, :, None] / 2 + 4 * mag * 2.0 ** -24

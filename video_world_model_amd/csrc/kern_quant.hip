@@ -73,8 +73,24 @@ __device__ __forceinline__ float nearest_cost(const float (&kf)[D], const float*
   return J;
 }
 
+// Smallest fp16 s >= x whose triple is an fp16 value too, so that every
+// offset code * s (code 0..3) is exactly an fp16 value (the attention kernels
+// contract the codes times the step in fp16): round up, then at most three
+// one-ulp steps upward while 3 s (exact in float32) is not an fp16 value.
+__device__ __forceinline__ uint32_t f16_step_up(float x) {
+  uint32_t b = f16_round_up(x);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const float t = 3.0f * half_bits_to_float(b);
+    if (half_bits_to_float(half_bits(__float2half_rn(t))) == t) break;
+    b = f16_next_up(b);
+  }
+  return b;
+}
+
 // Per-group INT2 parameters (signed zeros folded to +0):
-// zp = largest fp16 <= min, step = smallest fp16 >= (max - zp) / 3.
+// zp = largest fp16 <= min, step = smallest fp16 >= (max - zp) / 3 whose
+// triple is an fp16 value.
 __device__ __forceinline__ void int2_params(float mn, float mx, uint32_t& zpb, uint32_t& scb, float& zpf,
                                             float& scf) {
   mn = mn + 0.0f;
@@ -82,7 +98,7 @@ __device__ __forceinline__ void int2_params(float mn, float mx, uint32_t& zpb, u
   zpb = f16_round_down(mn);
   zpf = half_bits_to_float(zpb);
   const float step = (mx - zpf) / 3.0f;  // correctly rounded divide
-  scb = f16_round_up(step);
+  scb = f16_step_up(step);
   scf = half_bits_to_float(scb);
 }
 
