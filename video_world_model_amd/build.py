@@ -27,7 +27,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqwm.so")
 ARCH = os.environ.get("QWM_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["qwm_host.hip", "kern_quant.hip", "kern_calib.hip", "kern_attend.hip", "kern_decode.hip"]
+SOURCES = ["qwm_host.hip", "kern_quant.hip", "kern_calib.hip", "kern_attend.hip", "kern_attend_bf16.hip",
+           "kern_decode.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}",

@@ -880,6 +880,7 @@ static hipError_t launch_attend_impl(int D, int dtype, const AttnArgs& a, const 
 }
 
 hipError_t launch_attend(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
+  if (D == 128 && dtype == 0) return launch_attend_bf16(a, p, s);
   return launch_attend_impl<kModeAttend>(D, dtype, a, p, s);
 }
 hipError_t launch_attend_logits(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s) {

@@ -128,6 +128,8 @@ struct AttnArgs {
 hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, const float* Ubase,
                      int64_t epoch_U_stride_floats, int E, float* qU, hipStream_t s);
 hipError_t launch_attend(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+// bf16, head_dim 128: the exact-operand pipelined kernel (kern_attend_bf16.hip)
+hipError_t launch_attend_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_attend_logits(int D, int dtype, const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_merge(int D, const AttnArgs& a, hipStream_t s);
 // Top-1 mode: per (head, Query) the token with the largest unscaled logit
