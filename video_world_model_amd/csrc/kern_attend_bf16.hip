@@ -264,14 +264,23 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = h2_bits(bf2_to_h2(sw[i]));
     }
-    _Float16* base = Vs + (16 * kq) * kVRow + col;
+    // Lanes 2j and 2j+1 hold neighbouring columns: after swapping the pairs
+    // with the neighbour lane, the even lane writes channel 2i of both tokens
+    // and the odd lane channel 2i+1, one dword each (no two lanes of a store
+    // share a dword).
+    const bool odd = (lane & 1) != 0;
+    uint32_t* base = reinterpret_cast<uint32_t*>(Vs + (16 * kq + (odd ? 1 : 0)) * kVRow + (col & ~1));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const half2v hv = __builtin_bit_cast(half2v, v[i]);
-      base[(2 * i) * kVRow] = hv[0];
-      base[(2 * i + 1) * kVRow] = hv[1];
+      const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[i], kDppQuadSwap1, 0xF, 0xF, false);
+      const uint32_t w = odd ? __builtin_amdgcn_perm(v[i], other, 0x07060302u) : __builtin_amdgcn_perm(other, v[i], 0x05040100u);
+      base[(2 * i) * (kVRow / 2)] = w;
     }
-    if ((kq & 1) == 0) Vs[(128 + (kq >> 1)) * kVRow + col] = __builtin_bit_cast(_Float16, (uint16_t)(prm & 0xFFFFu));
+    if ((kq & 1) == 0) {
+      const uint32_t z = prm & 0xFFFFu;
+      const uint32_t zo = (uint32_t)__builtin_amdgcn_mov_dpp((int)z, kDppQuadSwap1, 0xF, 0xF, false);
+      if (!odd) *reinterpret_cast<uint32_t*>(Vs + (128 + (kq >> 1)) * kVRow + col) = z | (zo << 16);
+    }
   };
 
   // ---- Query operands (B): Query qw0 + 16 qb + l16, channels 32 ks + 8 g .. +7
@@ -333,39 +342,63 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
     }
   };
 
-  // logits S^T blocks [16 tokens x 16 Queries] of the tile in stage Ks
+  // logits S^T blocks [16 tokens x 16 Queries] of the tile in stage Ks, in
+  // eight steps (32 channels x two 16-token blocks: the c and code*s
+  // fragments, 4 reads). Each step's operands are read while the previous
+  // step's 8 MFMAs run, so a wait for LDS never idles the wave behind a
+  // single MFMA; the c products come before the code*s products of a step.
   auto logits = [&](const _Float16* Ks, floatx4 (&S)[2][4]) {
+    const _Float16* rb = Ks + l16 * kKRow + 8 * g;
+    half8 A[2][4];
+    auto rd = [&](half8 (&buf)[4], int stp) {  // ks = stp / 2, blocks tb = 2 (stp % 2) ..
+      const int ks = stp >> 1, tb0 = 2 * (stp & 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        buf[2 * j] = *reinterpret_cast<const half8*>(rb + 16 * (tb0 + j) * kKRow + 32 * ks);
+        buf[2 * j + 1] = *reinterpret_cast<const half8*>(rb + 16 * (tb0 + j) * kKRow + 32 * ks + kCsOff);
+      }
+    };
+    auto rdx = [&](half8 (&buf)[4], int tb0) {  // X operands of blocks tb0, tb0+1: [coef | coef], [zp | zp] or 0
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const _Float16* x0 = Ks + (16 * (tb0 + j) + l16) * kKRow + kXOff;
+        buf[2 * j] = *reinterpret_cast<const half8*>(x0 + 8 * (g & 1));
+        buf[2 * j + 1] = *reinterpret_cast<const half8*>(x0 + (g == 0 ? 16 : 24));
+      }
+    };
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) S[qb][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    rd(A[0], 0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int stp = 0; stp < 10; ++stp) {
       __builtin_amdgcn_sched_barrier(0);
+      if (stp < 7)
+        rd(A[(stp + 1) & 1], stp + 1);
+      else if (stp < 9)
+        rdx(A[(stp + 1) & 1], 2 * (stp - 7));
+      const int tb0 = 2 * (stp & 1);
+      if (stp < 8) {
+        const int ks = stp >> 1;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const _Float16* r0 = Ks + (16 * tb + l16) * kKRow + 32 * ks + 8 * g;
-        const half8 a1 = *reinterpret_cast<const half8*>(r0);
-        const half8 a2 = *reinterpret_cast<const half8*>(r0 + kCsOff);
+        for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          S[qb][tb] = mfma16(a1, qh[qb][ks], S[qb][tb]);
-          S[qb][tb] = mfma16(a2, qh[qb][ks], S[qb][tb]);
-        }
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              S[qb][tb0 + j] = mfma16(A[stp & 1][2 * j + pass], qh[qb][ks], S[qb][tb0 + j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            S[qb][tb0 + j] = mfma16(A[stp & 1][2 * j], xu[qb], S[qb][tb0 + j]);
+            S[qb][tb0 + j] = mfma16(A[stp & 1][2 * j + 1], xz[qb], S[qb][tb0 + j]);
+          }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const _Float16* x0 = Ks + (16 * tb + l16) * kKRow + kXOff;
-      const half8 ac = *reinterpret_cast<const half8*>(x0 + 8 * (g & 1));
-      const half8 az = *reinterpret_cast<const half8*>(x0 + (g == 0 ? 16 : 24));
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        S[qb][tb] = mfma16(ac, xu[qb], S[qb][tb]);
-        S[qb][tb] = mfma16(az, xz[qb], S[qb][tb]);
-      }
-    }
   };
 
   floatx4 O[2][kD / 16], Z[2];
@@ -441,21 +474,34 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
     }
   };
 
-  // o^T += (code * s)^T P^T and the zero-point rows
+  // o^T += (code * s)^T P^T and the zero-point rows, in eight steps of two
+  // channel blocks (the zero-point rows join the last step of each 32-token
+  // half); each step's operands are read while the previous step's MFMAs run.
   auto pv = [&](const _Float16* Vs, const half8 (&pf)[2][2]) {
+    const _Float16* rb = Vs + l16 * kVRow + 8 * g;
+    half8 B[2][3];
+    auto rd = [&](half8 (&buf)[3], int stp) {  // ks = stp / 4, channel blocks 2 (stp % 4), +1
+      const int ks = stp >> 2, cb0 = 2 * (stp & 3);
+      buf[0] = *reinterpret_cast<const half8*>(rb + 16 * cb0 * kVRow + 32 * ks);
+      buf[1] = *reinterpret_cast<const half8*>(rb + 16 * (cb0 + 1) * kVRow + 32 * ks);
+      if ((stp & 3) == 3) buf[2] = *reinterpret_cast<const half8*>(rb + 128 * kVRow + 32 * ks);
+    };
+    rd(B[0], 0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int stp = 0; stp < 8; ++stp) {
       __builtin_amdgcn_sched_barrier(0);
+      if (stp < 7) rd(B[(stp + 1) & 1], stp + 1);
+      const int ks = stp >> 2, cb0 = 2 * (stp & 3);
 #pragma unroll
-      for (int cb = 0; cb < kD / 16; ++cb) {
-        const half8 av = *reinterpret_cast<const half8*>(Vs + (16 * cb + l16) * kVRow + 32 * ks + 8 * g);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) O[qb][cb] = mfma16(av, pf[qb][ks], O[qb][cb]);
+        for (int qb = 0; qb < 2; ++qb) O[qb][cb0 + j] = mfma16(B[stp & 1][j], pf[qb][ks], O[qb][cb0 + j]);
+      if ((stp & 3) == 3) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) Z[qb] = mfma16(B[stp & 1][2], pf[qb][ks], Z[qb]);
       }
-      const half8 az = *reinterpret_cast<const half8*>(Vs + (128 + l16) * kVRow + 32 * ks + 8 * g);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) Z[qb] = mfma16(az, pf[qb][ks], Z[qb]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   _Float16* const Kst0 = lds;
@@ -488,12 +534,22 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
       set_epoch(t0.ep);
       logits(Kst0, S);
     }
+    // Tile descriptors of tiles i .. i+4 (clamped to the last tile) in a
+    // ring advanced once per step: a segment cursor moves by at most one
+    // segment per tile (every segment holds a tile), so each step costs a
+    // few scalar operations instead of a search of the plan.
+    TileInfo tr[5] = {t0, t1, t2, tile_info(p, clampt(tlo + 3)), tile_info(p, clampt(tlo + 4))};
+    int cur_t = clampt(tlo + 4);
+    int sg = 0;
+    while (p.tile_prefix[sg + 1] <= cur_t) ++sg;
+    int seg_tp = p.tile_prefix[sg], seg_tp1 = p.tile_prefix[sg + 1];
+    int seg_s = p.seg_start[sg], seg_e = p.seg_start[sg] + p.seg_len[sg], seg_ep = p.seg_epoch[sg];
     // Step i (stages: K(i) in ks0, K(i+1) in ks1, K(i+2) built into ks2;
     // V(i) in vs0, V(i+1) built into vs1)
     int ks0 = 0, vs0 = 0;
     for (int i = tlo; i < thi; ++i) {
       const int ks1 = ks0 == 2 ? 0 : ks0 + 1, ks2 = ks1 == 2 ? 0 : ks1 + 1;
-      const TileInfo ti = tile_info(p, i);
+      const TileInfo ti = tr[0];
       if (wave_live) {
         if (!lead) {
           set_epoch(ti.ep);
@@ -504,13 +560,37 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
         pv(Vst0 + vs0 * kVSt, pf);
       }
       __builtin_amdgcn_sched_barrier(0);
-      store_k(rk, tile_info(p, clampt(i + 2)), Kst0 + ks2 * kKSt);
-      store_v(rv, tile_info(p, clampt(i + 1)), Vst0 + (vs0 ^ 1) * kVSt);
-      load_k(rk, tile_info(p, clampt(i + 3)), id_next);
-      id_next = load_id(tile_info(p, clampt(i + 4)));
-      load_v(rv, tile_info(p, clampt(i + 2)));
+      store_k(rk, tr[2], Kst0 + ks2 * kKSt);
+      store_v(rv, tr[1], Vst0 + (vs0 ^ 1) * kVSt);
+      load_k(rk, tr[3], id_next);
+      // advance the ring to tiles i+1 .. i+5
+      {
+        const int nt = clampt(i + 5);
+        if (nt != cur_t) {
+          cur_t = nt;
+          if (nt >= seg_tp1) {
+            ++sg;
+            seg_tp = seg_tp1;
+            seg_tp1 = p.tile_prefix[sg + 1];
+            seg_s = p.seg_start[sg];
+            seg_e = seg_s + p.seg_len[sg];
+            seg_ep = p.seg_epoch[sg];
+          }
+        }
+        TileInfo tn;
+        tn.ep = seg_ep;
+        tn.tstart = seg_s + (cur_t - seg_tp) * kTileKV;
+        tn.tcount = (seg_e - tn.tstart) < kTileKV ? (seg_e - tn.tstart) : kTileKV;
+        tr[0] = tr[1];
+        tr[1] = tr[2];
+        tr[2] = tr[3];
+        tr[3] = tr[4];
+        tr[4] = tn;
+      }
+      id_next = load_id(tr[3]);  // tile i+4
+      load_v(rv, tr[1]);         // tile i+2
       if (lead && wave_live && i + 1 < thi) {
-        set_epoch(tile_info(p, i + 1).ep);
+        set_epoch(tr[0].ep);  // tile i+1
         logits(Kst0 + ks1 * kKSt, S);
       }
       __syncthreads();
