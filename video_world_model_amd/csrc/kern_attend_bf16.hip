@@ -17,7 +17,10 @@
 //  * code * s: the step is chosen so that 3 s is an fp16 value, so every
 //    code * s (code 0..3) is one;
 //  * q: bf16 Queries in fp16 (exact); the group sums of q as fp16 hi + lo;
-//  * q U_r as fp16 hi + lo against the fp16 coefficients;
+//  * q U_r as fp16 hi against the fp16 coefficients, plus the lo part for
+//    the 8 leading principal directions (which carry most of the Query
+//    energy; the lo parts of the other 8 are the one rounding left on the
+//    Key side, about 2^-12 of their already small share);
 //  * Values: o = P (code * s) + P zp, the zero-point term on its own MFMA
 //    with four rows (one per group) that is added to the output at the end.
 // The only roundings are the fp32 accumulations and P in fp16.
@@ -50,7 +53,7 @@ constexpr int kD = 128;
 constexpr int kNG = kD / kGroup;
 constexpr int kKRow = 296;   // halves per token row of a K stage: c (128) | code*s (128) | X (32) | pad (8)
 constexpr int kCsOff = 128;  // code * s
-constexpr int kXOff = 256;   // X: coef (16) | zp_0..3, zp_0..3 (8) | zeros (8)
+constexpr int kXOff = 256;   // X: coef 0..15 | zp_0..3, zp_0..3 | coef 0..7
 constexpr int kVRow = 72;    // halves per row of a V stage (64 token slots + pad)
 constexpr int kVRows = 144;  // 128 channels, 4 zero-point rows, 12 zero rows
 constexpr int kKSt = kTileKV * kKRow;
@@ -153,14 +156,10 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
   const char* C_h = reinterpret_cast<const char*>(a.Cbase) + (size_t)h * a.m * kD * 2;
 
   // rows of the stages that never change: the zero rows 132..143 of each V
-  // stage and the zero tail of every X block
+  // stage
   for (int e = tid; e < kVStages * 12 * kVRow; e += kAttnThreads) {
     const int st = e / (12 * kVRow), r = e % (12 * kVRow);
     lds[kKStages * kKSt + st * kVSt + 132 * kVRow + r] = (_Float16)0.0f;
-  }
-  for (int e = tid; e < kKStages * kTileKV * 8; e += kAttnThreads) {
-    const int st = e / (kTileKV * 8), r = e % (kTileKV * 8);
-    lds[st * kKSt + (r >> 3) * kKRow + kXOff + 24 + (r & 7)] = (_Float16)0.0f;
   }
 
   // ---- producer: loads (no use of the data) and stage construction
@@ -215,9 +214,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
     }
   };
   // K stage row of the thread's token: c (or the self Key), code * s, and
-  // the X block (coefficients from waves 0 and 1, the group's zero-point
-  // from the even waves); self tokens have zero code, step, zero-point and
-  // coefficients.
+  // the X block (coefficients from waves 0 and 1, the leading 8 once more
+  // from wave 0, the group's zero-point from the even waves); self tokens
+  // have zero code, step, zero-point and coefficients.
   auto store_k = [&](const RawK& r, const TileInfo& ti, _Float16* Ks) {
     const bool cache = ti.ep >= 0;
     _Float16* row = Ks + lane * kKRow;
@@ -245,6 +244,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
       cfw.z = (cache && j0 + 4 < a.r) ? (j0 + 5 < a.r ? cfw.z : cfw.z & 0xFFFFu) : 0u;
       cfw.w = (cache && j0 + 6 < a.r) ? (j0 + 7 < a.r ? cfw.w : cfw.w & 0xFFFFu) : 0u;
       *reinterpret_cast<uint4*>(row + kXOff + 8 * kq) = cfw;
+      if (kq == 0) *reinterpret_cast<uint4*>(row + kXOff + 24) = cfw;  // coef 0..7 again, against q U lo
     }
   };
   // V stage: (code * s)^T rows 16 kq .. 16 kq + 15 (or the self Values) and
@@ -285,7 +285,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
 
   // ---- Query operands (B): Query qw0 + 16 qb + l16, channels 32 ks + 8 g .. +7
   half8 qh[2][4];
-  half8 xz[2];  // [qsum_hi | qsum_lo] on lane group 0, zeros elsewhere
+  // B operand of the X MFMA, by lane group: 0: q U hi 0..7, 1: q U hi 8..15,
+  // 2: [group sums of q hi | lo], 3: q U lo 0..7
+  half8 xw[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int64_t qi = qw0 + 16 * qb + l16;
@@ -315,29 +317,30 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
     for (int G = 0; G < kNG; ++G) {
       const _Float16 hi = (_Float16)gs[G];
       const _Float16 lo = (_Float16)(gs[G] - (float)hi);
-      xz[qb][G] = (g == 0) ? hi : (_Float16)0.0f;
-      xz[qb][G + 4] = (g == 0) ? lo : (_Float16)0.0f;
+      xw[qb][G] = (g == 2) ? hi : (_Float16)0.0f;
+      xw[qb][G + 4] = (g == 2) ? lo : (_Float16)0.0f;
     }
   }
-  half8 xu[2];  // [qU_hi | qU_lo] of the current epoch: lanes g < 2 hi, g >= 2 lo
   int cur_epoch = -2;
   auto set_epoch = [&](int ep) {
     if (ep == cur_epoch) return;
     cur_epoch = ep;
+    if (g == 2) return;  // the group sums do not change
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int64_t qi = qw0 + 16 * qb + l16;
       if (ep >= 0 && qi < a.nq && a.r > 0) {
-        const float* src = a.qU + (((int64_t)h * a.n_epoch_slots + ep) * a.nq + qi) * kRankPad + 8 * (g & 1);
+        // lane group 1 takes directions 8..15 (hi); groups 0 and 3 take 0..7 (hi, lo)
+        const float* src = a.qU + (((int64_t)h * a.n_epoch_slots + ep) * a.nq + qi) * kRankPad + (g == 1 ? 8 : 0);
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2) {
           const float x = qsign * src[s2];
           const _Float16 hi = (_Float16)x;
-          xu[qb][s2] = (g < 2) ? hi : (_Float16)(x - (float)hi);
+          xw[qb][s2] = (g < 2) ? hi : (_Float16)(x - (float)hi);
         }
       } else {
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) xu[qb][s2] = (_Float16)0.0f;
+        for (int s2 = 0; s2 < 8; ++s2) xw[qb][s2] = (_Float16)0.0f;
       }
     }
   };
@@ -358,13 +361,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
         buf[2 * j + 1] = *reinterpret_cast<const half8*>(rb + 16 * (tb0 + j) * kKRow + 32 * ks + kCsOff);
       }
     };
-    auto rdx = [&](half8 (&buf)[4], int tb0) {  // X operands of blocks tb0, tb0+1: [coef | coef], [zp | zp] or 0
+    auto rdx = [&](half8 (&buf)[4]) {  // X operands of the four blocks (lane group g: X[8g .. 8g+7])
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const _Float16* x0 = Ks + (16 * (tb0 + j) + l16) * kKRow + kXOff;
-        buf[2 * j] = *reinterpret_cast<const half8*>(x0 + 8 * (g & 1));
-        buf[2 * j + 1] = *reinterpret_cast<const half8*>(x0 + (g == 0 ? 16 : 24));
-      }
+      for (int tb = 0; tb < 4; ++tb) buf[tb] = *reinterpret_cast<const half8*>(rb + 16 * tb * kKRow + kXOff);
     };
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -372,15 +371,14 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
       for (int tb = 0; tb < 4; ++tb) S[qb][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
     rd(A[0], 0);
 #pragma unroll
-    for (int stp = 0; stp < 10; ++stp) {
+    for (int stp = 0; stp < 9; ++stp) {
       __builtin_amdgcn_sched_barrier(0);
       if (stp < 7)
         rd(A[(stp + 1) & 1], stp + 1);
-      else if (stp < 9)
-        rdx(A[(stp + 1) & 1], 2 * (stp - 7));
-      const int tb0 = 2 * (stp & 1);
+      else if (stp == 7)
+        rdx(A[0]);
       if (stp < 8) {
-        const int ks = stp >> 1;
+        const int ks = stp >> 1, tb0 = 2 * (stp & 1);
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
@@ -390,12 +388,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
               S[qb][tb0 + j] = mfma16(A[stp & 1][2 * j + pass], qh[qb][ks], S[qb][tb0 + j]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            S[qb][tb0 + j] = mfma16(A[stp & 1][2 * j], xu[qb], S[qb][tb0 + j]);
-            S[qb][tb0 + j] = mfma16(A[stp & 1][2 * j + 1], xz[qb], S[qb][tb0 + j]);
-          }
+          for (int qb = 0; qb < 2; ++qb) S[qb][tb] = mfma16(A[0][tb], xw[qb], S[qb][tb]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
