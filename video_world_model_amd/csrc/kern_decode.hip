@@ -17,9 +17,11 @@
 //    float32 result;
 //  * zp . qsum and the PSAC term are one more pair of MFMAs ([qU_hi | qU_lo]
 //    x [coef | coef], [qsum_hi | qsum_lo] x [zp | zp]);
-//  * Values are dequantized once per token into LDS as fp16 hi + lo pairs
-//    (vhat^T, two passes of 64 channels) and o += P vhat by MFMA with P in
-//    fp16.
+//  * Values: o = P (code * s) + P zp. The codes times the group's step are
+//    exact fp16 values (the step is chosen so that 3 s is one), staged per
+//    tile in LDS (two passes of 64 channels); the zero-points of the four
+//    groups form a 4-row operand of their own whose MFMA result is added to
+//    the output per group at the end. P is fp16.
 // Requires bf16 inputs, head_dim 128 and an even PSAC rank.
 // Mapping: one workgroup = one wave = 16 Queries of one head and one
 // split of the KV tiles; every wave streams its own 64-token tiles, so many
@@ -158,9 +160,11 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
   // distinct banks), every 16-channel block skewed by 64 bytes so the four
   // blocks written together hit different banks.
   constexpr int VROW = 72;
-  constexpr int VPL = 64 * VROW + 4 * 32;  // halves of one plane
+  constexpr int VPL = 64 * VROW + 4 * 32;  // halves of the code * s plane
   constexpr int PROW = 80;                 // P [Query][token slot] fp16
-  __shared__ __attribute__((aligned(16))) _Float16 vt[2 * VPL];
+  constexpr int ZROW = 72;                 // zero-point plane: [16 rows: groups 0..3, then zeros][token slot]
+  __shared__ __attribute__((aligned(16))) _Float16 vt[VPL];
+  __shared__ __attribute__((aligned(16))) _Float16 zt[16 * ZROW];
   __shared__ __attribute__((aligned(16))) _Float16 pt[NQ * PROW];
   __shared__ __attribute__((aligned(16))) uint32_t kst[kTileKV * 8];  // K codes [token][kg][group] u16
   __shared__ __attribute__((aligned(16))) uint32_t kpr[kTileKV * 4];  // K params [token][group]
@@ -231,6 +235,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
   float mrow[4], lrow[4];
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) O[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 Zs = {0.f, 0.f, 0.f, 0.f};  // zero-point term: [Query 4kg + v][group j], groups 0..3
+  for (int e = lane; e < 12 * ZROW; e += 64) zt[4 * ZROW + e] = (_Float16)0.0f;  // rows 4..15 stay zero
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     mrow[v] = -__builtin_inff();
@@ -277,38 +283,47 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
   };
   // Values of one channel pass: 16 channels of 4 tokens -> hi and lo planes,
   // token slot 4j + tb (hi = fp16(zp + code * step), lo = fp16(rest))
+  // Values of one channel pass: 16 channels of 4 tokens (slots 4j + tb)
+  // as code * s (exact fp16).
   auto dequant_v = [&](const uint32_t (&vc)[4], const uint32_t (&vp)[4]) {
-    float zp[4], st[4];
+    uint32_t cs[4][8];  // [token tb][channel pair p]: channels 2p, 2p+1
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      zp[tb] = half_bits_to_float(vp[tb] & 0xFFFFu);
-      st[tb] = half_bits_to_float(vp[tb] >> 16);
+      const uint32_t sb = vp[tb] >> 16;
+      const half2v s2 = __builtin_bit_cast(half2v, sb | (sb << 16));
+      const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t x = (vc[tb] >> (16 * hh)) & 0xFFFFu;
+        const uint32_t y = x | (x << 14);  // code 2p at bits 4p, code 2p+1 at bits 16 + 4p
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const uint32_t b = ((y >> (4 * pp)) & 0x00030003u) | 0x64006400u;
+          cs[tb][4 * hh + pp] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, b) - k1024) * s2);
+        }
+      }
     }
     const int clb = 32 * (kg >> 1) + 16 * (kg & 1);  // first local channel
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // channels clb + k + 4b (b = 0..3) sit in byte b after the shift
-      uint32_t sp[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) sp[tb] = (vc[tb] >> (2 * k)) & 0x03030303u;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float x[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const float c = (float)((sp[tb] >> (8 * b)) & 0xFFu);  // v_cvt_f32_ubyte<b>
-          x[tb] = __builtin_fmaf(c, st[tb], zp[tb]);
-        }
-        const half2v h0 = pk_f16(x[0], x[1]), h1 = pk_f16(x[2], x[3]);
-        const half2v l0 = pk_f16(__builtin_fmaf((float)h0[0], -1.0f, x[0]), __builtin_fmaf((float)h0[1], -1.0f, x[1]));
-        const half2v l1 = pk_f16(__builtin_fmaf((float)h1[0], -1.0f, x[2]), __builtin_fmaf((float)h1[1], -1.0f, x[3]));
-        const int off = vrow_off(clb + k + 4 * b) + 4 * j;
-        *reinterpret_cast<half4*>(vt + off) = half4{h0[0], h0[1], h1[0], h1[1]};
-        *reinterpret_cast<half4*>(vt + VPL + off) = half4{l0[0], l0[1], l1[0], l1[1]};
-      }
+    for (int pp = 0; pp < 8; ++pp) {
+      // channel 2pp of the four tokens, then channel 2pp + 1
+      const uint32_t e01 = __builtin_amdgcn_perm(cs[1][pp], cs[0][pp], 0x05040100u);
+      const uint32_t e23 = __builtin_amdgcn_perm(cs[3][pp], cs[2][pp], 0x05040100u);
+      const uint32_t o01 = __builtin_amdgcn_perm(cs[1][pp], cs[0][pp], 0x07060302u);
+      const uint32_t o23 = __builtin_amdgcn_perm(cs[3][pp], cs[2][pp], 0x07060302u);
+      *reinterpret_cast<uint2*>(vt + vrow_off(clb + 2 * pp) + 4 * j) = make_uint2(e01, e23);
+      *reinterpret_cast<uint2*>(vt + vrow_off(clb + 2 * pp + 1) + 4 * j) = make_uint2(o01, o23);
     }
   };
-  // o += P vhat for the 64 channels of pass P (hi and lo planes)
+  // Zero-points of the 4 tokens (slots 4j + tb) of the lane's group into row
+  // `grow` of the zero-point plane (lanes of the first half of each group).
+  auto store_zp = [&](const uint32_t (&vp)[4], int grow) {
+    if ((kg & 1) == 0)
+      *reinterpret_cast<uint2*>(zt + grow * ZROW + 4 * j) =
+          make_uint2((vp[0] & 0xFFFFu) | (vp[1] << 16), (vp[2] & 0xFFFFu) | (vp[3] << 16));
+  };
+  // o += P (code * s) for the 64 channels of pass P; in pass 0 also the
+  // zero-point term of all four groups
   auto pv_pass = [&](int P) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -316,10 +331,12 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
 #pragma unroll
       for (int cbl = 0; cbl < 4; ++cbl) {
         const int off = vrow_off(16 * cbl + j) + 32 * ks + 8 * kg;
-        const half8 vh = *reinterpret_cast<const half8*>(vt + off);
-        const half8 vl = *reinterpret_cast<const half8*>(vt + VPL + off);
-        O[4 * P + cbl] = mfma_f16(pa, vh, O[4 * P + cbl]);
-        O[4 * P + cbl] = mfma_f16(pa, vl, O[4 * P + cbl]);
+        const half8 vv = *reinterpret_cast<const half8*>(vt + off);
+        O[4 * P + cbl] = mfma_f16(pa, vv, O[4 * P + cbl]);
+      }
+      if (P == 0) {
+        const half8 vz = *reinterpret_cast<const half8*>(zt + j * ZROW + 32 * ks + 8 * kg);
+        Zs = mfma_f16(pa, vz, Zs);
       }
     }
   };
@@ -360,6 +377,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
         vp1[tb] = cur.vp[tb][1];
       }
       dequant_v(vc0, vp0);
+      store_zp(vp0, kg >> 1);      // groups 0, 1
+      store_zp(vp1, 2 + (kg >> 1));  // groups 2, 3 (their codes are staged in pass 1)
     }
     // Prefetch without branches (indices clamped to the last tile): a load on
     // one path only would make the next wait cover every load in flight.
@@ -436,6 +455,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
         lrow[v] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < D / 16; ++cb) O[cb][v] *= alpha;
+        Zs[v] *= alpha;
       }
     }
 #pragma unroll
@@ -477,6 +497,15 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
 
   // ---- epilogue: row sums over the 16 token lanes; normalized output or a
   // split partial (o, running max, row sum) for the merge
+  // the zero-point term: group G of Query 4kg + v sits in lane (kg, G)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float zg[4];
+#pragma unroll
+    for (int G = 0; G < 4; ++G) zg[G] = __shfl(Zs[v], 16 * kg + G);
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) O[cb][v] += zg[cb >> 1];
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const float l = row16_sum(lrow[v]);
