@@ -152,7 +152,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 template <int NQ>
-__global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const AttnPlan p) {
+__global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const AttnPlan p) {
   static_assert(NQ == 16, "one 16-Query block per wave");
   constexpr int D = 128, NG = 4;
   // vhat^T of one 64-channel pass, fp16 hi and lo planes: [channel][token
@@ -286,31 +286,33 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
   // Values of one channel pass: 16 channels of 4 tokens (slots 4j + tb)
   // as code * s (exact fp16).
   auto dequant_v = [&](const uint32_t (&vc)[4], const uint32_t (&vp)[4]) {
-    uint32_t cs[4][8];  // [token tb][channel pair p]: channels 2p, 2p+1
+    const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    half2v s2[4];
+    uint32_t y[4][2];  // code 2p at bits 4p, code 2p+1 at bits 16 + 4p of each 8-code half
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const uint32_t sb = vp[tb] >> 16;
-      const half2v s2 = __builtin_bit_cast(half2v, sb | (sb << 16));
-      const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+      s2[tb] = __builtin_bit_cast(half2v, sb | (sb << 16));
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const uint32_t x = (vc[tb] >> (16 * hh)) & 0xFFFFu;
-        const uint32_t y = x | (x << 14);  // code 2p at bits 4p, code 2p+1 at bits 16 + 4p
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const uint32_t b = ((y >> (4 * pp)) & 0x00030003u) | 0x64006400u;
-          cs[tb][4 * hh + pp] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, b) - k1024) * s2);
-        }
+        y[tb][hh] = x | (x << 14);
       }
     }
     const int clb = 32 * (kg >> 1) + 16 * (kg & 1);  // first local channel
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
+      uint32_t cs[4];  // channels 2pp, 2pp + 1 of token tb
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const uint32_t b = ((y[tb][pp >> 2] >> (4 * (pp & 3))) & 0x00030003u) | 0x64006400u;
+        cs[tb] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, b) - k1024) * s2[tb]);
+      }
       // channel 2pp of the four tokens, then channel 2pp + 1
-      const uint32_t e01 = __builtin_amdgcn_perm(cs[1][pp], cs[0][pp], 0x05040100u);
-      const uint32_t e23 = __builtin_amdgcn_perm(cs[3][pp], cs[2][pp], 0x05040100u);
-      const uint32_t o01 = __builtin_amdgcn_perm(cs[1][pp], cs[0][pp], 0x07060302u);
-      const uint32_t o23 = __builtin_amdgcn_perm(cs[3][pp], cs[2][pp], 0x07060302u);
+      const uint32_t e01 = __builtin_amdgcn_perm(cs[1], cs[0], 0x05040100u);
+      const uint32_t e23 = __builtin_amdgcn_perm(cs[3], cs[2], 0x05040100u);
+      const uint32_t o01 = __builtin_amdgcn_perm(cs[1], cs[0], 0x07060302u);
+      const uint32_t o23 = __builtin_amdgcn_perm(cs[3], cs[2], 0x07060302u);
       *reinterpret_cast<uint2*>(vt + vrow_off(clb + 2 * pp) + 4 * j) = make_uint2(e01, e23);
       *reinterpret_cast<uint2*>(vt + vrow_off(clb + 2 * pp + 1) + 4 * j) = make_uint2(o01, o23);
     }
@@ -341,9 +343,11 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
     }
   };
 
-  // One tile: `cur` holds its raw words, `nxt` those of the next tile (in
-  // flight); `cur` is refilled with the tile after next once consumed.
-  auto process = [&](int tile, DecRaw& cur, DecRaw& nxt, floatx4 (&qcc)[4], floatx4 (&qcn)[4]) {
+  // One tile: `cur` holds its raw words and qcc its q . C values. Once the
+  // K words are staged and the V words copied out, `cur` is refilled with
+  // the next tile's words; its q . C values are gathered at the end (their
+  // ids have arrived by then).
+  auto process = [&](int tile, DecRaw& cur, floatx4 (&qcc)[4]) {
     const TileInfo ti = tile_info(p, tile);
     // ---- stage the K words: codes permuted to [token][kg][group] so a lane
     // reads the 4 groups of its channel octet in one 8-byte read
@@ -382,8 +386,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
     }
     // Prefetch without branches (indices clamped to the last tile): a load on
     // one path only would make the next wait cover every load in flight.
-    load_raw(cur, tile_info(p, tile + 2 < thi ? tile + 2 : thi - 1));
-    load_qc(qcn, tile_info(p, tile + 1 < thi ? tile + 1 : thi - 1), nxt.id);
+    const TileInfo tn = tile_info(p, tile + 1 < thi ? tile + 1 : thi - 1);
+    load_raw(cur, tn);
     wave_sync();
 
     // ---- PSAC Query operand of this epoch: lanes kg < 2 hold qU_hi, kg >= 2 qU_lo
@@ -478,21 +482,16 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a, const At
     wave_sync();
     pv_pass(1);
     wave_sync();
+    load_qc(qcc, tn, cur.id);
   };
 
-  DecRaw ra, rb;
-  floatx4 qa4[4], qb4[4];
-  int tile = tlo;
+  DecRaw rw;
+  floatx4 qcv[4];
   if (tlo < thi) {
     const TileInfo t0 = tile_info(p, tlo);
-    load_raw(ra, t0);
-    load_raw(rb, tile_info(p, tlo + 1 < thi ? tlo + 1 : thi - 1));
-    load_qc(qa4, t0, ra.id);
-    for (; tile + 1 < thi; tile += 2) {
-      process(tile, ra, rb, qa4, qb4);
-      process(tile + 1, rb, ra, qb4, qa4);
-    }
-    if (tile < thi) process(tile, ra, rb, qa4, qb4);
+    load_raw(rw, t0);
+    load_qc(qcv, t0, rw.id);
+    for (int tile = tlo; tile < thi; ++tile) process(tile, rw, qcv);
   }
 
   // ---- epilogue: row sums over the 16 token lanes; normalized output or a
