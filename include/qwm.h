@@ -36,8 +36,9 @@
  *   tensor). The handle itself is a small host object.
  * - Work is enqueued on the HIP stream given at qwm_create; the caller keeps
  *   input buffers alive until that stream has passed the call (every read of
- *   a caller buffer is enqueued on it). Two calls block the host:
- *   qwm_profile_read waits for the timing events it reads, and qwm_destroy
+ *   a caller buffer is enqueued on it). Three calls block the host:
+ *   qwm_profile_read waits for the timing events it reads,
+ *   qwm_profile_work for the counter it reads, and qwm_destroy
  *   waits for the eigensolve stream (when one was started) before releasing
  *   it. Every other call only enqueues work. The one exception
  *   to the single stream is the eigensolve of qwm_build_subspace, which
@@ -283,6 +284,17 @@ qwm_status qwm_profile_enable(qwm_cache* cache, int32_t enable);
 /* Total milliseconds and launch count of kernel class `kid` since enabling.
  * Synchronizes the cache stream. */
 qwm_status qwm_profile_read(qwm_cache* cache, int32_t kid, double* total_ms, int64_t* launches);
+/* Work of the centroid rule (QSAC assignment, roboind.com article, section
+ * "Step 1") done by launches of class `kid` since profiling was enabled, as
+ * channel evaluations: one is a (Key, centroid, channel) residual term
+ * r = k - c with its share of the group's max, min or square. A full
+ * assignment pass (QWM_K_QUANTIZE, and the first k-means iteration under
+ * QWM_K_ASSIGN) makes heads x tokens x n_centroids x head_dim of them; the
+ * pruned k-means assignment counts those its waves computed, so the figure
+ * is the work done, not the brute-force bound. Other classes report 0.
+ * Synchronizes the cache stream when a pruned launch has counted; fails with
+ * QWM_ERR_INVALID_ARG on a NULL argument or a bad class. */
+qwm_status qwm_profile_work(qwm_cache* cache, int32_t kid, double* evaluations);
 
 const char* qwm_last_error(void);
 const char* qwm_version(void);

@@ -21,7 +21,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 23
     L = Q.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -181,6 +181,10 @@ def test_call_order_and_argument_checks():
     assert L.qwm_export_bytes(h, 0, 0, ctypes.byref(nb)) == Q.QWM_OK and nb.value == 0
     assert L.qwm_profile_read(h, 99, ctypes.byref(ctypes.c_double()), ctypes.byref(ctypes.c_int64())) == \
         Q.QWM_ERR_INVALID_ARG
+    ev = ctypes.c_double(-1.0)
+    assert L.qwm_profile_work(h, 99, ctypes.byref(ev)) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_profile_work(h, 6, None) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_profile_work(h, 6, ctypes.byref(ev)) == Q.QWM_OK and ev.value == 0.0
     assert L.qwm_destroy(h) == Q.QWM_OK
     assert L.qwm_destroy(None) == Q.QWM_ERR_INVALID_ARG
 

@@ -381,6 +381,39 @@ def test_build_calibration(name, heads, n_keys, iters, seed):
             assert np.array_equal(C[h], Co)
 
 
+# The work counter behind the k-means roofline: a full assignment pass makes
+# heads x Keys x centroids x head_dim channel evaluations; the pruned pass
+# counts what its waves computed, at least the previous centroid's cost of
+# every Key and at most the full pass. Profiling must not change the result.
+@pytest.mark.parametrize("name,heads,n_keys,iters", [("video_chunk", 2, 1760, 3), ("wm_layer", 2, 9000, 3)])
+def test_assign_work_counter(name, heads, n_keys, iters):
+    w = small(W.workload(name), heads=heads)
+    log(f"[work] {name} H={heads} n_keys={n_keys} iters={iters}")
+    gens = [W.HeadGen(w, h, 0) for h in range(heads)]
+    qh = to_dev([g.hist_queries() for g in gens], w.dtype)
+    keys = to_dev([g.keys(0, n_keys) for g in gens], w.dtype)
+    Cs, works = [], []
+    for prof in (False, True):
+        cache = _cache(w, max_build=n_keys)
+        cache.profile_enable(prof)
+        cache.build_subspace(qh)
+        cache.build_centroids(keys, iters)
+        Cs.append(cache.export_calibration(0)[0].cpu())
+        works.append(cache.profile_work("assign"))
+        cache.profile_enable(False)
+    assert torch.equal(Cs[0].view(torch.int16) if Cs[0].dtype == torch.bfloat16 else Cs[0],
+                       Cs[1].view(torch.int16) if Cs[1].dtype == torch.bfloat16 else Cs[1])
+    assert works[0] == 0.0
+    full = float(heads * n_keys * w.n_centroids * w.head_dim)
+    log(f"  evaluations {works[1]:.6g} = {works[1] / full:.3f} full passes")
+    if w.n_centroids < 128:
+        assert works[1] == iters * full
+    else:
+        floor = full + (iters - 1) * float(heads * n_keys * w.head_dim)
+        assert floor <= works[1] <= iters * full
+        assert works[1] < 0.9 * iters * full  # the bound skips work on this data
+
+
 # Builds at the edges of the k-means kernels: fewer Keys than centroids
 # (duplicate seeds that never win a tie), a single Key, and odd Key counts
 # whose per-head id rows start off a 16-byte boundary (the update kernel reads

@@ -691,7 +691,7 @@ __global__ __launch_bounds__(NWB * 64) void assign_pruned_kernel(const void* key
                                                                  const float* C32, const float* S,
                                                                  const int32_t* perm, const int32_t* off,
                                                                  const int32_t* woff, const float* ccdtab,
-                                                                 uint8_t* ids_out) {
+                                                                 uint8_t* ids_out, unsigned long long* work) {
   constexpr int NG = D / kGroup;
   __shared__ float bj[NWB][64];
   __shared__ int bi[NWB][64];
@@ -732,6 +732,9 @@ __global__ __launch_bounds__(NWB * 64) void assign_pruned_kernel(const void* key
   float kf[D];
   load_row_span<D, DT>(keys, ((int64_t)h * n + tok) * D, kf);
   const float Jb = assign_cost<OBJ, D>(kf, Cb, SG);
+  // group terms computed for each Key of this wave (wave-uniform); the cost of
+  // the previous centroid, which every wave repeats, counts in wave 0 only
+  int terms = (NWB == 1 || wave == 0) ? NG : 0;
   float d = (lane < cnt) ? sqrtf(Jb) : 0.0f;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) d = fmaxf(d, __shfl_xor(d, o));
@@ -756,6 +759,7 @@ __global__ __launch_bounds__(NWB * 64) void assign_pruned_kernel(const void* key
 #pragma unroll
       for (int G = 0; G < NG; ++G) {
         const float u = group_term<OBJ, D>(kf, crow, G, SG);
+        ++terms;
         J = (G == 0) ? u : J + u;
         if (G < NG - 1 && __all(idle || J > bestJ || (J == bestJ && c > best))) {
           lost = true;
@@ -768,6 +772,8 @@ __global__ __launch_bounds__(NWB * 64) void assign_pruned_kernel(const void* key
       }
     }
   }
+  // channel evaluations of this wave: its group terms times the Keys it holds
+  if (work != nullptr && lane == 0) atomicAdd(work, (unsigned long long)terms * kGroup * (unsigned long long)cnt);
   if constexpr (NWB == 1) {
     if (lane < cnt) ids_out[(int64_t)h * n + tok] = (uint8_t)best;
   } else {
@@ -903,20 +909,21 @@ hipError_t launch_kmeans_ccd(int D, int obj, int H, int m, const float* C32, con
 
 hipError_t launch_kmeans_assign_pruned(int D, int dtype, int obj, const void* keys, int64_t n, int H, int m,
                                        const float* C32, const float* S, const int32_t* perm, const int32_t* off,
-                                       const int32_t* woff, const float* ccd, uint8_t* ids_out, hipStream_t s) {
+                                       const int32_t* woff, const float* ccd, uint8_t* ids_out,
+                                       unsigned long long* work, hipStream_t s) {
   dim3 grid((unsigned)((n + 63) / 64 + m), (unsigned)H);
   if (obj != kObjQsac && obj != kObjNearest) return hipErrorInvalidValue;
   const int nwb = pruned_waves(m);
 #define QWM_PLAUNCH(DD, TT, OO)                                                                                      \
   if (nwb == 1)                                                                                                      \
     hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 1>), grid, dim3(64), 0, s, keys, n, m, C32, S, perm, off,   \
-                       woff, ccd, ids_out);                                                                               \
+                       woff, ccd, ids_out, work);                                                                               \
   else if (nwb == 2)                                                                                                 \
     hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 2>), grid, dim3(128), 0, s, keys, n, m, C32, S, perm, off,  \
-                       woff, ccd, ids_out);                                                                               \
+                       woff, ccd, ids_out, work);                                                                               \
   else                                                                                                               \
     hipLaunchKernelGGL((assign_pruned_kernel<DD, TT, OO, 4>), grid, dim3(256), 0, s, keys, n, m, C32, S, perm, off,  \
-                       woff, ccd, ids_out);
+                       woff, ccd, ids_out, work);
 #define QWM_POBJ(DD, TT)                \
   if (obj == kObjNearest) {             \
     QWM_PLAUNCH(DD, TT, kObjNearest)    \

@@ -44,7 +44,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct Layout {
   size_t kcode, vcode, kparam, vparam, ids, coef;
   size_t epochC, epochS, epochU, C32, kmC32, U64, gram, diag, build_ids, km_perm, km_off, km_woff, km_ccd, qU, qc,
-      part_o, part_ml;
+      part_o, part_ml, work;
   size_t total;
   int64_t capP, part_rows;
 };
@@ -131,6 +131,7 @@ Layout make_layout(const qwm_desc* d) {
   L.qc = take((size_t)(H * E * m * nqp_max * 4));
   L.part_o = take((size_t)(pr * D * 4));
   L.part_ml = take((size_t)(pr * 2 * 4));
+  L.work = take(sizeof(unsigned long long) * QWM_K_COUNT);  // profiling work counters
   L.total = off;
   return L;
 }
@@ -198,6 +199,11 @@ struct qwm_cache {
   std::vector<ProfRec> pending;
   double prof_ms[QWM_K_COUNT] = {};
   int64_t prof_n[QWM_K_COUNT] = {};
+  // channel evaluations of the centroid rule while profiling: full passes are
+  // counted here, the pruned assignment counts its own in the arena's `work`
+  // counters, cleared before its first launch after profiling was enabled
+  double work_host[QWM_K_COUNT] = {};
+  bool work_clear = true;
 
   uint8_t* slotC(int slot) const {
     return arena + L.epochC + (size_t)slot * H * m * D * esz;
@@ -223,6 +229,20 @@ struct qwm_cache {
   float* qc() const { return reinterpret_cast<float*>(arena + L.qc); }
   float* part_o() const { return reinterpret_cast<float*>(arena + L.part_o); }
   float* part_ml() const { return reinterpret_cast<float*>(arena + L.part_ml); }
+  unsigned long long* work() const { return reinterpret_cast<unsigned long long*>(arena + L.work); }
+  // the pruned assignment's counter while profiling (cleared on first use), else null
+  unsigned long long* work_counter(int kid) {
+    if (!profile || no_events) return nullptr;
+    if (work_clear) {
+      if (qwm::launch_fill(reinterpret_cast<float*>(work()), 2 * QWM_K_COUNT, 0.0f, stream) != hipSuccess)
+        return nullptr;
+      work_clear = false;
+    }
+    return work() + kid;
+  }
+  void count_full_pass(int kid, int64_t n) {
+    if (profile && !no_events) work_host[kid] += (double)H * (double)n * m * D;
+  }
 
   // Launch wrapper: optional event timing around one launch on stream `s`.
   bool no_events = false;  // set by qwm_attend_noalloc: record no timing events
@@ -714,6 +734,7 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
       a.obj = c->obj;
       e = c->run(QWM_K_ASSIGN, [&] { return qwm::launch_quantize(c->D, c->dtype, a, c->stream); });
       if (e != hipSuccess) return fail_hip(e, "kmeans assign");
+      c->count_full_pass(QWM_K_ASSIGN, n_keys);
     } else {  // the same ids, skipping candidates the triangle inequality rules out
       e = c->run(QWM_K_OTHER, [&] {
         return qwm::launch_kmeans_ccd(c->D, c->obj, c->H, c->m, c->kmC32(), c->slotS(stg), c->km_ccd(), c->stream);
@@ -724,10 +745,11 @@ qwm_status qwm_build_centroids(qwm_cache* c, const void* keys, int64_t n_keys, i
                                          c->stream);
       });
       if (e != hipSuccess) return fail_hip(e, "kmeans bucket");
+      unsigned long long* work = c->work_counter(QWM_K_ASSIGN);
       e = c->run(QWM_K_ASSIGN, [&] {
         return qwm::launch_kmeans_assign_pruned(c->D, c->dtype, c->obj, keys, n_keys, c->H, c->m, c->kmC32(), c->slotS(stg),
                                                 c->km_perm(), c->km_off(), c->km_woff(), c->km_ccd(), c->build_ids(),
-                                                c->stream);
+                                                work, c->stream);
       });
       if (e != hipSuccess) return fail_hip(e, "kmeans assign");
     }
@@ -819,6 +841,7 @@ qwm_status qwm_quantize_append(qwm_cache* c, const void* k, const void* v, int64
   a.r = c->r;
   a.obj = c->obj;
   hipError_t e = c->run(QWM_K_QUANTIZE, [&] { return qwm::launch_quantize(c->D, c->dtype, a, c->stream); });
+  if (e == hipSuccess) c->count_full_pass(QWM_K_QUANTIZE, n_tokens);
   if (e != hipSuccess) return fail_hip(e, "quantize");
   c->length += n_tokens;
   return QWM_OK;
@@ -1041,7 +1064,9 @@ qwm_status qwm_profile_enable(qwm_cache* c, int32_t enable) {
   for (int i = 0; i < QWM_K_COUNT; ++i) {
     c->prof_ms[i] = 0.0;
     c->prof_n[i] = 0;
+    c->work_host[i] = 0.0;
   }
+  c->work_clear = true;
   c->profile = enable != 0;
   return QWM_OK;
 }
@@ -1066,6 +1091,22 @@ qwm_status qwm_profile_read(qwm_cache* c, int32_t kid, double* total_ms, int64_t
   c->pending.clear();
   *total_ms = c->prof_ms[kid];
   *launches = c->prof_n[kid];
+  return QWM_OK;
+}
+
+qwm_status qwm_profile_work(qwm_cache* c, int32_t kid, double* evaluations) {
+  if (!c || !evaluations) return fail(QWM_ERR_INVALID_ARG, "NULL argument");
+  if (kid < 0 || kid >= QWM_K_COUNT) return fail(QWM_ERR_INVALID_ARG, "bad kernel id");
+  unsigned long long dev_count = 0;
+  if (!c->work_clear) {  // a pruned launch wrote the counters since profiling was enabled
+    qwm_status st;
+    if ((st = need_device(c)) != QWM_OK) return st;
+    DeviceGuard g(c->device);
+    hipError_t e = hipMemcpyAsync(&dev_count, c->work() + kid, sizeof(dev_count), hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return fail_hip(e, "profile work read");
+  }
+  *evaluations = c->work_host[kid] + (double)dev_count;
   return QWM_OK;
 }
 

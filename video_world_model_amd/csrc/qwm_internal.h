@@ -65,13 +65,17 @@ hipError_t launch_kmeans_update(int D, int dtype, const void* keys, const uint8_
 // skipping candidates that provably lose.
 hipError_t launch_kmeans_bucket(const uint8_t* ids, int64_t n, int H, int m, int32_t* perm, int32_t* off,
                                 int32_t* woff, hipStream_t s);
+// With `work` not null, the pruned assignment adds to *work the channel
+// evaluations it made: for every wave, the Keys it holds times 32 times the
+// group terms it computed (the cost of the previous centroid included).
 // ccd[h][b][c] = sqrt of the rule's cost between centroids b and c (the
 // pruned assignment's bound), every pair of every head
 hipError_t launch_kmeans_ccd(int D, int obj, int H, int m, const float* C32, const float* S, float* ccd,
                              hipStream_t s);
 hipError_t launch_kmeans_assign_pruned(int D, int dtype, int obj, const void* keys, int64_t n, int H, int m,
                                        const float* C32, const float* S, const int32_t* perm, const int32_t* off,
-                                       const int32_t* woff, const float* ccd, uint8_t* ids_out, hipStream_t s);
+                                       const int32_t* woff, const float* ccd, uint8_t* ids_out,
+                                       unsigned long long* work, hipStream_t s);
 // p[0 .. n) = v
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 // Copy a staged calibration (C, S, U) into an epoch slot and write its shadows.

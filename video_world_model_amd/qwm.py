@@ -84,6 +84,7 @@ _SIGS = {
     "qwm_attend_top1": [_VP, _VP, _I64, _VP, _I64, _VP],
     "qwm_profile_enable": [_VP, _I32],
     "qwm_profile_read": [_VP, _I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)],
+    "qwm_profile_work": [_VP, _I32, ctypes.POINTER(ctypes.c_double)],
 }
 
 
@@ -394,3 +395,10 @@ class Cache:
         n = _I64(0)
         check(lib().qwm_profile_read(self._h, KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n)))
         return float(ms.value), int(n.value)
+
+    def profile_work(self, kernel: str) -> float:
+        """Channel evaluations of the centroid rule made by `kernel` launches
+        since profiling was enabled (qwm_profile_work)."""
+        ev = ctypes.c_double(0)
+        check(lib().qwm_profile_work(self._h, KERNELS[kernel], ctypes.byref(ev)))
+        return float(ev.value)
