@@ -129,9 +129,23 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int h = (int)blockIdx.z;
-  const int split = blockIdx.y;
-  const int64_t qw0 = (int64_t)blockIdx.x * a.qpb + wave * 32;
+  // Workgroups go to the 8 XCDs in turn (dispatch id mod 8). Renumber them so
+  // that each XCD receives one contiguous run of logical ids, Query blocks
+  // fastest: the Query blocks of one (head, split) then run side by side on
+  // one XCD and read each KV tile once into its L2 (a bijection of the grid
+  // whatever the dispatch order).
+  int h, split, qblk;
+  {
+    const int nwg = (int)gridDim.x, bid = (int)blockIdx.x;
+    const int per = nwg >> 3, rem = nwg & 7, xcd = bid & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+    const int nqb = (int)((a.nq + a.qpb - 1) / a.qpb);
+    qblk = logical % nqb;
+    const int hs = logical / nqb;
+    split = hs % a.splits;
+    h = hs / a.splits;
+  }
+  const int64_t qw0 = (int64_t)qblk * a.qpb + wave * 32;
   const bool wave_live = wave * 32 < a.qpb && qw0 < a.nq;
   const bool lead = wave < 4;  // the group that computes the next tile's logits at the end of a step
   const int kq = wave;  // producer channel slice 16 kq .. 16 kq + 15 (group kq / 2)
@@ -636,7 +650,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
 }  // namespace
 
 hipError_t launch_attend_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
-  dim3 grid((unsigned)((a.nq + a.qpb - 1) / a.qpb), (unsigned)a.splits, (unsigned)a.H), block(kAttnThreads);
+  const int64_t nwg = (a.nq + a.qpb - 1) / a.qpb * a.splits * a.H;
+  if (nwg <= 0 || nwg > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nwg), block(kAttnThreads);
   if (a.nself > 0)
     hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, block, 0, s, a, p);
   else
