@@ -85,10 +85,11 @@ __device__ __forceinline__ half8 codes_to_f16(uint32_t w) {
 }
 
 // ---------------------------------------------------------------- q . C table
-// qc[h][e][c][j] = q_j . C_c^(e) for Queries j < nqp (zero past nq). One wave
-// per 16 centroids x 16 Queries, K = 128 in four bf16 MFMAs.
+// qc[h][e][c][j] = sign * q_j . C_c^(e) for Queries j < nqp (zero past nq),
+// sign = the sign of the softmax scale. One wave per 16 centroids x 16
+// Queries, K = 128 in four bf16 MFMAs.
 __global__ __launch_bounds__(64) void qc_kernel(const uint16_t* q, int64_t nq, int nqp, const uint16_t* Cbase,
-                                                int64_t epoch_C_stride, int H, int m, float* qc) {
+                                                int64_t epoch_C_stride, int H, int m, float sign, float* qc) {
   const int lane = threadIdx.x, i = lane & 15, kg = lane >> 4;
   const int qb = blockIdx.x, cb = blockIdx.y;
   const int h = blockIdx.z % H, e = blockIdx.z / H;
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(64) void qc_kernel(const uint16_t* q, int64_t nq, i
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int cr = 16 * cb + 4 * kg + v;
-    if (cr < m) qc[(((size_t)h * (gridDim.z / H) + e) * m + cr) * nqp + 16 * qb + i] = acc[v];
+    if (cr < m) qc[(((size_t)h * (gridDim.z / H) + e) * m + cr) * nqp + 16 * qb + i] = sign * acc[v];
   }
 }
 
@@ -119,8 +120,9 @@ struct TileInfo {
   int tcount;  // tokens in the tile (1..64)
 };
 
-__device__ __forceinline__ TileInfo tile_info(const AttnPlan& p, int tile) {
-  int sg = 0;
+// Tile `tile` of the plan; `sg` is a segment cursor at or before the tile's
+// segment (tiles are visited in increasing order, so it only moves forward).
+__device__ __forceinline__ TileInfo tile_info(const AttnPlan& p, int tile, int& sg) {
   while (p.tile_prefix[sg + 1] <= tile) ++sg;
   TileInfo ti;
   ti.ep = p.seg_epoch[sg];
@@ -172,8 +174,23 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
   auto vrow_off = [](int cl) { return cl * VROW + 32 * (cl >> 4); };  // local channel 0..63
 
   const int lane = threadIdx.x, j = lane & 15, kg = lane >> 4;
-  const int h = blockIdx.z, split = blockIdx.y;
-  const int64_t q0 = (int64_t)blockIdx.x * NQ;
+  // Workgroups go to the 8 XCDs in turn (dispatch id mod 8). Renumber them so
+  // that each XCD receives one contiguous run of logical ids (Query blocks,
+  // then splits, then heads): an XCD then serves a few heads, whose q . C
+  // tables stay in its L2 (a bijection of the grid whatever the dispatch
+  // order).
+  int h, split, qblk;
+  {
+    const int nwg = (int)gridDim.x, bid = (int)blockIdx.x;
+    const int per = nwg >> 3, rem = nwg & 7, xcd = bid & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
+    const int nqb = (int)((a.nq + NQ - 1) / NQ);
+    qblk = logical % nqb;
+    const int hs = logical / nqb;
+    split = hs % a.splits;
+    h = hs / a.splits;
+  }
+  const int64_t q0 = (int64_t)qblk * NQ;
   // the softmax runs in the log2 domain with a positive factor; a negative
   // scale is carried by negated Queries (exact) and a negated q . C table
   const float qsign = (a.scale_log2 < 0.0f) ? -1.0f : 1.0f;
@@ -347,8 +364,9 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
   // K words are staged and the V words copied out, `cur` is refilled with
   // the next tile's words; its q . C values are gathered at the end (their
   // ids have arrived by then).
-  auto process = [&](int tile, DecRaw& cur, floatx4 (&qcc)[4]) {
-    const TileInfo ti = tile_info(p, tile);
+  int sg = 0;  // segment cursor of the tiles visited
+  auto process = [&](int tile, DecRaw& cur, floatx4 (&qcc)[4], TileInfo& tinfo) {
+    const TileInfo ti = tinfo;
     // ---- stage the K words: codes permuted to [token][kg][group] so a lane
     // reads the 4 groups of its channel octet in one 8-byte read
     {
@@ -386,7 +404,7 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
     }
     // Prefetch without branches (indices clamped to the last tile): a load on
     // one path only would make the next wait cover every load in flight.
-    const TileInfo tn = tile_info(p, tile + 1 < thi ? tile + 1 : thi - 1);
+    const TileInfo tn = tile_info(p, tile + 1 < thi ? tile + 1 : thi - 1, sg);
     load_raw(cur, tn);
     wave_sync();
 
@@ -417,12 +435,11 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       const uint4 kp = *reinterpret_cast<const uint4*>(kpr + tt * 4);
       const uint4 cf = *reinterpret_cast<const uint4*>(cst + tt * 8 + 4 * (kg & 1));
       const uint32_t kpw[4] = {kp.x, kp.y, kp.z, kp.w};
-      half8 bzp;
-#pragma unroll
-      for (int G = 0; G < NG; ++G) {
-        bzp[G] = (kg < 2) ? __builtin_bit_cast(_Float16, (uint16_t)(kpw[G] & 0xFFFFu)) : (_Float16)0.0f;
-        bzp[G + 4] = (_Float16)0.0f;
-      }
+      // zero-points of groups 0..3 at k = 8kg + G; ax2 is zero for k = 8kg + 4..7
+      // and for kg >= 2, where the (finite) repeats below meet zeros
+      const uint32_t z01 = __builtin_amdgcn_perm(kp.y, kp.x, 0x05040100u);
+      const uint32_t z23 = __builtin_amdgcn_perm(kp.w, kp.z, 0x05040100u);
+      const half8 bzp = __builtin_bit_cast(half8, make_uint4(z01, z23, z01, z23));
       floatx4 acc = mfma_f16(ax1, __builtin_bit_cast(half8, cf), floatx4{0.f, 0.f, 0.f, 0.f});
       acc = mfma_f16(ax2, bzp, acc);
       const uint32_t cws[4] = {cw.x & 0xFFFFu, cw.x >> 16, cw.y & 0xFFFFu, cw.y >> 16};
@@ -434,9 +451,14 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
         for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(st, dg[v], acc[v]);
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += qsign * qcc[tb][v];
-      if (tt >= ti.tcount) acc = floatx4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      for (int v = 0; v < 4; ++v) acc[v] += qcc[tb][v];  // the table carries the sign
       S[tb] = acc;
+    }
+    if (ti.tcount < kTileKV) {  // wave-uniform: the last tile of a segment
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        if (16 * tb + j >= ti.tcount)
+          S[tb] = floatx4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
     }
 
     // ---- online softmax (log2 domain); the running max is raised only when
@@ -483,15 +505,16 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
     pv_pass(1);
     wave_sync();
     load_qc(qcc, tn, cur.id);
+    tinfo = tn;
   };
 
   DecRaw rw;
   floatx4 qcv[4];
   if (tlo < thi) {
-    const TileInfo t0 = tile_info(p, tlo);
-    load_raw(rw, t0);
-    load_qc(qcv, t0, rw.id);
-    for (int tile = tlo; tile < thi; ++tile) process(tile, rw, qcv);
+    TileInfo ti = tile_info(p, tlo, sg);
+    load_raw(rw, ti);
+    load_qc(qcv, ti, rw.id);
+    for (int tile = tlo; tile < thi; ++tile) process(tile, rw, qcv, ti);
   }
 
   // ---- epilogue: row sums over the 16 token lanes; normalized output or a
@@ -531,15 +554,17 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
 }  // namespace
 
 hipError_t launch_qc(const void* q, int64_t nq, int nqp, const void* Cbase, int64_t epoch_C_stride, int H, int m,
-                     int E, float* qc, hipStream_t s) {
+                     int E, float sign, float* qc, hipStream_t s) {
   dim3 grid((unsigned)(nqp / 16), (unsigned)((m + 15) / 16), (unsigned)(H * E)), block(64);
   hipLaunchKernelGGL(qc_kernel, grid, block, 0, s, reinterpret_cast<const uint16_t*>(q), nq, nqp,
-                     reinterpret_cast<const uint16_t*>(Cbase), epoch_C_stride, H, m, qc);
+                     reinterpret_cast<const uint16_t*>(Cbase), epoch_C_stride, H, m, sign, qc);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const AttnPlan& p, hipStream_t s) {
-  dim3 grid((unsigned)((a.nq + kDecodeQ - 1) / kDecodeQ), (unsigned)a.splits, (unsigned)a.H), block(64);
+  const int64_t nwg = (a.nq + kDecodeQ - 1) / kDecodeQ * a.splits * a.H;
+  if (nwg <= 0 || nwg > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nwg), block(64);
   hipLaunchKernelGGL(decode_kernel<kDecodeQ>, grid, block, 0, s, a, p);
   return hipGetLastError();
 }

@@ -414,8 +414,11 @@ qwm_status attend_decode(qwm_cache* c, const void* q, int64_t n_q, float softmax
   const int E = (int)c->epoch_start.size();
   const int64_t qtiles = (n_q + qwm::kDecodeQ - 1) / qwm::kDecodeQ;
   const int nqp = (int)(qtiles * qwm::kDecodeQ);
-  // about 8 single-wave workgroups per CU, at least 4 tiles per split
-  int64_t splits = (8 * (int64_t)c->ncu + qtiles * c->H - 1) / (qtiles * c->H);
+  // as many single-wave workgroups as the CUs hold at once (one round: a
+  // workgroup past that would start when the first round ends), at least 4
+  // tiles per split
+  int64_t splits = (int64_t)qwm::kDecodeWavesPerCU * c->ncu / (qtiles * c->H);
+  if (splits < 1) splits = 1;
   const int64_t cap = T / 4 > 1 ? T / 4 : 1;
   if (splits > cap) splits = cap;
   if (splits > 64) splits = 64;
@@ -445,7 +448,8 @@ qwm_status attend_decode(qwm_cache* c, const void* q, int64_t n_q, float softmax
     if (e != hipSuccess) return fail_hip(e, "qU");
   }
   e = c->run(QWM_K_QU, [&] {
-    return qwm::launch_qc(q, n_q, nqp, c->slotC(0), (int64_t)c->H * c->m * c->D, c->H, c->m, E, w.qc, c->stream);
+    return qwm::launch_qc(q, n_q, nqp, c->slotC(0), (int64_t)c->H * c->m * c->D, c->H, c->m, E,
+                          softmax_scale < 0.0f ? -1.0f : 1.0f, w.qc, c->stream);
   });
   if (e != hipSuccess) return fail_hip(e, "qC");
   e = c->run(QWM_K_ATTEND, [&] { return qwm::launch_decode(d, p, c->stream); });

@@ -159,10 +159,12 @@ struct DecodeArgs {
   float* part_o;      // [splits][H][nq][128]
   float* part_ml;     // [splits][H][nq][2]
 };
+// sign: the sign of the softmax scale, carried by the table
 hipError_t launch_qc(const void* q, int64_t nq, int nqp, const void* Cbase, int64_t epoch_C_stride, int H, int m,
-                     int E, float* qc, hipStream_t s);
+                     int E, float sign, float* qc, hipStream_t s);
 constexpr int kDecodeQ = 16;        // Queries per decode workgroup
 constexpr int kDecodeMaxQ = 64;     // largest n_q served by the decode kernel
+constexpr int kDecodeWavesPerCU = 8;  // resident decode workgroups per CU (2 waves per SIMD)
 hipError_t launch_decode(const DecodeArgs& a, const AttnPlan& p, hipStream_t s);
 
 // ---------------------------------------------------------------- export
