@@ -606,9 +606,11 @@ def main():
     ap.add_argument("--graph", type=int, default=0,
                     help="1: capture one step in a HIP graph (through torch.cuda.graph) and time its replays; "
                          "0: time eager calls")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle's timed sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="heads in the oracle's timed sample of the streaming, long_horizon and wm_layer steps "
+                         "(tiny and video_chunk take one head per core); 0: skip the oracle")
     ap.add_argument("--cpu-cores", type=int, default=0,
-                    help="processes of the streaming oracle sample (default: one per available core)")
+                    help="processes of the oracle sample (default: one per available core)")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="MiB written before every timed step, outside its events, to evict the L2 caches and "
                          "the 256 MB MALL (streaming and long_horizon; 0: no flush)")
@@ -629,7 +631,14 @@ def main():
     objective, psac = MODES[args.mode]
     r = w.rank if psac else 0
     needs_queries = psac or objective == "qsac"  # QVG uses no historical Queries
-    cpu = cpu_baseline(w, args.cpu_heads, objective, r) if args.cpu_heads > 0 else None
+    cpu = None
+    if args.cpu_heads > 0:
+        # the small workloads: one head per host core (all 12 of video_chunk
+        # on a 16-core host); wm_layer's oracle step takes about a minute per
+        # head, so it keeps --cpu-heads
+        cores = args.cpu_cores or len(os.sched_getaffinity(0))
+        n_cpu = min(w.heads, cores) if w.name in ("tiny", "video_chunk") else args.cpu_heads
+        cpu = cpu_baseline(w, n_cpu, objective, r)
 
     import torch
     from video_world_model_amd import Cache

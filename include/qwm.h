@@ -247,8 +247,12 @@ qwm_status qwm_export_bytes(const qwm_cache* cache, int64_t t0, int64_t t1, size
 qwm_status qwm_export(const qwm_cache* cache, int64_t t0, int64_t t1, void* dev_buf);
 
 /* Compensated, scaled logits of n_q Queries q [heads][n_q][head_dim] against
- * every cached token of one head: logits [n_q][length] float, computed by the
- * same contraction path qwm_attend uses. */
+ * every cached token of one head: logits [n_q][length] float. They come from
+ * the general attention kernel, whose Key operand is khat split into fp16 hi
+ * and lo parts; qwm_attend on bf16 caches with head_dim 128 uses a kernel
+ * with exact fp16 operands instead (centroid, code times step, zero-point
+ * and PSAC terms). Both equal the definition up to the float32 rounding of
+ * their sums. */
 qwm_status qwm_attend_logits(qwm_cache* cache, const void* q, int64_t n_q, int32_t head,
                              float softmax_scale, float* logits);
 
@@ -259,8 +263,8 @@ qwm_status qwm_attend_logits(qwm_cache* cache, const void* q, int64_t n_q, int32
  * the cached ones and the logit is the compensated q . khat_j + (q . U_r) .
  * coef_j of qwm_attend (unscaled); with k_ref [heads][n_ref][head_dim] in the
  * cache dtype (1 <= n_ref <= 2^22) they are those full-precision Keys and the
- * logit is q . k_j. Both go through the contraction path of qwm_attend, whose
- * float32 logits decide the order. */
+ * logit is q . k_j. Both go through the general attention kernel (as
+ * qwm_attend_logits), whose float32 logits decide the order. */
 qwm_status qwm_attend_top1(qwm_cache* cache, const void* q, int64_t n_q, const void* k_ref, int64_t n_ref,
                            int32_t* top1);
 
