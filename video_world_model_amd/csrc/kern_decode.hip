@@ -67,21 +67,28 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// Eight 2-bit codes (bits 2e .. 2e+1 of w, e = 0..7) -> eight fp16 values
-// 0..3: y = w | w << 14 puts code 2p+1 beside code 2p in the high half, the
-// pair is or-ed into 1024 + c (0x6400 | c, exact) and 1024 is subtracted.
-__device__ __forceinline__ half8 codes_to_f16(uint32_t w) {
-  const uint32_t y = w | (w << 14);
-  const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  half8 r;
+// The eight 2-bit codes of one 16-bit unit (code e in bits 2e .. 2e+1),
+// spread by a byte permute so that codes 0..3 sit in byte 0 and codes 4..7
+// in byte 2 (sel 0x0C010C00 for the low unit of a word, 0x0C030C02 for the
+// high one).
+__device__ __forceinline__ uint32_t spread_unit(uint32_t word, uint32_t sel) {
+  return __builtin_amdgcn_perm(0u, word, sel);
+}
+// Spread codes -> eight fp16 values c * 2^-24 (the codes as fp16 subnormals:
+// exact, no offset to remove), in the channel order 0, 4, 1, 5, 2, 6, 3, 7.
+__device__ __forceinline__ half8 codes_to_f16_sub(uint32_t w) {
+  uint32_t d[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t x = ((y >> (4 * p)) & 0x00030003u) | 0x64006400u;
-    const half2v v = __builtin_bit_cast(half2v, x) - k1024;
-    r[2 * p] = v[0];
-    r[2 * p + 1] = v[1];
-  }
-  return r;
+  for (int p = 0; p < 4; ++p) d[p] = (w >> (2 * p)) & 0x00030003u;
+  return __builtin_bit_cast(half8, make_uint4(d[0], d[1], d[2], d[3]));
+}
+// 0x64006400 (fp16 1024, 1024) in a VGPR: with the mask in an SGPR the
+// compiler can then fuse "(x & mask) | magic" into one v_and_or_b32 (a VOP3
+// reads at most one scalar operand here).
+__device__ __forceinline__ uint32_t magic_1024_vgpr() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
 }
 
 // ---------------------------------------------------------------- q . C table
@@ -224,10 +231,13 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       float s = 0.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
+        // channels 2k and 2k+1 of the octet go to the positions of the
+        // spread code order (channel c at 2c for c < 4, at 2(c - 4) + 1)
         const float x0 = qv ? qsign * __uint_as_float(ww[k] << 16) : 0.0f;
         const float x1 = qv ? qsign * __uint_as_float(ww[k] & 0xFFFF0000u) : 0.0f;
-        qa[G][2 * k] = (_Float16)x0;
-        qa[G][2 * k + 1] = (_Float16)x1;
+        const int c0 = 2 * k, c1 = 2 * k + 1;
+        qa[G][c0 < 4 ? 2 * c0 : 2 * (c0 - 4) + 1] = (_Float16)x0;
+        qa[G][c1 < 4 ? 2 * c1 : 2 * (c1 - 4) + 1] = (_Float16)x1;
         s += x0;
         s += x1;
       }
@@ -304,34 +314,34 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
   // as code * s (exact fp16).
   auto dequant_v = [&](const uint32_t (&vc)[4], const uint32_t (&vp)[4]) {
     const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const uint32_t magic = magic_1024_vgpr();
     half2v s2[4];
-    uint32_t y[4][2];  // code 2p at bits 4p, code 2p+1 at bits 16 + 4p of each 8-code half
+    uint32_t y[4][2];  // spread 8-code halves: codes 0..3 in byte 0, codes 4..7 in byte 2
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const uint32_t sb = vp[tb] >> 16;
       s2[tb] = __builtin_bit_cast(half2v, sb | (sb << 16));
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t x = (vc[tb] >> (16 * hh)) & 0xFFFFu;
-        y[tb][hh] = x | (x << 14);
-      }
+      y[tb][0] = spread_unit(vc[tb], 0x0C010C00u);
+      y[tb][1] = spread_unit(vc[tb], 0x0C030C02u);
     }
     const int clb = 32 * (kg >> 1) + 16 * (kg & 1);  // first local channel
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      uint32_t cs[4];  // channels 2pp, 2pp + 1 of token tb
+      const int hh = pp >> 2, pq = pp & 3;
+      const int ca = 8 * hh + pq, cb = ca + 4;  // the pair's channels
+      uint32_t cs[4];  // channels ca, cb of token tb
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const uint32_t b = ((y[tb][pp >> 2] >> (4 * (pp & 3))) & 0x00030003u) | 0x64006400u;
+        const uint32_t b = ((y[tb][hh] >> (2 * pq)) & 0x00030003u) | magic;  // 1024 + code, exact
         cs[tb] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, b) - k1024) * s2[tb]);
       }
-      // channel 2pp of the four tokens, then channel 2pp + 1
+      // channel ca of the four tokens, then channel cb
       const uint32_t e01 = __builtin_amdgcn_perm(cs[1], cs[0], 0x05040100u);
       const uint32_t e23 = __builtin_amdgcn_perm(cs[3], cs[2], 0x05040100u);
       const uint32_t o01 = __builtin_amdgcn_perm(cs[1], cs[0], 0x07060302u);
       const uint32_t o23 = __builtin_amdgcn_perm(cs[3], cs[2], 0x07060302u);
-      *reinterpret_cast<uint2*>(vt + vrow_off(clb + 2 * pp) + 4 * j) = make_uint2(e01, e23);
-      *reinterpret_cast<uint2*>(vt + vrow_off(clb + 2 * pp + 1) + 4 * j) = make_uint2(o01, o23);
+      *reinterpret_cast<uint2*>(vt + vrow_off(clb + ca) + 4 * j) = make_uint2(e01, e23);
+      *reinterpret_cast<uint2*>(vt + vrow_off(clb + cb) + 4 * j) = make_uint2(o01, o23);
     }
   };
   // Zero-points of the 4 tokens (slots 4j + tb) of the lane's group into row
@@ -442,11 +452,13 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       const half8 bzp = __builtin_bit_cast(half8, make_uint4(z01, z23, z01, z23));
       floatx4 acc = mfma_f16(ax1, __builtin_bit_cast(half8, cf), floatx4{0.f, 0.f, 0.f, 0.f});
       acc = mfma_f16(ax2, bzp, acc);
-      const uint32_t cws[4] = {cw.x & 0xFFFFu, cw.x >> 16, cw.y & 0xFFFFu, cw.y >> 16};
+      const uint32_t cws[4] = {spread_unit(cw.x, 0x0C010C00u), spread_unit(cw.x, 0x0C030C02u),
+                               spread_unit(cw.y, 0x0C010C00u), spread_unit(cw.y, 0x0C030C02u)};
 #pragma unroll
       for (int G = 0; G < NG; ++G) {
-        const floatx4 dg = mfma_f16(qa[G], codes_to_f16(cws[G]), floatx4{0.f, 0.f, 0.f, 0.f});
-        const float st = half_bits_to_float(kpw[G] >> 16);
+        // q_G . (code_G * 2^-24), exact in float32; the step carries the 2^24
+        const floatx4 dg = mfma_f16(qa[G], codes_to_f16_sub(cws[G]), floatx4{0.f, 0.f, 0.f, 0.f});
+        const float st = half_bits_to_float(kpw[G] >> 16) * 16777216.0f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(st, dg[v], acc[v]);
       }
