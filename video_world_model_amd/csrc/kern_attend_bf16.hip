@@ -74,16 +74,21 @@ __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cas
 // times the step s, as fp16 pairs (channels 2p, 2p+1 in out[p]): the pair is
 // or-ed into fp16 1024 + code (exact), 1024 is subtracted (exact) and the
 // codes are multiplied by s (exact: 3 s is an fp16 value).
+// (The fp16 1024 pair comes from a VGPR: with the mask in an SGPR the
+// compiler fuses "(x & mask) | magic" into one v_and_or_b32, which reads at
+// most one scalar operand here.)
 __device__ __forceinline__ void codes_times_step(uint32_t w, uint32_t s_bits, uint32_t (&out)[8]) {
   const half2v s2 = __builtin_bit_cast(half2v, s_bits | (s_bits << 16));
   const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  uint32_t magic;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const uint32_t x = (w >> (16 * half)) & 0xFFFFu;
     const uint32_t y = x | (x << 14);  // code 2p at bits 4p, code 2p+1 at bits 16+4p
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t b = ((y >> (4 * p)) & 0x00030003u) | 0x64006400u;
+      const uint32_t b = ((y >> (4 * p)) & 0x00030003u) | magic;
       out[4 * half + p] = h2_bits((__builtin_bit_cast(half2v, b) - k1024) * s2);
     }
   }
