@@ -141,13 +141,14 @@ def _degenerate_rows(rng, n, d, dtype, C):
     return rows
 
 
-@pytest.mark.parametrize("name", ["tiny", "video_chunk"])
-def test_quantize_degenerate_groups(name):
+# bf16 at 64 Queries runs the decode kernel, at 96 the prefill kernel
+@pytest.mark.parametrize("name,n_q", [("tiny", 64), ("video_chunk", 64), ("video_chunk", 96)])
+def test_quantize_degenerate_groups(name, n_q):
     """Quantize-append and attention over Keys and Values made of degenerate
     groups: the records equal the oracle's bit for bit and the outputs stay
     within 1e-3 of its rows."""
     n = 448
-    w = small(W.workload(name), heads=1, n_kv=n, n_q=64)
+    w = small(W.workload(name), heads=1, n_kv=n, n_q=n_q)
     rng = np.random.default_rng(11)
     g = W.HeadGen(w, 0)
     C = W.round_to_bf16(g.keys(0, w.n_centroids)) if w.dtype == "bf16" else g.keys(0, w.n_centroids)
