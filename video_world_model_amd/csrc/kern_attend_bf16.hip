@@ -69,6 +69,26 @@ __device__ __forceinline__ half2v bf2_to_h2(uint32_t w) {
   return pk_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
 }
 __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+// x combined with lane l ^ 16 / l ^ 32 through the gfx950 row-swap
+// permutes (VALU; a __shfl_xor becomes an LDS-pipe ds_bpermute): after the
+// swap of a register with itself the two results hold, in every lane, the
+// lane's own value and its partner's.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {  // x + partner (addition commutes exactly)
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // The 16 codes of one 32-bit word (code c of channel c in bits 2c..2c+1)
 // times the step s, as fp16 pairs (channels 2p, 2p+1 in out[p]): the pair is
@@ -328,9 +348,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
         s += x1;
       }
       // group ks = channels 32 ks .. 32 ks + 31: the four lane groups' parts
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      gs[ks] = s;
+      gs[ks] = add_xor32(add_xor16(s));
     }
 #pragma unroll
     for (int G = 0; G < kNG; ++G) {
@@ -451,8 +469,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) mx = fmaxf(mx, S[qb][tb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       mx *= cl2;
       const bool raise = mx > mrow[qb] + 8.0f;
       if (__ballot(raise)) {  // wave-uniform: rescale every lane (alpha = 1 where unchanged)
@@ -623,9 +640,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
     for (int G = 0; G < kNG; ++G) zg[G] = __shfl(Z[qb][G], l16);
 #pragma unroll
     for (int cb = 0; cb < kD / 16; ++cb) O[qb][cb] += zg[cb >> 1];
-    float l = lrow[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    float l = add_xor32(add_xor16(lrow[qb]));
     const int64_t qi = qw0 + 16 * qb + l16;
     if (qi >= a.nq) continue;
     if (a.splits == 1) {
