@@ -266,7 +266,12 @@ __device__ __forceinline__ void load_row_span(const void* base, int64_t off, flo
 //           adjacent), and all records are written with contiguous stores.
 constexpr int kQTok = 64;
 
-template <int D, int DT, bool ASSIGN_ONLY, int OBJ>
+// PART 0: the whole kernel. For k-means passes over too few Keys to fill
+// the device twice over, the centroid scan is split: PART 1 scans one half of the centroids
+// (blockIdx.z) and writes each token's best (J, id) of that half to a.part;
+// PART 2 takes the better of the two halves (the first on equal J, so the
+// smallest id keeps a tie) and runs phases 3 and on.
+template <int D, int DT, bool ASSIGN_ONLY, int OBJ, int PART>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   constexpr int NG = D / kGroup;
   __shared__ float bj[4][kQTok];
@@ -280,17 +285,21 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   const int64_t t0 = (int64_t)blockIdx.x * kQTok;
   const int nt = (int)((a.n - t0) < kQTok ? (a.n - t0) : kQTok);
 
-  // ---- phase 1: assignment cost over this wave's candidate quarter. It runs
-  // before any barrier so that the wave-uniform candidate rows are fetched
-  // with scalar loads (a barrier would make them possibly clobbered).
-  {
+  // ---- phase 1: assignment cost over this wave's candidate quarter (of the
+  // block's range). It runs before any barrier so that the wave-uniform
+  // candidate rows are fetched with scalar loads (a barrier would make them
+  // possibly clobbered).
+  if constexpr (PART != 2) {
     float kf[D];
     load_row_span<D, DT>(a.k, ((int64_t)h * a.n + t0 + (lane < nt ? lane : 0)) * D, kf);
     float SG[NG];
 #pragma unroll
     for (int G = 0; G < NG; ++G) SG[G] = a.S[h * NG + G];
-    const int mq = (a.m + 3) / 4;
-    const int c0 = wave * mq, c1 = (c0 + mq) < a.m ? (c0 + mq) : a.m;
+    const int mh = (a.m + 1) / 2;  // PART 1: half 0 = [0, mh), half 1 = [mh, m)
+    const int rb = (PART == 1 && blockIdx.z == 1) ? mh : 0;
+    const int re = (PART == 1 && blockIdx.z == 0) ? mh : a.m;
+    const int mq = (re - rb + 3) / 4;
+    const int c0 = rb + wave * mq, c1 = (c0 + mq) < re ? (c0 + mq) : re;  // may be empty
     const float* __restrict__ Ch = a.C32 + (int64_t)h * a.m * D;
     float bestJ = __builtin_inff();
     int best = c0;
@@ -304,6 +313,21 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     bj[wave][lane] = bestJ;
     bi[wave][lane] = best;
   }
+  if constexpr (PART == 1) {
+    __syncthreads();
+    if (tid < nt) {
+      float J = bj[0][tid];
+      int id = bi[0][tid];
+#pragma unroll
+      for (int w = 1; w < 4; ++w)
+        if (bj[w][tid] < J) {
+          J = bj[w][tid];
+          id = bi[w][tid];
+        }
+      a.part[((int64_t)blockIdx.z * a.H + h) * a.n + t0 + tid] = make_uint2(__float_as_uint(J), (uint32_t)id);
+    }
+    return;
+  }
   if constexpr (!ASSIGN_ONLY) {
     const double* Uh = a.U64 + (int64_t)h * D * a.r;
     for (int i = tid; i < D * kRankPad; i += 256) {
@@ -313,17 +337,26 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 2: combine the quarters in candidate order
+  // ---- phase 2: combine the quarters (or the halves) in candidate order
   auto combined = [&](int t) {
-    float J = bj[0][t];
-    int id = bi[0][t];
+    if constexpr (PART == 2) {
+      // the scan wrote tokens below nt only: padding lanes of the last block
+      // take the block's first token (their results are never stored)
+      const int tc = t < nt ? t : 0;
+      const uint2 p0 = a.part[(int64_t)h * a.n + t0 + tc];
+      const uint2 p1 = a.part[((int64_t)a.H + h) * a.n + t0 + tc];
+      return (int)((__uint_as_float(p1.x) < __uint_as_float(p0.x)) ? p1.y : p0.y);
+    } else {
+      float J = bj[0][t];
+      int id = bi[0][t];
 #pragma unroll
-    for (int w = 1; w < 4; ++w)
-      if (bj[w][t] < J) {
-        J = bj[w][t];
-        id = bi[w][t];
-      }
-    return id;
+      for (int w = 1; w < 4; ++w)
+        if (bj[w][t] < J) {
+          J = bj[w][t];
+          id = bi[w][t];
+        }
+      return id;
+    }
   };
   if constexpr (ASSIGN_ONLY) {
     if (tid < nt) a.ids_out[(int64_t)h * a.n + t0 + tid] = (uint8_t)combined(tid);
@@ -832,13 +865,22 @@ __global__ void shadow_kernel(const void* C, const float* U, int64_t nC, int64_t
 hipError_t launch_quantize(int D, int dtype, const QuantArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   dim3 grid((unsigned)((a.n + kQTok - 1) / kQTok), (unsigned)a.H);
+  dim3 grid2(grid.x, grid.y, 2);
   dim3 block(256);
   const bool assign = (a.v == nullptr);
-#define QWM_QLAUNCH(DD, TT, OO)                                                   \
-  if (assign)                                                                     \
-    hipLaunchKernelGGL((quantize_kernel<DD, TT, true, OO>), grid, block, 0, s, a); \
-  else                                                                            \
-    hipLaunchKernelGGL((quantize_kernel<DD, TT, false, OO>), grid, block, 0, s, a);
+  if (a.part != nullptr && a.n > kQuantSplitMaxTokens) return hipErrorInvalidValue;
+#define QWM_QLAUNCH(DD, TT, OO)                                                                \
+  if (a.part != nullptr) {                                                                     \
+    hipLaunchKernelGGL((quantize_kernel<DD, TT, true, OO, 1>), grid2, block, 0, s, a);         \
+    if (assign)                                                                                \
+      hipLaunchKernelGGL((quantize_kernel<DD, TT, true, OO, 2>), grid, block, 0, s, a);        \
+    else                                                                                       \
+      hipLaunchKernelGGL((quantize_kernel<DD, TT, false, OO, 2>), grid, block, 0, s, a);       \
+  } else if (assign) {                                                                         \
+    hipLaunchKernelGGL((quantize_kernel<DD, TT, true, OO, 0>), grid, block, 0, s, a);          \
+  } else {                                                                                     \
+    hipLaunchKernelGGL((quantize_kernel<DD, TT, false, OO, 0>), grid, block, 0, s, a);         \
+  }
 #define QWM_QOBJ(DD, TT)                  \
   if (a.obj == kObjNearest) {             \
     QWM_QLAUNCH(DD, TT, kObjNearest)      \

@@ -52,7 +52,12 @@ struct QuantArgs {
   uint8_t* ids_out;        // assignment-only output [H][n] (k-means)
   int H, m, r;
   int obj;                 // kObjQsac, kObjNearest or kObjPostq
+  uint2* part;             // not null: split centroid scan, [2][H][n] best (J bits, id) per half
+                           // (used by the assignment-only passes of the k-means)
 };
+// Split scans need n <= kQuantSplitMaxTokens (the size of their buffer).
+constexpr int64_t kQuantSplitMaxTokens = 4096;
+constexpr int kQuantBlocksPerCU = 3;  // resident 4-wave quantize workgroups per CU (166 VGPRs)
 hipError_t launch_quantize(int D, int dtype, const QuantArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- k-means
