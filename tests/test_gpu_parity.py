@@ -444,3 +444,60 @@ def test_build_small_and_ragged(name, heads, n_keys, iters):
             jg = O.mean_objective(keys[h], C[h], So, w.group)
             jo = O.mean_objective(keys[h], Co, So, w.group)
             assert abs(jg - jo) <= 0.01 * max(jo, 1e-30)
+
+
+# The most epochs a cache holds (64), most of them shorter than one 64-token
+# tile: the prefill kernel's tile ring and segment cursor step through
+# segments of 1 to 100 tokens, the q.U and q.C tables span 64 epochs, and with
+# a self segment the plan holds its most segments (65).
+@pytest.mark.parametrize("n_q,mask", [(16, "none"), (96, "none"), (48, "full")])
+def test_max_epochs_short_segments(n_q, mask):
+    from video_world_model_amd import Cache
+    w = small(W.workload("video_chunk"), heads=2, n_centroids=16, rank=8)
+    rng = np.random.default_rng(64)
+    lens = [int(x) for x in rng.integers(1, 101, size=64)]
+    lens[5] = 64  # one epoch of exactly one tile
+    total = sum(lens)
+    log(f"[64 epochs] total {total} tokens, n_q={n_q}, mask={mask}")
+    gens = [W.HeadGen(w, h, 3) for h in range(2)]
+    keys = [g.keys(0, total + n_q) for g in gens]
+    vals = [g.values(0, total + n_q) for g in gens]
+    cache = Cache(2, w.head_dim, w.n_centroids, w.rank, total, dtype=torch.bfloat16, max_epochs=64,
+                  max_query_tokens=max(n_q, 16), max_build_tokens=64)
+    hcs = [O.HeadCache(w.group, w.dtype) for _ in range(2)]
+    t = 0
+    for e, n in enumerate(lens):
+        cals = []
+        for h in range(2):
+            qh = gens[h].hist_queries(e % 8)
+            S = O.sensitivity(qh, w.group)
+            U = O.subspace(qh, w.rank)
+            C = O.init_centroids(keys[h][t:t + max(n, w.n_centroids)], w.n_centroids)
+            cals.append((C, S, U))
+            hcs[h].add_epoch(C, S, U)
+        import_calibration(cache, cals, w.dtype)
+        cache.quantize_append(to_dev([k[t:t + n] for k in keys], w.dtype), to_dev([v[t:t + n] for v in vals], w.dtype))
+        for h in range(2):
+            hcs[h].append(keys[h][t:t + n], vals[h][t:t + n])
+        t += n
+    assert cache.epochs() == 64 and cache.length() == total
+    dec = cache.decode_export(cache.export().cpu().numpy(), total)
+    for h in range(2):
+        for start, rec in hcs[h].records:
+            compare_records(dec, h, rec, start)
+        assert np.array_equal(dec["epoch"][h], hcs[h].field("epoch"))
+    q = [g.current_queries()[:n_q] for g in gens]
+    if mask == "none":
+        out = cache.attend(to_dev(q, w.dtype)).cpu().numpy()
+        ks = vs = [None, None]
+    else:
+        ks = [k[total:total + n_q] for k in keys]
+        vs = [v[total:total + n_q] for v in vals]
+        out = cache.attend(to_dev(q, w.dtype), to_dev(ks, w.dtype), to_dev(vs, w.dtype), mask=mask).cpu().numpy()
+    worst = 0.0
+    for h in range(2):
+        ref = O.attend(q[h], hcs[h], ks[h], vs[h], mask=mask)
+        e = row_rel_err(out[h], ref)
+        worst = max(worst, float(e.max()))
+        assert e.max() <= ROW_TOL
+    log(f"  64 epochs: records bit-exact, worst row error {worst:.3e}")
