@@ -179,7 +179,9 @@ qwm_status qwm_build_centroids(qwm_cache* cache, const void* keys, int64_t n_key
  *   coef = U_r^T (k - (c_id + reconstructed residual)), float64, rounded once
  *   to fp16 (PSAC, "Step 2"); none at rank 0.
  * The records go to positions length .. length + n_tokens - 1 and the length
- * advances. Bit-identical whether tokens arrive in one call or several. */
+ * advances. Bit-identical whether tokens arrive in one call or several.
+ * n_tokens = 0 does nothing after the state check and reads nothing: k and
+ * v may then be NULL. */
 qwm_status qwm_quantize_append(qwm_cache* cache, const void* k, const void* v, int64_t n_tokens);
 
 /* Attention of n_q Queries q [heads][n_q][head_dim] over every cached token

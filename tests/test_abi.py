@@ -154,6 +154,7 @@ def test_call_order_and_argument_checks():
     assert L.qwm_build_subspace(h, ctypes.c_void_p(4096 + 2), 10) == Q.QWM_ERR_INVALID_ARG  # misaligned
     assert L.qwm_build_subspace(h, P, 0) == Q.QWM_ERR_INVALID_ARG
     assert L.qwm_quantize_append(h, P, None, 10) == Q.QWM_ERR_INVALID_ARG
+    assert L.qwm_quantize_append(h, None, None, 0) == Q.QWM_ERR_STATE  # the state is checked first
     assert L.qwm_quantize_append(h, P, P, -1) == Q.QWM_ERR_INVALID_ARG
     assert L.qwm_attend(h, P, 65, None, None, 0, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_CAPACITY
     assert L.qwm_attend(h, P, 0, None, None, 0, 0, ctypes.c_float(0.1), out) == Q.QWM_ERR_INVALID_ARG

@@ -501,3 +501,37 @@ def test_max_epochs_short_segments(n_q, mask):
         worst = max(worst, float(e.max()))
         assert e.max() <= ROW_TOL
     log(f"  64 epochs: records bit-exact, worst row error {worst:.3e}")
+
+
+# Empty inputs: an append of no tokens changes nothing, and a chunk attends to
+# its own Keys alone while the cache holds no token yet (the plan's one
+# segment is the self segment), with both self masks and on both kernels'
+# dtypes.
+@pytest.mark.parametrize("name,mask", [("video_chunk", "full"), ("video_chunk", "causal"), ("tiny", "causal")])
+def test_empty_append_and_self_only(name, mask):
+    n_q = 70
+    w = small(W.workload(name), heads=2, n_q=n_q, n_self=n_q)
+    log(f"[empty] {name} mask={mask}")
+    g0 = [W.HeadGen(w, h) for h in range(2)]
+    cals = [oracle_calibration(w, g, g.keys(0, 256), g.hist_queries(), 1) for g in g0]
+    cache = _cache(w, capacity=512, max_q=n_q)
+    import_calibration(cache, cals, w.dtype)
+    empty = to_dev([g.keys(0, 1)[:0] for g in g0], w.dtype)
+    cache.quantize_append(empty, empty)
+    assert cache.length() == 0
+    q = [g.current_queries()[:n_q] for g in g0]
+    ks = [g.keys(300, 300 + n_q) for g in g0]
+    vs = [g.values(300, 300 + n_q) for g in g0]
+    out = cache.attend(to_dev(q, w.dtype), to_dev(ks, w.dtype), to_dev(vs, w.dtype), mask=mask).cpu().numpy()
+    for h in range(2):
+        hc = O.HeadCache(w.group, w.dtype)
+        hc.add_epoch(*cals[h])
+        ref = O.attend(q[h], hc, ks[h], vs[h], mask=mask)
+        assert row_rel_err(out[h], ref).max() <= ROW_TOL
+    # then tokens, an empty append between two real ones: identical bytes
+    keys = [g.keys(0, 200) for g in g0]
+    vals = [g.values(0, 200) for g in g0]
+    cache.quantize_append(to_dev([k[:120] for k in keys], w.dtype), to_dev([v[:120] for v in vals], w.dtype))
+    before = cache.export().cpu().numpy()
+    cache.quantize_append(empty, empty)
+    assert cache.length() == 120 and np.array_equal(cache.export().cpu().numpy(), before)

@@ -839,8 +839,10 @@ qwm_status qwm_export_calibration(const qwm_cache* cc, int32_t epoch, void* C, f
 qwm_status qwm_quantize_append(qwm_cache* c, const void* k, const void* v, int64_t n_tokens) {
   qwm_status st;
   if ((st = check_cache(c)) != QWM_OK) return st;
-  if ((st = check_ptr(k, "k")) != QWM_OK) return st;
-  if ((st = check_ptr(v, "v")) != QWM_OK) return st;
+  if (n_tokens != 0) {  // with no tokens nothing is read: k and v may be NULL
+    if ((st = check_ptr(k, "k")) != QWM_OK) return st;
+    if ((st = check_ptr(v, "v")) != QWM_OK) return st;
+  }
   if (n_tokens < 0) return fail(QWM_ERR_INVALID_ARG, "n_tokens must be >= 0");
   if (c->epoch_start.empty()) return fail(QWM_ERR_STATE, "quantize_append before a committed epoch");
   if (c->length + n_tokens > c->desc.capacity_tokens) return fail(QWM_ERR_CAPACITY, "capacity exceeded");
