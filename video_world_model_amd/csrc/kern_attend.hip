@@ -1,4 +1,6 @@
-// Attention over the 2-bit QuantWM cache with PSAC logit compensation (gfx950).
+// Attention over the 2-bit QuantWM cache with PSAC logit compensation (gfx950):
+// the general kernel (float32 caches, head_dim 64, and the logits and top-1
+// modes); bf16 caches with head_dim 128 attend through kern_attend_bf16.hip.
 //
 // Method (QuantWM; fugumt.com abstract: PSAC puts the Key error left after
 // quantization back along the dominant Query subspace so the attention logits

@@ -164,7 +164,7 @@ template <int NQ>
 __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const AttnPlan p) {
   static_assert(NQ == 16, "one 16-Query block per wave");
   constexpr int D = 128, NG = 4;
-  // vhat^T of one 64-channel pass, fp16 hi and lo planes: [channel][token
+  // (code * s)^T of one 64-channel pass, one fp16 plane: [channel][token
   // slot], rows of 72 halves (16-byte aligned; 16 consecutive rows hit
   // distinct banks), every 16-channel block skewed by 64 bytes so the four
   // blocks written together hit different banks.
@@ -308,8 +308,6 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       dst[tb] = floatx4{x.x, x.y, x.z, x.w};
     }
   };
-  // Values of one channel pass: 16 channels of 4 tokens -> hi and lo planes,
-  // token slot 4j + tb (hi = fp16(zp + code * step), lo = fp16(rest))
   // Values of one channel pass: 16 channels of 4 tokens (slots 4j + tb)
   // as code * s (exact fp16).
   auto dequant_v = [&](const uint32_t (&vc)[4], const uint32_t (&vp)[4]) {

@@ -400,8 +400,8 @@ int queries_per_block(int64_t n_q) {
 
 // Split the KV tiles so that the workgroups fill the device in as few
 // rounds as possible: cost = rounds x (tiles per workgroup + 2 for its
-// prologue and epilogue) + 2 for the merge pass when split; one 145 KB-LDS
-// workgroup per CU for head_dim 128.
+// prologue and epilogue) + 2 for the merge pass when split; one workgroup
+// per CU for head_dim 128 (their LDS stages take most of the CU's 160 KB).
 int choose_splits(const qwm_cache* c, int64_t n_q, int T, int64_t part_rows) {
   const int64_t qtiles = (n_q + qwm::kTileQ - 1) / qwm::kTileQ;
   const int64_t slots = (int64_t)c->ncu * (c->D == 128 ? 1 : 2);
