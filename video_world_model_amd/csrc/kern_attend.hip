@@ -796,7 +796,7 @@ __global__ __launch_bounds__(kMergeRowThreads) void merge_rows_kernel(const Attn
 }
 
 // q . U_r for every epoch slot: qU[h][e][i][k] (k < 16, zero for k >= r).
-// One wave per 16 Queries of one head, all epoch slots: D[Query][rank] =
+// One wave per 16 Queries of one head and one epoch slot: D[Query][rank] =
 // q U by v_mfma_f32_16x16x32_f16 with the Query fragments in fp16 (bf16
 // inputs are exact; float32 inputs add a lo part) and U as fp16 hi + lo
 // (products exact, float32 sums).
@@ -822,7 +822,10 @@ __global__ __launch_bounds__(64) void qu_kernel(const void* q, int64_t nq, int r
       }
   }
   const bool rv = l16 < r;
-  for (int ep = 0; ep < E; ++ep) {
+  {
+    // one epoch slot per workgroup (blockIdx.z): the slots' U loads and MFMA
+    // chains run side by side instead of one after another
+    const int ep = blockIdx.z;
     // B: U column l16 (rank), channels 32ks + 8g .. +7; ranks past r are zero
     const float* U = Ubase + (int64_t)ep * ustride + (int64_t)h * D * r;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -853,7 +856,8 @@ __global__ __launch_bounds__(64) void qu_kernel(const void* q, int64_t nq, int r
 
 hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, const float* Ubase,
                      int64_t ustride, int E, float* qU, hipStream_t s) {
-  dim3 grid((unsigned)((nq + 15) / 16), (unsigned)H), block(64);
+  if (E < 1) return hipSuccess;
+  dim3 grid((unsigned)((nq + 15) / 16), (unsigned)H, (unsigned)E), block(64);
   if (D == 128 && dtype == 0)
     hipLaunchKernelGGL((qu_kernel<128, 0>), grid, block, 0, s, q, nq, r, Ubase, ustride, E, qU);
   else if (D == 128)
