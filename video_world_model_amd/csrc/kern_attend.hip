@@ -796,7 +796,7 @@ __global__ __launch_bounds__(kMergeRowThreads) void merge_rows_kernel(const Attn
 }
 
 // q . U_r for every epoch slot: qU[h][e][i][k] (k < 16, zero for k >= r).
-// One wave per 16 Queries of one head and one epoch slot: D[Query][rank] =
+// One wave per 64 Queries of one head and one epoch slot: D[Query][rank] =
 // q U by v_mfma_f32_16x16x32_f16 with the Query fragments in fp16 (bf16
 // inputs are exact; float32 inputs add a lo part) and U as fp16 hi + lo
 // (products exact, float32 sums).
@@ -804,50 +804,67 @@ template <int D, int DT>
 __global__ __launch_bounds__(64) void qu_kernel(const void* q, int64_t nq, int r, const float* Ubase,
                                                 int64_t ustride, int E, float* qU) {
   constexpr int KS = D / 32;
+  constexpr int QB = 4;  // 16-Query blocks per wave: the U fragments are loaded once for all of them
   const int lane = threadIdx.x, g = lane >> 4, l16 = lane & 15;
   const int h = blockIdx.y;
-  const int64_t q0 = (int64_t)blockIdx.x * 16;
-  // A: Query q0 + l16, channels 32ks + 8g .. +7
-  half8 qa[KS], qb[KS];
-  {
-    const int64_t qi = q0 + l16 < nq ? q0 + l16 : nq - 1;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = load_in<DT>(q, ((int64_t)h * nq + qi) * D + 32 * ks + 8 * g + e);
-        const _Float16 hi = (_Float16)x;
-        qa[ks][e] = hi;
-        qb[ks][e] = (_Float16)(x - (float)hi);
-      }
-  }
+  // one epoch slot per workgroup (blockIdx.z): the slots' U loads and MFMA
+  // chains run side by side instead of one after another
+  const int ep = blockIdx.z;
+  // B: U column l16 (rank), channels 32ks + 8g .. +7, as fp16 hi + lo;
+  // ranks past r are zero
   const bool rv = l16 < r;
-  {
-    // one epoch slot per workgroup (blockIdx.z): the slots' U loads and MFMA
-    // chains run side by side instead of one after another
-    const int ep = blockIdx.z;
-    // B: U column l16 (rank), channels 32ks + 8g .. +7; ranks past r are zero
-    const float* U = Ubase + (int64_t)ep * ustride + (int64_t)h * D * r;
+  const float* U = Ubase + (int64_t)ep * ustride + (int64_t)h * D * r;
+  half8 uh[KS], ul[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = rv ? U[(32 * ks + 8 * g + e) * r + l16] : 0.0f;
+      const _Float16 hi = (_Float16)x;
+      uh[ks][e] = hi;
+      ul[ks][e] = (_Float16)(x - (float)hi);
+    }
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t q0 = ((int64_t)blockIdx.x * QB + qb) * 16;
+    if (q0 >= nq) break;  // wave-uniform
+    // A: Query q0 + l16, channels 32ks + 8g .. +7, in one 16-byte load per
+    // step (two for float32)
+    const int64_t qi = q0 + l16 < nq ? q0 + l16 : nq - 1;
+    const int64_t row = ((int64_t)h * nq + qi) * D;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      half8 uh, ul;
+      float x[8];
+      if constexpr (DT == 0) {
+        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + row + 32 * ks + 8 * g);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = __uint_as_float(ww[k] << 16);
+          x[2 * k + 1] = __uint_as_float(ww[k] & 0xFFFF0000u);
+        }
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + row + 32 * ks + 8 * g);
+        const float4 a0 = src[0], a1 = src[1];
+        x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+        x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+      }
+      half8 qa, qlo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = rv ? U[(32 * ks + 8 * g + e) * r + l16] : 0.0f;
-        const _Float16 hi = (_Float16)x;
-        uh[e] = hi;
-        ul[e] = (_Float16)(x - (float)hi);
+        const _Float16 hi = (_Float16)x[e];
+        qa[e] = hi;
+        qlo[e] = (_Float16)(x[e] - (float)hi);
       }
-      acc = mfma16(qa[ks], uh, acc);
-      acc = mfma16(qa[ks], ul, acc);
-      if constexpr (DT == 1) acc = mfma16(qb[ks], uh, acc);
+      acc = mfma16(qa, uh[ks], acc);
+      acc = mfma16(qa, ul[ks], acc);
+      if constexpr (DT == 1) acc = mfma16(qlo, uh[ks], acc);
     }
     // D[Query 4g + v][rank l16]
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t qi = q0 + 4 * g + v;
-      if (qi < nq) qU[(((int64_t)h * E + ep) * nq + qi) * kRankPad + l16] = acc[v];
+      const int64_t qo = q0 + 4 * g + v;
+      if (qo < nq) qU[(((int64_t)h * E + ep) * nq + qo) * kRankPad + l16] = acc[v];
     }
   }
 }
@@ -857,7 +874,7 @@ __global__ __launch_bounds__(64) void qu_kernel(const void* q, int64_t nq, int r
 hipError_t launch_qu(int D, int dtype, const void* q, int64_t nq, int H, int r, const float* Ubase,
                      int64_t ustride, int E, float* qU, hipStream_t s) {
   if (E < 1) return hipSuccess;
-  dim3 grid((unsigned)((nq + 15) / 16), (unsigned)H, (unsigned)E), block(64);
+  dim3 grid((unsigned)((nq + 63) / 64), (unsigned)H, (unsigned)E), block(64);
   if (D == 128 && dtype == 0)
     hipLaunchKernelGGL((qu_kernel<128, 0>), grid, block, 0, s, q, nq, r, Ubase, ustride, E, qU);
   else if (D == 128)
