@@ -30,7 +30,8 @@
 //    one split of the KV tiles (64 tokens, never crossing an epoch or the
 //    cache/self boundary);
 //  * the tile's K operands ([c | code*s | coef, zp]) and V^T operands are
-//    built ONCE per workgroup in LDS (thread = one token x 16 channels);
+//    built ONCE per workgroup in LDS (thread = one token x 16 channels of K,
+//    two tokens x 8 channels of V^T);
 //  * two wave groups in opposite phase: each SIMD holds one wave of waves
 //    0-3 and one of waves 4-7. In step i the first group runs the softmax
 //    and P . V of tile i, builds its share of the next stages and then the
@@ -72,14 +73,16 @@ __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cas
 // x combined with lane l ^ 16 / l ^ 32 through the gfx950 row-swap
 // permutes (VALU; a __shfl_xor becomes an LDS-pipe ds_bpermute): after the
 // swap of a register with itself the two results hold, in every lane, the
-// lane's own value and its partner's.
+// lane's own value and its partner's. The larger of the two is the median
+// of (a, b, +inf): one v_med3_f32, where fmaxf would first quiet both
+// inputs (logits are never NaN).
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __builtin_inff());
 }
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __builtin_inff());
 }
 __device__ __forceinline__ float add_xor16(float x) {  // x + partner (addition commutes exactly)
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -139,15 +142,30 @@ struct RawK {
   uint4 c0, c1, cf;
   uint32_t code, prm;
 };
-// ... and for the V^T operands: code and parameter words, and the self Value
-// slice (SELF kernels only).
+// ... and for the V^T operands, where a thread takes two neighbouring tokens
+// (2 p and 2 p + 1, p = lane mod 32) and 8 channels (16 kq + 8 hh .. +7,
+// hh = lane / 32): both tokens' code and parameter words, and their self
+// Value slices (SELF kernels only).
 struct RawV {
-  uint32_t code, prm;
+  uint32_t code0, code1, prm0, prm1;
   uint4 s0, s1;
 };
 
+// The centroid tables of epoch slots 0 .. n - 1 (n * H * m rows of 128 bf16)
+// as fp16, rounded to nearest even: read by the tile loads of the kernel
+// below, so that no workgroup converts a centroid row per tile.
+__global__ __launch_bounds__(256) void c16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const uint4 w = src[i];
+    dst[i] = make_uint4(h2_bits(bf2_to_h2(w.x)), h2_bits(bf2_to_h2(w.y)), h2_bits(bf2_to_h2(w.z)),
+                        h2_bits(bf2_to_h2(w.w)));
+  }
+}
+
 // SELF: the plan may hold a self segment (full-precision K/V of the chunk).
-template <bool SELF>
+// C16: the centroid rows come from the fp16 copy (a.C16) instead of the bf16
+// tables.
+template <bool SELF, bool C16>
 __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArgs a, const AttnPlan p) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[kKStages * kKSt + kVStages * kVSt];
 
@@ -192,7 +210,8 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
   const uint16_t* coef_h = a.cache.coef + (size_t)h * a.cache.capP * a.r;
   const uint16_t* kself_h = reinterpret_cast<const uint16_t*>(a.kself) + (size_t)h * a.nself * kD;
   const uint16_t* vself_h = reinterpret_cast<const uint16_t*>(a.vself) + (size_t)h * a.nself * kD;
-  const char* C_h = reinterpret_cast<const char*>(a.Cbase) + (size_t)h * a.m * kD * 2;
+  // centroid rows: 128 halves (bf16, or fp16 in the copy), same layout
+  const char* C_h = reinterpret_cast<const char*>(C16 ? a.C16 : a.Cbase) + (size_t)h * a.m * kD * 2;
 
   // rows of the stages that never change: the zero rows 132..143 of each V
   // stage
@@ -208,10 +227,18 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
   // written on another path.
   auto load_id = [&](const TileInfo& ti) -> uint32_t {
     const int t = lane < ti.tcount ? lane : ti.tcount - 1;
-    return ids_h[ti.ep >= 0 ? (uint32_t)(ti.tstart + t) : 0u];
+    return ids_h[(!SELF || ti.ep >= 0) ? (uint32_t)(ti.tstart + t) : 0u];
   };
+  // coefficient halves 8 kq .. 8 kq + 7 that lie below r (waves 0 and 1),
+  // as masks of the four words: wave-uniform, computed once
+  uint32_t cfm[4];
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const int j = 8 * kq + 2 * s2;
+    cfm[s2] = (kq < 2 && j < a.r) ? (j + 1 < a.r ? 0xFFFFFFFFu : 0xFFFFu) : 0u;
+  }
   auto load_k = [&](RawK& r, const TileInfo& ti, uint32_t id) {
-    const bool cache = ti.ep >= 0;
+    const bool cache = !SELF || ti.ep >= 0;
     const uint32_t slot = (uint32_t)(ti.tstart + (lane < ti.tcount ? lane : ti.tcount - 1));
     const uint32_t cs = cache ? slot : 0u;
     const uint4* src =
@@ -240,16 +267,21 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
     }
   };
   auto load_v = [&](RawV& r, const TileInfo& ti) {
-    const bool cache = ti.ep >= 0;
-    const uint32_t slot = (uint32_t)(ti.tstart + (lane < ti.tcount ? lane : ti.tcount - 1));
-    const uint32_t cs = cache ? slot : 0u;
-    r.code = *reinterpret_cast<const uint32_t*>(vcode_h + cs * (kD / 4) + 4 * kq);
-    r.prm = vparam_h[cs * kNG + (kq >> 1)];
+    const bool cache = !SELF || ti.ep >= 0;
+    const int j0 = 2 * (lane & 31);
+    const uint32_t slot0 = (uint32_t)(ti.tstart + (j0 < ti.tcount ? j0 : ti.tcount - 1));
+    const uint32_t slot1 = (uint32_t)(ti.tstart + (j0 + 1 < ti.tcount ? j0 + 1 : ti.tcount - 1));
+    const uint32_t cs0 = cache ? slot0 : 0u, cs1 = cache ? slot1 : 0u;
+    r.code0 = *reinterpret_cast<const uint32_t*>(vcode_h + cs0 * (kD / 4) + 4 * kq);
+    r.code1 = *reinterpret_cast<const uint32_t*>(vcode_h + cs1 * (kD / 4) + 4 * kq);
+    r.prm0 = vparam_h[cs0 * kNG + (kq >> 1)];
+    r.prm1 = vparam_h[cs1 * kNG + (kq >> 1)];
     if constexpr (SELF) {
-      const uint4* src = cache ? reinterpret_cast<const uint4*>(vcode_h)
-                               : reinterpret_cast<const uint4*>(vself_h + (size_t)slot * kD + 16 * kq);
-      r.s0 = src[0];
-      r.s1 = src[1];
+      const int ch = 16 * kq + 8 * (lane >> 5);
+      r.s0 = cache ? *reinterpret_cast<const uint4*>(vcode_h)
+                   : *reinterpret_cast<const uint4*>(vself_h + (size_t)slot0 * kD + ch);
+      r.s1 = cache ? *reinterpret_cast<const uint4*>(vcode_h)
+                   : *reinterpret_cast<const uint4*>(vself_h + (size_t)slot1 * kD + ch);
     }
   };
   // K stage row of the thread's token: c (or the self Key), code * s, and
@@ -257,12 +289,12 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
   // from wave 0, the group's zero-point from the even waves); self tokens
   // have zero code, step, zero-point and coefficients.
   auto store_k = [&](const RawK& r, const TileInfo& ti, _Float16* Ks) {
-    const bool cache = ti.ep >= 0;
+    const bool cache = !SELF || ti.ep >= 0;
     _Float16* row = Ks + lane * kKRow;
     const uint32_t cw[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
     uint32_t ch[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ch[i] = h2_bits(bf2_to_h2(cw[i]));
+    for (int i = 0; i < 8; ++i) ch[i] = (C16 && cache) ? cw[i] : h2_bits(bf2_to_h2(cw[i]));
     *reinterpret_cast<uint4*>(row + 16 * kq) = make_uint4(ch[0], ch[1], ch[2], ch[3]);
     *reinterpret_cast<uint4*>(row + 16 * kq + 8) = make_uint4(ch[4], ch[5], ch[6], ch[7]);
     const uint32_t prm = cache ? r.prm : 0u;
@@ -276,12 +308,8 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
       row[kXOff + 20 + (kq >> 1)] = zp;
     }
     if (kq < 2) {
-      uint4 cfw = r.cf;
-      const int j0 = 8 * kq;  // halves j0 .. j0+7; keep those below r
-      cfw.x = (cache && j0 + 0 < a.r) ? (j0 + 1 < a.r ? cfw.x : cfw.x & 0xFFFFu) : 0u;
-      cfw.y = (cache && j0 + 2 < a.r) ? (j0 + 3 < a.r ? cfw.y : cfw.y & 0xFFFFu) : 0u;
-      cfw.z = (cache && j0 + 4 < a.r) ? (j0 + 5 < a.r ? cfw.z : cfw.z & 0xFFFFu) : 0u;
-      cfw.w = (cache && j0 + 6 < a.r) ? (j0 + 7 < a.r ? cfw.w : cfw.w & 0xFFFFu) : 0u;
+      uint4 cfw = make_uint4(r.cf.x & cfm[0], r.cf.y & cfm[1], r.cf.z & cfm[2], r.cf.w & cfm[3]);
+      if (!cache) cfw = make_uint4(0u, 0u, 0u, 0u);
       *reinterpret_cast<uint4*>(row + kXOff + 8 * kq) = cfw;
       if (kq == 0) *reinterpret_cast<uint4*>(row + kXOff + 24) = cfw;  // coef 0..7 again, against q U lo
     }
@@ -290,35 +318,46 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
   // the group's zero-point row 128 + kq / 2. Token j of the tile goes to
   // column 32 (j / 32) + 8 gg + 4 b + u (b = bit 4, gg = bits 2-3, u = bits
   // 0-1 of j): the order in which lane group gg holds the tokens of a
-  // 32-token step in its P fragment.
+  // 32-token step in its P fragment. Tokens 2p and 2p + 1 land in
+  // neighbouring columns, so the thread writes one dword per channel: the
+  // two tokens' codes of a channel are gathered into one word (token 2p in
+  // bits 0-1, 2p + 1 in bits 16-17) and turned into an fp16 pair at once.
+  // The two half-waves write rows 8 apart (the same banks) in separate
+  // cycles.
   auto store_v = [&](const RawV& r, const TileInfo& ti, _Float16* Vs) {
-    const bool cache = ti.ep >= 0;
-    const int col = (lane & ~31) + 8 * ((lane >> 2) & 3) + 4 * ((lane >> 4) & 1) + (lane & 3);
+    const bool cache = !SELF || ti.ep >= 0;
+    const int hh = lane >> 5, j0 = 2 * (lane & 31);
+    const int col = (j0 & ~31) + 8 * ((j0 >> 2) & 3) + 4 * ((j0 >> 4) & 1) + (j0 & 3);
     uint32_t v[8];
-    const uint32_t prm = cache ? r.prm : 0u;
     if (!SELF || cache) {
-      codes_times_step(r.code, prm >> 16, v);
+      // both tokens' codes of channels 8 hh .. 8 hh + 7: channel c in bits
+      // 2c (token 2p) and 16 + 2c (token 2p + 1)
+      const uint32_t z = __builtin_amdgcn_perm(r.code1, r.code0, hh ? 0x07060302u : 0x05040100u);
+      const half2v s2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(r.prm1, r.prm0, 0x07060302u));
+      const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+      uint32_t magic;
+      asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t b = ((z >> (2 * c)) & 0x00030003u) | magic;
+        v[c] = h2_bits((__builtin_bit_cast(half2v, b) - k1024) * s2);
+      }
     } else {
-      const uint32_t sw[8] = {r.s0.x, r.s0.y, r.s0.z, r.s0.w, r.s1.x, r.s1.y, r.s1.z, r.s1.w};
+      // self Values: channel 2i / 2i + 1 in the low / high half of word i
+      const uint32_t a[4] = {r.s0.x, r.s0.y, r.s0.z, r.s0.w};
+      const uint32_t b[4] = {r.s1.x, r.s1.y, r.s1.z, r.s1.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = h2_bits(bf2_to_h2(sw[i]));
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = h2_bits(pk_f16(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16)));
+        v[2 * i + 1] = h2_bits(pk_f16(__uint_as_float(a[i] & 0xFFFF0000u), __uint_as_float(b[i] & 0xFFFF0000u)));
+      }
     }
-    // Lanes 2j and 2j+1 hold neighbouring columns: after swapping the pairs
-    // with the neighbour lane, the even lane writes channel 2i of both tokens
-    // and the odd lane channel 2i+1, one dword each (no two lanes of a store
-    // share a dword).
-    const bool odd = (lane & 1) != 0;
-    uint32_t* base = reinterpret_cast<uint32_t*>(Vs + (16 * kq + (odd ? 1 : 0)) * kVRow + (col & ~1));
+    uint32_t* base = reinterpret_cast<uint32_t*>(Vs + (16 * kq + 8 * hh) * kVRow + col);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[i], kDppQuadSwap1, 0xF, 0xF, false);
-      const uint32_t w = odd ? __builtin_amdgcn_perm(v[i], other, 0x07060302u) : __builtin_amdgcn_perm(other, v[i], 0x05040100u);
-      base[(2 * i) * (kVRow / 2)] = w;
-    }
-    if ((kq & 1) == 0) {
-      const uint32_t z = prm & 0xFFFFu;
-      const uint32_t zo = (uint32_t)__builtin_amdgcn_mov_dpp((int)z, kDppQuadSwap1, 0xF, 0xF, false);
-      if (!odd) *reinterpret_cast<uint32_t*>(Vs + (128 + (kq >> 1)) * kVRow + col) = z | (zo << 16);
+    for (int c = 0; c < 8; ++c) base[c * (kVRow / 2)] = v[c];
+    if ((kq & 1) == 0 && hh == 0) {
+      const uint32_t z = cache ? __builtin_amdgcn_perm(r.prm1, r.prm0, 0x05040100u) : 0u;
+      *reinterpret_cast<uint32_t*>(Vs + (128 + (kq >> 1)) * kVRow + col) = z;
     }
   };
 
@@ -672,11 +711,25 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
 hipError_t launch_attend_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const int64_t nwg = (a.nq + a.qpb - 1) / a.qpb * a.splits * a.H;
   if (nwg <= 0 || nwg > INT32_MAX) return hipErrorInvalidValue;
+  const bool c16 = a.C16 != nullptr && a.n_epoch_slots > 0;
+  if (c16) {
+    const int64_t n = (int64_t)a.n_epoch_slots * a.epoch_C_stride / 16;  // uint4 units
+    const int64_t nb = (n + 255) / 256;
+    hipLaunchKernelGGL(c16_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, s,
+                       reinterpret_cast<const uint4*>(a.Cbase), reinterpret_cast<uint4*>(a.C16), n);
+  }
   dim3 grid((unsigned)nwg), block(kAttnThreads);
-  if (a.nself > 0)
-    hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, block, 0, s, a, p);
-  else
-    hipLaunchKernelGGL(attend_bf16_kernel<false>, grid, block, 0, s, a, p);
+  if (a.nself > 0) {
+    if (c16)
+      hipLaunchKernelGGL((attend_bf16_kernel<true, true>), grid, block, 0, s, a, p);
+    else
+      hipLaunchKernelGGL((attend_bf16_kernel<true, false>), grid, block, 0, s, a, p);
+  } else {
+    if (c16)
+      hipLaunchKernelGGL((attend_bf16_kernel<false, true>), grid, block, 0, s, a, p);
+    else
+      hipLaunchKernelGGL((attend_bf16_kernel<false, false>), grid, block, 0, s, a, p);
+  }
   return hipGetLastError();
 }
 

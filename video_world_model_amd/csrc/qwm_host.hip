@@ -128,7 +128,11 @@ Layout make_layout(const qwm_desc* d) {
   // centroid-to-centroid bounds of the pruned assignment (128 or more centroids)
   L.km_ccd = take(m >= 128 ? (size_t)(H * m * m * 4) : 0);
   L.qU = take((size_t)(H * E * maxq * qwm::kRankPad * 4));
-  L.qc = take((size_t)(H * E * m * nqp_max * 4));
+  // the decode path's q . C tables; the bf16 head_dim-128 prefill path keeps
+  // an fp16 copy of the epochs' centroid tables in the same region
+  const int64_t qc_bytes = H * E * m * nqp_max * 4;
+  const int64_t c16_bytes = (d->dtype == QWM_BF16 && D == 128) ? H * E * m * D * 2 : 0;
+  L.qc = take((size_t)(qc_bytes > c16_bytes ? qc_bytes : c16_bytes));
   L.part_o = take((size_t)(pr * D * 4));
   L.part_ml = take((size_t)(pr * 2 * 4));
   L.work = take(sizeof(unsigned long long) * QWM_K_COUNT);  // profiling work counters
@@ -370,9 +374,14 @@ struct AttnWork {
   float* part_o;
   float* part_ml;
   int64_t part_rows;
+  void* c16;  // room for the fp16 centroid copy of the bf16 head_dim-128 prefill path, or null
 };
 
-AttnWork arena_work(const qwm_cache* c) { return {c->qU(), c->qc(), c->part_o(), c->part_ml(), c->L.part_rows}; }
+AttnWork arena_work(const qwm_cache* c) {
+  // the arena's q . C region is sized to hold the copy (make_layout)
+  void* c16 = (c->dtype == QWM_BF16 && c->D == 128) ? static_cast<void*>(c->qc()) : nullptr;
+  return {c->qU(), c->qc(), c->part_o(), c->part_ml(), c->L.part_rows, c16};
+}
 
 qwm::AttnArgs base_args(qwm_cache* c, const AttnWork& w) {
   qwm::AttnArgs a{};
@@ -531,6 +540,7 @@ qwm_status attend_impl(qwm_cache* c, const void* q, int64_t n_q, const void* k_s
   a.n_epoch_slots = E;
   a.qpb = queries_per_block(n_q);
   a.out = out;
+  a.C16 = w.c16;
   // Few Queries over bf16 Keys: the decode kernel (2-bit codes as the MFMA
   // operand, one wave per workgroup, many splits)
   if (use_decode(c, mask, n_q)) return attend_decode(c, q, n_q, softmax_scale, out, p, w);
@@ -900,6 +910,11 @@ qwm_status qwm_attend_noalloc(qwm_cache* c, const void* q, int64_t n_q, const vo
   };
   const size_t oU = take(H * E * (size_t)n_q * qwm::kRankPad * 4);
   const size_t oC = decode ? take(H * E * (size_t)c->m * nqp * 4) : off;
+  // the fp16 centroid copy of the bf16 head_dim-128 prefill path, where it
+  // fits (without it the kernel converts the bf16 rows of every tile)
+  const size_t c16_bytes = H * E * (size_t)c->m * c->D * 2;
+  const bool c16 = !decode && c->dtype == QWM_BF16 && c->D == 128 && align_up(off + c16_bytes) + 2 * kAlign <= kScratchBytes;
+  const size_t oC16 = c16 ? take(c16_bytes) : 0;
   if (off + 2 * kAlign > kScratchBytes)
     return fail(QWM_ERR_CAPACITY, "qwm_attend_noalloc: n_q = " + std::to_string(n_q) + " needs " + std::to_string(off) +
                                       " bytes of tables, beyond the " + std::to_string(kScratchBytes >> 20) +
@@ -907,7 +922,8 @@ qwm_status qwm_attend_noalloc(qwm_cache* c, const void* q, int64_t n_q, const vo
   const size_t rows = (kScratchBytes - off - 2 * kAlign) / ((size_t)c->D * 4 + 8);
   const size_t oO = take(rows * c->D * 4), oML = take(rows * 8);
   AttnWork w{reinterpret_cast<float*>(base + oU), reinterpret_cast<float*>(base + oC),
-             reinterpret_cast<float*>(base + oO), reinterpret_cast<float*>(base + oML), (int64_t)rows};
+             reinterpret_cast<float*>(base + oO), reinterpret_cast<float*>(base + oML), (int64_t)rows,
+             c16 ? static_cast<void*>(base + oC16) : nullptr};
   c->no_events = true;  // hipEventCreate is not called on this path
   st = attend_impl(c, q, n_q, k_self, v_self, n_self, mask, softmax_scale, out, w);
   c->no_events = false;

@@ -122,6 +122,8 @@ struct AttnArgs {
   CacheView cache;
   const void* Cbase;      // epoch slot 0 centroid table; slot e at + e * epoch_C_stride bytes
   int64_t epoch_C_stride; // bytes
+  void* C16;              // bf16 head_dim-128 prefill: room for an fp16 copy of slots 0..n_epoch_slots-1
+                          // (same layout), or null: the tiles then convert the bf16 rows
   int n_epoch_slots;      // E of qU
   int H, m, r;
   int splits;
