@@ -93,28 +93,62 @@ __device__ __forceinline__ float add_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The 16 codes of one 32-bit word (code c of channel c in bits 2c..2c+1)
-// times the step s, as fp16 pairs (channels 2p, 2p+1 in out[p]): the pair is
-// or-ed into fp16 1024 + code (exact), 1024 is subtracted (exact) and the
-// codes are multiplied by s (exact: 3 s is an fp16 value).
+// Codes times steps as fp16 pairs. A code pair c0, c1 (bits 0-1 and 16-17
+// of x, the rest zero) is or-ed into the fp16 pair 1024 + c (exact); then
+// c s is either (b - 1024) * s, two exact operations, or, when every lane's
+// steps are below 64 (wave-uniform `small`), one fused b * s - 1024 s: -1024 s
+// is exact there and the single rounding returns the exact c s (3 s is an
+// fp16 value by the step rule).
 // (The fp16 1024 pair comes from a VGPR: with the mask in an SGPR the
 // compiler fuses "(x & mask) | magic" into one v_and_or_b32, which reads at
 // most one scalar operand here.)
-__device__ __forceinline__ void codes_times_step(uint32_t w, uint32_t s_bits, uint32_t (&out)[8]) {
-  const half2v s2 = __builtin_bit_cast(half2v, s_bits | (s_bits << 16));
-  const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+struct CodeScale {
+  half2v s2, nb;  // steps; -1024 * steps (used when small)
   uint32_t magic;
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  bool small;
+};
+__device__ __forceinline__ CodeScale code_scale(uint32_t s2_bits) {
+  CodeScale cs;
+  cs.s2 = __builtin_bit_cast(half2v, s2_bits);
+  cs.nb = cs.s2 * (half2v){(_Float16)-1024.0f, (_Float16)-1024.0f};
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(cs.magic));
+  // fp16 bits below 0x5400 (64.0) in both halves (steps are >= 0)
+  const bool ok = (s2_bits & 0x7FFFu) < 0x5400u && ((s2_bits >> 16) & 0x7FFFu) < 0x5400u;
+  cs.small = __builtin_amdgcn_ballot_w64(!ok) == 0;
+  return cs;
+}
+// out[i] = the code pair in bits 2 sh[i] of x[i] times the steps, for the
+// eight pairs (the branch on `small` is taken once for all of them)
+__device__ __forceinline__ void code_pairs(const uint32_t (&x)[8], const CodeScale& cs, uint32_t (&out)[8]) {
+  if (cs.small) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const uint32_t x = (w >> (16 * half)) & 0xFFFFu;
-    const uint32_t y = x | (x << 14);  // code 2p at bits 4p, code 2p+1 at bits 16+4p
+    for (int i = 0; i < 8; ++i) {
+      const half2v b = __builtin_bit_cast(half2v, (x[i] & 0x00030003u) | cs.magic);
+      out[i] = h2_bits(__builtin_elementwise_fma(b, cs.s2, cs.nb));
+    }
+  } else {
+    const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t b = ((y >> (4 * p)) & 0x00030003u) | magic;
-      out[4 * half + p] = h2_bits((__builtin_bit_cast(half2v, b) - k1024) * s2);
+    for (int i = 0; i < 8; ++i) {
+      const half2v b = __builtin_bit_cast(half2v, (x[i] & 0x00030003u) | cs.magic);
+      out[i] = h2_bits((b - k1024) * cs.s2);
     }
   }
+}
+// The 16 codes of one 32-bit word (code c of channel c in bits 2c..2c+1)
+// times the step s (fp16 bits s_bits), as fp16 pairs (channels 2p, 2p+1 in
+// out[p]).
+__device__ __forceinline__ void codes_times_step(uint32_t w, uint32_t s_bits, uint32_t (&out)[8]) {
+  const CodeScale cs = code_scale(s_bits | (s_bits << 16));
+  uint32_t x[8];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t h = (w >> (16 * half)) & 0xFFFFu;
+    const uint32_t y = h | (h << 14);  // code 2p at bits 4p, code 2p+1 at bits 16+4p
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x[4 * half + p] = y >> (4 * p);
+  }
+  code_pairs(x, cs, out);
 }
 
 struct TileInfo {
@@ -333,15 +367,11 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
       // both tokens' codes of channels 8 hh .. 8 hh + 7: channel c in bits
       // 2c (token 2p) and 16 + 2c (token 2p + 1)
       const uint32_t z = __builtin_amdgcn_perm(r.code1, r.code0, hh ? 0x07060302u : 0x05040100u);
-      const half2v s2 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(r.prm1, r.prm0, 0x07060302u));
-      const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-      uint32_t magic;
-      asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+      const CodeScale cs = code_scale(__builtin_amdgcn_perm(r.prm1, r.prm0, 0x07060302u));
+      uint32_t x[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t b = ((z >> (2 * c)) & 0x00030003u) | magic;
-        v[c] = h2_bits((__builtin_bit_cast(half2v, b) - k1024) * s2);
-      }
+      for (int c = 0; c < 8; ++c) x[c] = z >> (2 * c);
+      code_pairs(x, cs, v);
     } else {
       // self Values: channel 2i / 2i + 1 in the low / high half of word i
       const uint32_t a[4] = {r.s0.x, r.s0.y, r.s0.z, r.s0.w};
@@ -508,10 +538,13 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) mx = fmaxf(mx, S[qb][tb][v]);
-      mx = max_xor32(max_xor16(mx));
-      mx *= cl2;
-      const bool raise = mx > mrow[qb] + 8.0f;
-      if (__ballot(raise)) {  // wave-uniform: rescale every lane (alpha = 1 where unchanged)
+      // The row maximum is needed only where the running max rises, which
+      // any of its four lanes sees from its own 16 logits; the lanes
+      // exchange maxima only then (wave-uniform: rescale every lane, alpha
+      // = 1 where unchanged).
+      if (__ballot(mx * cl2 > mrow[qb] + 8.0f)) {
+        mx = max_xor32(max_xor16(mx)) * cl2;
+        const bool raise = mx > mrow[qb] + 8.0f;
         const float mnew = raise ? mx : mrow[qb];
         const float alpha = (mrow[qb] == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(mrow[qb] - mnew);
         mrow[qb] = mnew;
