@@ -18,7 +18,8 @@ and reported per refresh and per frame.
 Other workloads (--workload): video_chunk (a whole step of calibration,
 quantize-append of 7,040 tokens and attention of 880 Queries with their own
 K/V; --mode picks QVG and the ablations), wm_layer, long_horizon (attention
-over a prebuilt 131,072-token cache; decode-shaped with --nq <= 64).
+over a prebuilt 131,072-token cache; with --nq <= 48 the decode kernel runs,
+and up to 64 Queries the launch is priced against HBM, past that against MFMA).
 
 Prints ONE JSON line. `value` = cache token-heads attended per second of
 step time (H * N_kv / t_step). `roofline` reports the kernel with the most
@@ -68,13 +69,18 @@ MODES = {  # objective, PSAC on
 }
 
 KERNELS = ["quantize", "attend", "merge", "qu", "gram", "eigen", "assign", "update", "other"]
+# The sources each kernel class is compiled from: its file(s) and the headers
+# every kernel includes (device helpers and the internal constants).
+_HEADERS = ("qwm_dev.h", "qwm_internal.h")
 KERNEL_SOURCES = {
-    "quantize": "kern_quant.hip", "assign": "kern_quant.hip", "update": "kern_quant.hip",
+    "quantize": ("kern_quant.hip",) + _HEADERS, "assign": ("kern_quant.hip",) + _HEADERS,
+    "update": ("kern_quant.hip",) + _HEADERS, "other": ("kern_quant.hip",) + _HEADERS,
     # the attention class: the general kernel, the bf16 head_dim-128 kernel and the decode kernel
-    "attend": ("kern_attend.hip", "kern_attend_bf16.hip", "kern_decode.hip"),
-    "merge": "kern_attend.hip", "qu": "kern_attend.hip",
-    "gram": "kern_calib.hip", "eigen": "kern_calib.hip", "diag": "kern_calib.hip", "other": "kern_quant.hip",
-    "decode": "kern_decode.hip", "qc": "kern_decode.hip",
+    "attend": ("kern_attend.hip", "kern_attend_bf16.hip", "kern_decode.hip", "qwm_codes.h") + _HEADERS,
+    "merge": ("kern_attend.hip",) + _HEADERS, "qu": ("kern_attend.hip",) + _HEADERS,
+    "gram": ("kern_calib.hip",) + _HEADERS, "eigen": ("kern_calib.hip",) + _HEADERS,
+    "diag": ("kern_calib.hip",) + _HEADERS,
+    "decode": ("kern_decode.hip", "qwm_codes.h") + _HEADERS, "qc": ("kern_decode.hip", "qwm_codes.h") + _HEADERS,
 }
 
 
@@ -547,8 +553,11 @@ def bench_long_horizon(args, w):
     attend_bytes = w.heads * (w.n_kv * B + nq * w.head_dim * 2 + nq * w.head_dim * 4)
     attend_flops = w.heads * nq * w.n_kv * (4 * w.head_dim + 2 * w.rank)
     ta = kern["attend"]["avg_launch_ms"] * 1e-3
-    decode = nq <= 64
-    if decode:
+    # the packed cache's bytes bound the launch up to about 79 Queries per head
+    # (2.5 PFLOP/s over 8 TB/s against 4 * 128 flops per Query and ~130 B per
+    # token); 64 is the round cut used here
+    hbm_bound = nq <= 64
+    if hbm_bound:
         achieved = attend_bytes / ta / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS,
                     work=f"{w.heads} heads x ({w.n_kv} tokens x {B} B + {nq} Queries x {w.head_dim} x (2 + 4) B) "
@@ -559,7 +568,9 @@ def bench_long_horizon(args, w):
                     frac=achieved / MFMA_F16_PEAK_TFLOPS,
                     work=f"{w.heads} heads x {nq} Queries x {w.n_kv} tokens x (4*{w.head_dim} + 2*{w.rank}) flops "
                          f"= {attend_flops:.4g} per launch")
-    roof["kernel"] = "decode" if decode else "attend"
+    # the library's dispatch: bf16 head_dim-128 calls of at most 48 Queries
+    # and no self segment run the decode kernel
+    roof["kernel"] = "decode" if nq <= 48 else "attend"
     roof["traffic"] = measured_traffic(roof["kernel"], f"{w.name}_nq{nq}" if args.nq else w.name)
     rec = {
         "metric": METRIC,
@@ -600,7 +611,7 @@ def main():
                     help="streaming: the 100,000-token cache is built once (untimed); a step appends one "
                          "1,560-token frame and attends with 1,560 Queries; the every-8-frames refresh is timed "
                          "apart. long_horizon: the 131,072-token, 11-epoch cache is built once (untimed) and a "
-                         "step is one attention of --nq Queries per head over it (decode-shaped when --nq <= 64)")
+                         "step is one attention of --nq Queries per head over it (decode kernel when --nq <= 48)")
     ap.add_argument("--nq", type=int, default=0, help="Queries per head for long_horizon (default: the workload's)")
     ap.add_argument("--mode", default="quantwm", choices=sorted(MODES))
     ap.add_argument("--graph", type=int, default=0,

@@ -206,9 +206,13 @@ qwm_status qwm_attend(qwm_cache* cache, const void* q, int64_t n_q, const void* 
  * static device array of the library, 64 MiB on each device, instead of the
  * cache's arena. n_q is bounded by that array, not by max_query_tokens: the
  * tables need heads * epochs * n_q * 64 bytes (plus heads * epochs *
- * n_centroids * 16 * ceil(n_q / 16) * 4 on the decode path, n_q <= 64), and
+ * n_centroids * 16 * ceil(n_q / 16) * 4 on the decode path, n_q <= 48), and
  * a call whose tables do not fit returns QWM_ERR_CAPACITY before anything is
  * enqueued; the partials take what is left (fewer KV splits, down to none).
+ * On the prefill path of a bf16 head_dim-128 cache an fp16 copy of the
+ * epochs' centroid tables (heads * epochs * n_centroids * 256 bytes) comes
+ * before the partials where it fits; without it the kernel converts the
+ * rows it reads (same results).
  * It calls nothing that allocates (no hipMalloc, no hipEventCreate: kernel
  * timing is not recorded for it). Every call on one device shares the array,
  * which keeps the previous call's contents (a call writes every entry it

@@ -9,7 +9,7 @@ configuration the bench uses, on outputs the oracle can recompute one by one:
   heads; 32 sampled Queries of one head attend over all 101,560 tokens.
 * long_horizon: 131,072 tokens with per-frame mean drift, 11 epochs; 32
   sampled Queries of a 390-Query chunk on one head, and every Query of
-  64- and 16-Query decode chunks on one head.
+  48- and 16-Query decode chunks on one head.
 
 Calibration is imported (oracle-made: sensitivity and subspace from the
 epoch's historical Queries, centroids seeded from the epoch's first frame)
@@ -142,9 +142,9 @@ def test_long_horizon_full_size():
     log("  last 2,000 tokens bit-exact on 2 heads")
     q_idx = np.unique(np.concatenate([[0, w.n_q - 1], rng.integers(0, w.n_q, 30)]))
     _check_attention(w, cache, gens, cals_all, 11, q_idx, w.n_kv)
-    # decode-shaped chunks (the decode kernel): 64 and 16 Queries, all rows of one head
+    # decode-shaped chunks (the decode kernel): 48 and 16 Queries, all rows of one head
     hc = _oracle_head(w, gens[11], cals_all, w.n_kv)
-    for nq in (64, 16):
+    for nq in (48, 16):
         q_all = [g.current_queries()[:nq] for g in gens]
         out = cache.attend(to_dev(q_all, w.dtype)).cpu().numpy()
         assert np.isfinite(out).all()

@@ -141,8 +141,8 @@ def _degenerate_rows(rng, n, d, dtype, C):
     return rows
 
 
-# bf16 at 64 Queries runs the decode kernel, at 96 the prefill kernel
-@pytest.mark.parametrize("name,n_q", [("tiny", 64), ("video_chunk", 64), ("video_chunk", 96)])
+# bf16 at 48 Queries runs the decode kernel, at 96 the prefill kernel
+@pytest.mark.parametrize("name,n_q", [("tiny", 64), ("video_chunk", 48), ("video_chunk", 96)])
 def test_quantize_degenerate_groups(name, n_q):
     """Quantize-append and attention over Keys and Values made of degenerate
     groups: the records equal the oracle's bit for bit and the outputs stay
@@ -189,14 +189,14 @@ def _oracle_heads(w, keys, vals, cals):
     return hcs
 
 
-# 65 Queries: the first count past the decode kernel's 64 (prefill path);
+# 49 Queries: the first count past the decode kernel's 48 (prefill path);
 # 257: one live Query in the second 256-Query workgroup; 1000 Keys: a ragged
 # last tile.
 @pytest.mark.parametrize("name,heads,n_kv,n_q,mask", [
     ("tiny", 1, 1024, 16, "none"),
     ("video_chunk", 12, 7040, 880, "full"),
     ("video_chunk", 2, 1000, 200, "none"),
-    ("video_chunk", 2, 1000, 65, "none"),
+    ("video_chunk", 2, 1000, 49, "none"),
     ("video_chunk", 2, 3001, 257, "none"),
 ])
 def test_attend_matches_oracle(name, heads, n_kv, n_q, mask):

@@ -40,6 +40,7 @@
 //    construction) the other is on the MFMA pipe. K stages are triple
 //    buffered (tiles i and i+1 are read while i+2 is built), V stages double
 //    buffered; one barrier per tile.
+#include "qwm_codes.h"
 #include "qwm_dev.h"
 #include "qwm_internal.h"
 
@@ -47,7 +48,6 @@ namespace qwm {
 
 namespace {
 
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
@@ -93,54 +93,12 @@ __device__ __forceinline__ float add_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Codes times steps as fp16 pairs. A code pair c0, c1 (bits 0-1 and 16-17
-// of x, the rest zero) is or-ed into the fp16 pair 1024 + c (exact); then
-// c s is either (b - 1024) * s, two exact operations, or, when every lane's
-// steps are below 64 (wave-uniform `small`), one fused b * s - 1024 s: -1024 s
-// is exact there and the single rounding returns the exact c s (3 s is an
-// fp16 value by the step rule).
-// (The fp16 1024 pair comes from a VGPR: with the mask in an SGPR the
-// compiler fuses "(x & mask) | magic" into one v_and_or_b32, which reads at
-// most one scalar operand here.)
-struct CodeScale {
-  half2v s2, nb;  // steps; -1024 * steps (used when small)
-  uint32_t magic;
-  bool small;
-};
-__device__ __forceinline__ CodeScale code_scale(uint32_t s2_bits) {
-  CodeScale cs;
-  cs.s2 = __builtin_bit_cast(half2v, s2_bits);
-  cs.nb = cs.s2 * (half2v){(_Float16)-1024.0f, (_Float16)-1024.0f};
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(cs.magic));
-  // fp16 bits below 0x5400 (64.0) in both halves (steps are >= 0)
-  const bool ok = (s2_bits & 0x7FFFu) < 0x5400u && ((s2_bits >> 16) & 0x7FFFu) < 0x5400u;
-  cs.small = __builtin_amdgcn_ballot_w64(!ok) == 0;
-  return cs;
-}
-// out[i] = the code pair in bits 2 sh[i] of x[i] times the steps, for the
-// eight pairs (the branch on `small` is taken once for all of them)
-__device__ __forceinline__ void code_pairs(const uint32_t (&x)[8], const CodeScale& cs, uint32_t (&out)[8]) {
-  if (cs.small) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const half2v b = __builtin_bit_cast(half2v, (x[i] & 0x00030003u) | cs.magic);
-      out[i] = h2_bits(__builtin_elementwise_fma(b, cs.s2, cs.nb));
-    }
-  } else {
-    const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const half2v b = __builtin_bit_cast(half2v, (x[i] & 0x00030003u) | cs.magic);
-      out[i] = h2_bits((b - k1024) * cs.s2);
-    }
-  }
-}
 // The 16 codes of one 32-bit word (code c of channel c in bits 2c..2c+1)
 // times the step s (fp16 bits s_bits), as fp16 pairs (channels 2p, 2p+1 in
 // out[p]).
 __device__ __forceinline__ void codes_times_step(uint32_t w, uint32_t s_bits, uint32_t (&out)[8]) {
   const CodeScale cs = code_scale(s_bits | (s_bits << 16));
-  uint32_t x[8];
+  uint32_t x[8];  // codes 2p, 2p+1 of half `half` (x[4 half + p]) in bits 0-1 and 16-17
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const uint32_t h = (w >> (16 * half)) & 0xFFFFu;

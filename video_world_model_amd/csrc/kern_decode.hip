@@ -27,6 +27,7 @@
 // split of the KV tiles; every wave streams its own 64-token tiles, so many
 // tiles are in flight per CU. The packed words of the next tile are loaded
 // while the current one is computed.
+#include "qwm_codes.h"
 #include "qwm_dev.h"
 #include "qwm_internal.h"
 
@@ -34,7 +35,6 @@ namespace qwm {
 
 namespace {
 
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -81,14 +81,6 @@ __device__ __forceinline__ half8 codes_to_f16_sub(uint32_t w) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) d[p] = (w >> (2 * p)) & 0x00030003u;
   return __builtin_bit_cast(half8, make_uint4(d[0], d[1], d[2], d[3]));
-}
-// 0x64006400 (fp16 1024, 1024) in a VGPR: with the mask in an SGPR the
-// compiler can then fuse "(x & mask) | magic" into one v_and_or_b32 (a VOP3
-// reads at most one scalar operand here).
-__device__ __forceinline__ uint32_t magic_1024_vgpr() {
-  uint32_t m;
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
-  return m;
 }
 
 // ---------------------------------------------------------------- q . C table
@@ -309,37 +301,29 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
     }
   };
   // Values of one channel pass: 16 channels of 4 tokens (slots 4j + tb)
-  // as code * s (exact fp16).
+  // as code * s (exact fp16). The tokens go in pairs (tb 0, 1) and (2, 3):
+  // one byte permute puts both tokens' codes of 8 channels into one word
+  // (the first token's channel c in bits 2c, the second's in 16 + 2c), so
+  // each channel's fp16 pair is already the two slots' values of its row.
   auto dequant_v = [&](const uint32_t (&vc)[4], const uint32_t (&vp)[4]) {
-    const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    const uint32_t magic = magic_1024_vgpr();
-    half2v s2[4];
-    uint32_t y[4][2];  // spread 8-code halves: codes 0..3 in byte 0, codes 4..7 in byte 2
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const uint32_t sb = vp[tb] >> 16;
-      s2[tb] = __builtin_bit_cast(half2v, sb | (sb << 16));
-      y[tb][0] = spread_unit(vc[tb], 0x0C010C00u);
-      y[tb][1] = spread_unit(vc[tb], 0x0C030C02u);
-    }
+    const CodeScale cs01 = code_scale(__builtin_amdgcn_perm(vp[1], vp[0], 0x07060302u));
+    const CodeScale cs23 = code_scale(__builtin_amdgcn_perm(vp[3], vp[2], 0x07060302u));
     const int clb = 32 * (kg >> 1) + 16 * (kg & 1);  // first local channel
 #pragma unroll
-    for (int pp = 0; pp < 8; ++pp) {
-      const int hh = pp >> 2, pq = pp & 3;
-      const int ca = 8 * hh + pq, cb = ca + 4;  // the pair's channels
-      uint32_t cs[4];  // channels ca, cb of token tb
+    for (int hh = 0; hh < 2; ++hh) {  // channels clb + 8 hh .. +7
+      const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
+      const uint32_t z01 = __builtin_amdgcn_perm(vc[1], vc[0], sel), z23 = __builtin_amdgcn_perm(vc[3], vc[2], sel);
+      uint32_t x01[8], x23[8], w01[8], w23[8];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const uint32_t b = ((y[tb][hh] >> (2 * pq)) & 0x00030003u) | magic;  // 1024 + code, exact
-        cs[tb] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2v, b) - k1024) * s2[tb]);
+      for (int c = 0; c < 8; ++c) {
+        x01[c] = z01 >> (2 * c);
+        x23[c] = z23 >> (2 * c);
       }
-      // channel ca of the four tokens, then channel cb
-      const uint32_t e01 = __builtin_amdgcn_perm(cs[1], cs[0], 0x05040100u);
-      const uint32_t e23 = __builtin_amdgcn_perm(cs[3], cs[2], 0x05040100u);
-      const uint32_t o01 = __builtin_amdgcn_perm(cs[1], cs[0], 0x07060302u);
-      const uint32_t o23 = __builtin_amdgcn_perm(cs[3], cs[2], 0x07060302u);
-      *reinterpret_cast<uint2*>(vt + vrow_off(clb + ca) + 4 * j) = make_uint2(e01, e23);
-      *reinterpret_cast<uint2*>(vt + vrow_off(clb + cb) + 4 * j) = make_uint2(o01, o23);
+      code_pairs(x01, cs01, w01);
+      code_pairs(x23, cs23, w23);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<uint2*>(vt + vrow_off(clb + 8 * hh + c) + 4 * j) = make_uint2(w01[c], w23[c]);
     }
   };
   // Zero-points of the 4 tokens (slots 4j + tb) of the lane's group into row

@@ -170,7 +170,10 @@ struct DecodeArgs {
 hipError_t launch_qc(const void* q, int64_t nq, int nqp, const void* Cbase, int64_t epoch_C_stride, int H, int m,
                      int E, float sign, float* qc, hipStream_t s);
 constexpr int kDecodeQ = 16;        // Queries per decode workgroup
-constexpr int kDecodeMaxQ = 64;     // largest n_q served by the decode kernel
+// largest n_q served by the decode kernel: each 16-Query block streams the
+// cache on its own, so from the fourth block on the prefill kernel (which
+// stages every tile once per workgroup) is the faster one
+constexpr int kDecodeMaxQ = 48;
 constexpr int kDecodeWavesPerCU = 8;  // resident decode workgroups per CU (2 waves per SIMD)
 hipError_t launch_decode(const DecodeArgs& a, const AttnPlan& p, hipStream_t s);
 
