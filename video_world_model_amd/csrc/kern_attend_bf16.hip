@@ -73,16 +73,14 @@ __device__ __forceinline__ uint32_t h2_bits(half2v h) { return __builtin_bit_cas
 // x combined with lane l ^ 16 / l ^ 32 through the gfx950 row-swap
 // permutes (VALU; a __shfl_xor becomes an LDS-pipe ds_bpermute): after the
 // swap of a register with itself the two results hold, in every lane, the
-// lane's own value and its partner's. The larger of the two is the median
-// of (a, b, +inf): one v_med3_f32, where fmaxf would first quiet both
-// inputs (logits are never NaN).
+// lane's own value and its partner's.
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __builtin_inff());
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __builtin_inff());
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float add_xor16(float x) {  // x + partner (addition commutes exactly)
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

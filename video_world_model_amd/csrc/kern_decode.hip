@@ -51,12 +51,24 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_row(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+// +inf in a VGPR, opaque to the compiler: max2 below would otherwise be
+// folded back into a maximum.
+__device__ __forceinline__ float opaque_inf() {
+  float x;
+  asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(x));
+  return x;
+}
+// The larger of a and b as the median of (a, b, +inf): one v_med3_f32. A
+// maximum (fmaxf) first quiets both inputs in IEEE mode, two more
+// instructions where an input is not known to be canonical (a lane move, a
+// sum); logits are never NaN.
+__device__ __forceinline__ float max2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
 // Max / sum over the 16 lanes of a row; every lane of the row gets the result.
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_row<kDppQuadSwap1>(x));
-  x = fmaxf(x, dpp_row<kDppQuadSwap2>(x));
-  x = fmaxf(x, dpp_row<kDppRowHalfMirror>(x));
-  x = fmaxf(x, dpp_row<kDppRowMirror>(x));
+__device__ __forceinline__ float row16_max(float x, float inf) {
+  x = max2(x, dpp_row<kDppQuadSwap1>(x), inf);
+  x = max2(x, dpp_row<kDppQuadSwap2>(x), inf);
+  x = max2(x, dpp_row<kDppRowHalfMirror>(x), inf);
+  x = max2(x, dpp_row<kDppRowMirror>(x), inf);
   return x;
 }
 __device__ __forceinline__ float row16_sum(float x) {
@@ -169,6 +181,7 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
   __shared__ __attribute__((aligned(16))) _Float16 pt[NQ * PROW];
   __shared__ __attribute__((aligned(16))) uint32_t kst[kTileKV * 8];  // K codes [token][kg][group] u16
   __shared__ __attribute__((aligned(16))) uint32_t kpr[kTileKV * 4];  // K params [token][group]
+  __shared__ __attribute__((aligned(16))) float kst24[kTileKV * 4];   // K steps times 2^24 [token][group]
   __shared__ __attribute__((aligned(16))) uint32_t cst[kTileKV * 8];  // PSAC coefficients [token][16]
   auto vrow_off = [](int cl) { return cl * VROW + 32 * (cl >> 4); };  // local channel 0..63
 
@@ -290,7 +303,9 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       }
     }
   };
-  // q . C of the lane's 4 Queries (4kg .. +3) and token 16tb + j
+  // q . C of the lane's 4 Queries (4kg .. +3) and token 16tb + j; -inf for
+  // the token slots past the end of a segment's last tile, so that their
+  // logits are -inf (the other terms are finite)
   auto load_qc = [&](floatx4 (&dst)[4], const TileInfo& ti, uint32_t id_lane) {
     const float* base = qc_h + (size_t)ti.ep * a.m * a.nqp + q0 + 4 * kg;
 #pragma unroll
@@ -298,6 +313,15 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       const uint32_t id = (uint32_t)__shfl((int)id_lane, 16 * tb + j);
       const float4 x = *reinterpret_cast<const float4*>(base + id * (uint32_t)a.nqp);
       dst[tb] = floatx4{x.x, x.y, x.z, x.w};
+    }
+    if (ti.tcount < kTileKV) {  // wave-uniform
+      // (keeps this rare branch a branch: the selects would otherwise run
+      // on every tile)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        if (16 * tb + j >= ti.tcount)
+          dst[tb] = floatx4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
     }
   };
   // Values of one channel pass: 16 channels of 4 tokens (slots 4j + tb)
@@ -376,6 +400,10 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       ks4[0] = make_uint4(nw[0], nw[1], nw[2], nw[3]);
       ks4[1] = make_uint4(nw[4], nw[5], nw[6], nw[7]);
       *reinterpret_cast<uint4*>(kpr + lane * 4) = cur.kp;
+      // the steps times 2^24 (exact in float32), once per token
+      *reinterpret_cast<float4*>(kst24 + lane * 4) =
+          make_float4(half_bits_to_float(cur.kp.x >> 16) * 16777216.0f, half_bits_to_float(cur.kp.y >> 16) * 16777216.0f,
+                      half_bits_to_float(cur.kp.z >> 16) * 16777216.0f, half_bits_to_float(cur.kp.w >> 16) * 16777216.0f);
       uint4* cs4 = reinterpret_cast<uint4*>(cst + lane * 8);
       cs4[0] = make_uint4(cur.c0.x & cmask[0], cur.c0.y & cmask[1], cur.c0.z & cmask[2], cur.c0.w & cmask[3]);
       cs4[1] = make_uint4(cur.c1.x & cmask[4], cur.c1.y & cmask[5], cur.c1.z & cmask[6], cur.c1.w & cmask[7]);
@@ -425,8 +453,9 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       const int tt = 16 * tb + j;
       const uint2 cw = *reinterpret_cast<const uint2*>(kst + tt * 8 + 2 * kg);
       const uint4 kp = *reinterpret_cast<const uint4*>(kpr + tt * 4);
+      const float4 st4 = *reinterpret_cast<const float4*>(kst24 + tt * 4);
+      const float st[4] = {st4.x, st4.y, st4.z, st4.w};
       const uint4 cf = *reinterpret_cast<const uint4*>(cst + tt * 8 + 4 * (kg & 1));
-      const uint32_t kpw[4] = {kp.x, kp.y, kp.z, kp.w};
       // zero-points of groups 0..3 at k = 8kg + G; ax2 is zero for k = 8kg + 4..7
       // and for kg >= 2, where the (finite) repeats below meet zeros
       const uint32_t z01 = __builtin_amdgcn_perm(kp.y, kp.x, 0x05040100u);
@@ -436,42 +465,42 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
       acc = mfma_f16(ax2, bzp, acc);
       const uint32_t cws[4] = {spread_unit(cw.x, 0x0C010C00u), spread_unit(cw.x, 0x0C030C02u),
                                spread_unit(cw.y, 0x0C010C00u), spread_unit(cw.y, 0x0C030C02u)};
+      // q_G . (code_G * 2^-24), exact in float32; the step carries the 2^24.
+      // The four MFMAs go first, so that each result has arrived when its
+      // multiply-adds start.
+      floatx4 dg[NG];
 #pragma unroll
-      for (int G = 0; G < NG; ++G) {
-        // q_G . (code_G * 2^-24), exact in float32; the step carries the 2^24
-        const floatx4 dg = mfma_f16(qa[G], codes_to_f16_sub(cws[G]), floatx4{0.f, 0.f, 0.f, 0.f});
-        const float st = half_bits_to_float(kpw[G] >> 16) * 16777216.0f;
+      for (int G = 0; G < NG; ++G) dg[G] = mfma_f16(qa[G], codes_to_f16_sub(cws[G]), floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(st, dg[v], acc[v]);
-      }
+      for (int G = 0; G < NG; ++G)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += qcc[tb][v];  // the table carries the sign
+        for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(st[G], dg[G][v], acc[v]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += qcc[tb][v];  // the table carries the sign (and the mask)
       S[tb] = acc;
-    }
-    if (ti.tcount < kTileKV) {  // wave-uniform: the last tile of a segment
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        if (16 * tb + j >= ti.tcount)
-          S[tb] = floatx4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
     }
 
     // ---- online softmax (log2 domain); the running max is raised only when
-    // a row's max exceeds it by more than 8, so the rescale of O is rare
+    // a row's max exceeds it by more than 8, so the rescale of O is rare. A
+    // lane sees from its own 4 logits whether its row rises; the 16 lanes of
+    // a row exchange maxima only then (wave-uniform branch).
     bool raise_any = false;
-    float mnew[4];
+    float lmx[4];
+    const float inf = opaque_inf();
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float mx = fmaxf(fmaxf(S[0][v], S[1][v]), fmaxf(S[2][v], S[3][v]));
-      mx = row16_max(mx) * cl2;
-      const bool raise = mx > mrow[v] + 8.0f;
-      mnew[v] = raise ? mx : mrow[v];
-      raise_any |= raise;
+      lmx[v] = max2(max2(S[0][v], S[1][v], inf), max2(S[2][v], S[3][v], inf), inf);
+      raise_any |= lmx[v] * cl2 > mrow[v] + 8.0f;
     }
-    if (__builtin_amdgcn_ballot_w64(raise_any)) {  // wave-uniform
+    if (__builtin_amdgcn_ballot_w64(raise_any)) {
+      // (keeps the lane exchanges inside this rare branch)
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float alpha = (mrow[v] == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(mrow[v] - mnew[v]);
-        mrow[v] = mnew[v];
+        const float mx = row16_max(lmx[v], inf) * cl2;
+        const float mnew = mx > mrow[v] + 8.0f ? mx : mrow[v];
+        const float alpha = (mrow[v] == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(mrow[v] - mnew);
+        mrow[v] = mnew;
         lrow[v] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < D / 16; ++cb) O[cb][v] *= alpha;
