@@ -409,12 +409,15 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
 
   // logits S^T blocks [16 tokens x 16 Queries] of the tile in stage Ks, in
   // eight steps (32 channels x two 16-token blocks: the c and code*s
-  // fragments, 4 reads). Each step's operands are read while the previous
-  // step's 8 MFMAs run, so a wait for LDS never idles the wave behind a
-  // single MFMA; the c products come before the code*s products of a step.
+  // fragments, 4 reads) and the X step. Each step's operands are read while
+  // earlier steps' MFMAs run (kAhead steps ahead: two where the registers
+  // allow, in the kernel without a self segment), so a wait for LDS never
+  // idles the wave behind a single MFMA; the c products come before the
+  // code*s products of a step.
+  constexpr int kAhead = SELF ? 1 : 2, kBufs = kAhead + 1;
   auto logits = [&](const _Float16* Ks, floatx4 (&S)[2][4]) {
     const _Float16* rb = Ks + l16 * kKRow + 8 * g;
-    half8 A[2][4];
+    half8 A[kBufs][4];
     auto rd = [&](half8 (&buf)[4], int stp) {  // ks = stp / 2, blocks tb = 2 (stp % 2) ..
       const int ks = stp >> 1, tb0 = 2 * (stp & 1);
 #pragma unroll
@@ -431,14 +434,16 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) S[qb][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    rd(A[0], 0);
+#pragma unroll
+    for (int stp = 0; stp < kAhead; ++stp) rd(A[stp], stp);
 #pragma unroll
     for (int stp = 0; stp < 9; ++stp) {
       __builtin_amdgcn_sched_barrier(0);
-      if (stp < 7)
-        rd(A[(stp + 1) & 1], stp + 1);
-      else if (stp == 7)
-        rdx(A[0]);
+      const int nx = stp + kAhead;  // the step whose operands are read now
+      if (nx < 8)
+        rd(A[nx % kBufs], nx);
+      else if (nx == 8)
+        rdx(A[8 % kBufs]);
       if (stp < 8) {
         const int ks = stp >> 1, tb0 = 2 * (stp & 1);
 #pragma unroll
@@ -447,12 +452,12 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
           for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
-              S[qb][tb0 + j] = mfma16(A[stp & 1][2 * j + pass], qh[qb][ks], S[qb][tb0 + j]);
+              S[qb][tb0 + j] = mfma16(A[stp % kBufs][2 * j + pass], qh[qb][ks], S[qb][tb0 + j]);
       } else {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) S[qb][tb] = mfma16(A[0][tb], xw[qb], S[qb][tb]);
+          for (int qb = 0; qb < 2; ++qb) S[qb][tb] = mfma16(A[8 % kBufs][tb], xw[qb], S[qb][tb]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -538,26 +543,27 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(const AttnArg
   // half); each step's operands are read while the previous step's MFMAs run.
   auto pv = [&](const _Float16* Vs, const half8 (&pf)[2][2]) {
     const _Float16* rb = Vs + l16 * kVRow + 8 * g;
-    half8 B[2][3];
+    half8 B[kBufs][3];
     auto rd = [&](half8 (&buf)[3], int stp) {  // ks = stp / 4, channel blocks 2 (stp % 4), +1
       const int ks = stp >> 2, cb0 = 2 * (stp & 3);
       buf[0] = *reinterpret_cast<const half8*>(rb + 16 * cb0 * kVRow + 32 * ks);
       buf[1] = *reinterpret_cast<const half8*>(rb + 16 * (cb0 + 1) * kVRow + 32 * ks);
       if ((stp & 3) == 3) buf[2] = *reinterpret_cast<const half8*>(rb + 128 * kVRow + 32 * ks);
     };
-    rd(B[0], 0);
+#pragma unroll
+    for (int stp = 0; stp < kAhead; ++stp) rd(B[stp], stp);
 #pragma unroll
     for (int stp = 0; stp < 8; ++stp) {
       __builtin_amdgcn_sched_barrier(0);
-      if (stp < 7) rd(B[(stp + 1) & 1], stp + 1);
+      if (stp + kAhead < 8) rd(B[(stp + kAhead) % kBufs], stp + kAhead);
       const int ks = stp >> 2, cb0 = 2 * (stp & 3);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) O[qb][cb0 + j] = mfma16(B[stp & 1][j], pf[qb][ks], O[qb][cb0 + j]);
+        for (int qb = 0; qb < 2; ++qb) O[qb][cb0 + j] = mfma16(B[stp % kBufs][j], pf[qb][ks], O[qb][cb0 + j]);
       if ((stp & 3) == 3) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) Z[qb] = mfma16(B[stp & 1][2], pf[qb][ks], Z[qb]);
+        for (int qb = 0; qb < 2; ++qb) Z[qb] = mfma16(B[stp % kBufs][2], pf[qb][ks], Z[qb]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
