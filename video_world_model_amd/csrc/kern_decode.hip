@@ -283,23 +283,29 @@ __global__ __launch_bounds__(64, 2) void decode_kernel(const DecodeArgs a, const
   auto load_raw = [&](DecRaw& r, const TileInfo& ti) {
     const uint32_t t = (uint32_t)ti.tstart + (uint32_t)(lane < ti.tcount ? lane : ti.tcount - 1);
     r.id = ids_h[t];
-    const uint4* kc = reinterpret_cast<const uint4*>(kcode_h + t * (D / 4));
+    const uint4* kc = reinterpret_cast<const uint4*>(kcode_h) + t * 2u;
     r.k0 = kc[0];
     r.k1 = kc[1];
-    r.kp = *reinterpret_cast<const uint4*>(kparam_h + t * NG);
+    r.kp = reinterpret_cast<const uint4*>(kparam_h)[t];
     // r is even: 4-byte aligned rows; halves past r are dropped when staged
-    const uint32_t* cw = reinterpret_cast<const uint32_t*>(coef_h + t * (uint32_t)a.r);
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(coef_h) + t * ((uint32_t)a.r >> 1);
     r.c0 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     r.c1 = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+    // (unsigned 32-bit element offsets from the uniform per-head bases: the
+    // loads then take a VGPR offset against an SGPR base, no 64-bit adds)
+    const uint32_t ukg = (uint32_t)kg;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int tt = 16 * tb + j;
       const uint32_t tv = (uint32_t)ti.tstart + (uint32_t)(tt < ti.tcount ? tt : ti.tcount - 1);
+      // group 2P + kg / 2, channels 16 (kg & 1) .. : code word 4 kg + 16 P of
+      // the token's 32-byte row, parameter word 4 tv + 2P + kg / 2
+      const uint32_t* vrow = reinterpret_cast<const uint32_t*>(vcode_h) + (tv * (uint32_t)(D / 16) + ukg);
+      const uint32_t* prow = vparam_h + (tv * (uint32_t)NG + (ukg >> 1));
 #pragma unroll
       for (int P = 0; P < 2; ++P) {
-        const int g = 2 * P + (kg >> 1);
-        r.vc[tb][P] = *reinterpret_cast<const uint32_t*>(vcode_h + tv * (D / 4) + 8 * g + 4 * (kg & 1));
-        r.vp[tb][P] = vparam_h[tv * NG + g];
+        r.vc[tb][P] = vrow[4 * P];
+        r.vp[tb][P] = prow[2 * P];
       }
     }
   };
