@@ -70,3 +70,56 @@ def test_noalloc_attend_matches_attend():
     assert "static scratch" in Q.last_error()
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+def test_noalloc_without_room_for_the_fp16_centroid_copy():
+    """On the bf16 head_dim-128 prefill path qwm_attend reads an fp16 copy of
+    the epochs' centroid tables made at the start of the call (in the cache's
+    arena). The allocation-free call keeps that copy in its static array only
+    where it fits; here it does not (16 heads x 64 epochs x 256 centroids x
+    256 bytes = 64 MiB, next to the q . U table), so its kernels convert the
+    bf16 rows of every tile instead. Both must agree, with and without a self
+    segment, within the attention bar (the two may split the KV sequence
+    differently)."""
+    from video_world_model_amd import Cache
+    import oracle.qwm_oracle as O
+    H, D, m, r, E, G = 16, 128, 256, 16, 64, 32
+    rng = np.random.default_rng(64)
+    lens = [int(x) for x in rng.integers(17, 80, size=E)]  # ragged epochs: partial tiles
+    n_kv = sum(lens)
+    assert H * E * m * D * 2 == 64 << 20
+    cache = Cache(H, D, m, r, n_kv, dtype=torch.bfloat16, max_epochs=E, max_query_tokens=96, max_build_tokens=64)
+    basis = rng.standard_normal((H, D, 8))
+    for e, n in enumerate(lens):
+        C = W.round_to_bf16(rng.standard_normal((H, m, D)).astype(np.float32))
+        S, U = [], []
+        for h in range(H):
+            qh = 2.0 * (rng.standard_normal((64, 8)) @ basis[h].T + 0.1 * rng.standard_normal((64, D)))
+            qh = W.round_to_bf16(qh.astype(np.float32))
+            S.append(O.sensitivity(qh, G))
+            U.append(O.subspace(qh, r))
+        cache.import_calibration(to_dev(list(C), "bf16"), torch.from_numpy(np.stack(S)).cuda(),
+                                 torch.from_numpy(np.ascontiguousarray(np.stack(U))).cuda())
+        k = W.round_to_bf16((C[:, rng.integers(0, m, n)] + 0.5 * rng.standard_normal((H, n, D))).astype(np.float32))
+        v = W.round_to_bf16(rng.standard_normal((H, n, D)).astype(np.float32))
+        cache.quantize_append(to_dev(list(k), "bf16"), to_dev(list(v), "bf16"))
+    assert cache.epochs() == E and cache.length() == n_kv
+    nq = 96  # past the decode kernel's 48: the prefill kernel
+    q = W.round_to_bf16((2.0 * np.einsum("hqk,hdk->hqd", rng.standard_normal((H, nq, 8)), basis)).astype(np.float32))
+    ks = W.round_to_bf16(rng.standard_normal((H, nq, D)).astype(np.float32))
+    vs = W.round_to_bf16(rng.standard_normal((H, nq, D)).astype(np.float32))
+    qd, kd, vd = to_dev(list(q), "bf16"), to_dev(list(ks), "bf16"), to_dev(list(vs), "bf16")
+    for self_seg in (False, True):
+        log(f"[noalloc, no room for the copy] H={H} epochs={E} n_kv={n_kv} n_q={nq} self={self_seg}")
+        out = torch.full((H, nq, D), float("nan"), dtype=torch.float32, device="cuda")
+        if self_seg:
+            ref = cache.attend(qd, kd, vd, mask="causal")
+            cache.attend_noalloc(qd, out, kd, vd, mask="causal")
+        else:
+            ref = cache.attend(qd)
+            cache.attend_noalloc(qd, out)
+        ref, got = ref.cpu().numpy(), out.cpu().numpy()
+        assert np.all(np.isfinite(got))
+        err = max(row_rel_err(got[h], ref[h]).max() for h in range(H))
+        log(f"  worst row error against qwm_attend {err:.2e}")
+        assert err <= ROW_TOL
